@@ -1,0 +1,427 @@
+"""Pins for the CPU oracle: each check ties an oracle function to something
+other than itself -- the pages' worked example, closed forms, an independent
+library routine (numpy FFT, numpy/scipy linear algebra, scipy's matrix
+exponential and IIR filter) or brute force on tiny inputs.  The mutation test
+at the end plants plausible mistakes in the oracle (on the CPU) and checks that
+at least one pin catches each of them."""
+import json
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.signal
+
+import oracle as O
+from structured_state_space_amd import inputs as I
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _cplx(a):
+    a = np.asarray(a, np.float64)
+    return a[..., 0] + 1j * a[..., 1]
+
+
+def _random_channel(seed, N, r, dt, kind="random"):
+    p = I.random_params(seed, 1, N, r, 8, dt_range=(dt, dt), lambda_kind=kind)
+    return p.Lambda[0].astype(np.complex128), p.P[0].astype(np.complex128), \
+        p.Q[0].astype(np.complex128), p.B[0].astype(np.complex128), p.C[0].astype(np.complex128)
+
+
+# --------------------------------------------------------------------------
+# worked example (page "... -- Examples", scalar model A = 0, B = C = 1)
+# --------------------------------------------------------------------------
+def test_cumsum_example_golden():
+    g = _golden("cumsum_example.json")
+    A = np.array([[g["A"]]], complex)
+    Abar, Bbar, st = O.bilinear(A, np.array([g["B"]], complex), g["dt"])
+    assert st == O.OK
+    assert Abar[0, 0] == g["Abar"] and Bbar[0] == g["Bbar"]          # bit-exact
+    u = np.array(g["u"], np.float64)
+    L = len(u)
+    K = O.kernel_by_iteration(Abar, Bbar, np.array([g["C"]], complex), L)
+    assert np.array_equal(K, np.array(g["K"], complex))
+    y = O.recurrence(Abar, Bbar, np.array([g["C"]], complex), g["D"], u[None])[0]
+    assert np.array_equal(y, np.array(g["y"], complex))
+    yc = O.causal_conv(K, u[None], g["D"])[0]
+    assert np.array_equal(yc, y)
+    # the same model through the input generator used by the GPU tests
+    p = I.cumsum_model(L)
+    A2 = O.dplr_matrix(p.Lambda[0], p.P[0], p.Q[0])
+    assert np.array_equal(A2, A)
+    # C~ = (I - 1^M)^* C = 0 exactly
+    assert O.truncated_output(Abar, np.array([1.0 + 0j]), O.transform_length(L))[0] == 0
+
+
+# --------------------------------------------------------------------------
+# closed forms
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_diagonal_closed_form(seed):
+    """P = Q = 0: Abar = diag((1 + a lam)/(1 - a lam)), Bbar = dt B/(1 - a lam),
+    K_j = sum conj(C_n) abar_n^j bbar_n, C~_n = (1 - conj(abar_n)^M) C_n."""
+    N, dt, L = 6, 0.07, 37
+    lam, _, _, B, C = _random_channel(seed, N, 1, dt)
+    zero = np.zeros((N, 1), complex)
+    Abar, Bbar, st = O.bilinear(O.dplr_matrix(lam, zero, zero), B, dt)
+    assert st == O.OK
+    al = dt / 2
+    abar = (1 + al * lam) / (1 - al * lam)
+    bbar = dt * B / (1 - al * lam)
+    np.testing.assert_allclose(Abar, np.diag(abar), atol=1e-14)
+    np.testing.assert_allclose(Bbar, bbar, rtol=1e-13)
+    K = O.kernel_by_iteration(Abar, Bbar, C, L)
+    j = np.arange(L)
+    Kc = (np.conj(C)[None, :] * abar[None, :] ** j[:, None] * bbar[None, :]).sum(1)
+    np.testing.assert_allclose(K, Kc, rtol=1e-12, atol=1e-14)
+    M = O.transform_length(L)
+    Ct = O.truncated_output(Abar, C, M)
+    np.testing.assert_allclose(Ct, (1 - np.conj(abar) ** M) * C, rtol=1e-12, atol=1e-14)
+
+
+def test_scalar_rank_one_closed_form():
+    """N = 1: A = lam - p conj(q) is a scalar; abar = (1 + aA)/(1 - aA)."""
+    lam, p, q, b, c, dt = -0.3 + 2.0j, 0.4 - 0.1j, -0.2 + 0.7j, 1.3 + 0.2j, 0.5 - 1.1j, 0.2
+    A = lam - p * np.conj(q)
+    Abar, Bbar, st = O.bilinear(O.dplr_matrix([lam], [[p]], [[q]]), np.array([b]), dt)
+    assert st == O.OK
+    abar = (1 + dt / 2 * A) / (1 - dt / 2 * A)
+    bbar = dt * b / (1 - dt / 2 * A)
+    assert abs(Abar[0, 0] - abar) < 1e-15 and abs(Bbar[0] - bbar) < 1e-15
+    K = O.kernel_by_iteration(Abar, Bbar, np.array([c]), 20)
+    np.testing.assert_allclose(K, np.conj(c) * abar ** np.arange(20) * bbar, rtol=1e-13)
+
+
+@pytest.mark.parametrize("dt", [0.02, 0.01, 0.005])
+def test_bilinear_matches_matrix_exponential_to_third_order(dt):
+    """The bilinear step is the (1,1) Pade approximant of expm(dt A):
+    expm(X) - (I - X/2)^{-1}(I + X/2) = -X^3/12 + O(X^4)."""
+    lam, P, Q, _, _ = _random_channel(7, 5, 2, dt)
+    A = O.dplr_matrix(lam, P, Q)
+    Abar, _, st = O.bilinear(A, np.ones(5, complex), dt)
+    assert st == O.OK
+    X = dt * A
+    err = scipy.linalg.expm(X) - Abar
+    lead = -np.linalg.matrix_power(X, 3) / 12
+    nx = np.linalg.norm(X, 2)
+    assert np.linalg.norm(err - lead, 2) <= 0.2 * nx ** 4 + 1e-14
+
+
+def test_kernel_iteration_matches_literal_powers():
+    lam, P, Q, B, C = _random_channel(3, 5, 2, 0.1)
+    Abar, Bbar, _ = O.bilinear(O.dplr_matrix(lam, P, Q), B, 0.1)
+    np.testing.assert_allclose(O.kernel_by_iteration(Abar, Bbar, C, 25),
+                               O.kernel_by_matrix_power(Abar, Bbar, C, 25), rtol=1e-12, atol=1e-13)
+
+
+# --------------------------------------------------------------------------
+# Fourier transforms against numpy's FFT and the unitarity identity
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("M", [1, 2, 4, 8, 64, 512])
+def test_radix2_matches_numpy_fft(M):
+    rng = np.random.default_rng(M)
+    a = rng.standard_normal(M) + 1j * rng.standard_normal(M)
+    np.testing.assert_allclose(O.radix2_dft(a), np.fft.fft(a), atol=1e-12 * max(1, M))
+    np.testing.assert_allclose(O.radix2_dft(a, inverse=True), np.fft.ifft(a), atol=1e-13)
+    np.testing.assert_allclose(O.dft_direct(a), np.fft.fft(a), atol=1e-11 * max(1, M))
+
+
+@pytest.mark.parametrize("M", [1, 2, 16, 128])
+def test_dft_matrix_unitarity(M):
+    F = O.dft_matrix(M)
+    np.testing.assert_allclose(F.conj().T @ F, M * np.eye(M), atol=1e-11 * M)
+
+
+def test_radix2_rejects_non_power_of_two():
+    with pytest.raises(ValueError):
+        O.radix2_dft(np.ones(6))
+
+
+# --------------------------------------------------------------------------
+# Woodbury and the structured solver against dense linear algebra
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("r", [1, 2, 4])
+def test_woodbury_matches_dense_inverse(r):
+    rng = np.random.default_rng(r)
+    N = 7
+    d = rng.standard_normal(N) + 1j * rng.standard_normal(N) + 3
+    U = rng.standard_normal((N, r)) + 1j * rng.standard_normal((N, r))
+    V = rng.standard_normal((N, r)) + 1j * rng.standard_normal((N, r))
+    dense = np.linalg.inv(np.diag(d) + U @ V.conj().T)
+    np.testing.assert_allclose(O.woodbury_inverse(d, U, V), dense, atol=1e-11)
+
+
+@pytest.mark.parametrize("r", [1, 2, 3])
+def test_dplr_solve_matches_dense(r):
+    lam, P, Q, B, _ = _random_channel(11 + r, 9, r, 0.3)
+    x, st = O.dplr_solve(lam, P, Q, 0.3, B)
+    G = np.eye(9) - 0.15 * O.dplr_matrix(lam, P, Q)
+    assert st == O.OK
+    np.testing.assert_allclose(x, np.linalg.solve(G, B), rtol=1e-12, atol=1e-13)
+
+
+def test_bordered_branch_matches_dense():
+    g = _golden("status_cases.json")
+    case = [c for c in g["cases"] if c["name"] == "bordered"][0]
+    lam, P, Q = _cplx(case["Lambda"]), _cplx(case["P"]), _cplx(case["Q"])
+    dt = case["dt"]
+    d = 1 - dt / 2 * lam
+    assert np.count_nonzero(d == 0) == 1          # the bordered branch is taken
+    b = np.array([0.3 - 0.2j, 1.1 + 0.4j])
+    x, st = O.dplr_solve(lam, P, Q, dt, b)
+    G = np.eye(2) - dt / 2 * O.dplr_matrix(lam, P, Q)
+    assert st == O.OK
+    np.testing.assert_allclose(x, np.linalg.solve(G, b), rtol=1e-14, atol=1e-15)
+
+
+# --------------------------------------------------------------------------
+# filter mode: root values equal the DFT of the first M kernel taps
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("N,r,L,dt,kind", [(8, 1, 13, 0.05, "random"), (6, 2, 16, 0.3, "random"),
+                                           (5, 3, 7, 1.0, "random"), (8, 1, 64, 0.01, "s4"),
+                                           (4, 1, 1, 0.1, "random"), (4, 2, 2, 0.1, "random")])
+def test_root_values_equal_dft_of_kernel(N, r, L, dt, kind):
+    lam, P, Q, B, C = _random_channel(N * 10 + r, N, r, dt, kind)
+    disc = O.discretize_channel(lam, P, Q, B, C, dt, L)
+    M = disc["M"]
+    K_M = O.kernel_by_iteration(disc["Abar"], disc["Bbar"], C, M)
+    Hk, st = O.root_values(lam, P, Q, B, disc["Ctilde"], dt, M)
+    assert st == O.OK
+    ref = np.fft.fft(K_M)
+    np.testing.assert_allclose(Hk, ref, atol=1e-11 * np.abs(ref).max())
+    Hc, st2 = O.root_values_cauchy(lam, P, Q, B, disc["Ctilde"], dt, M)
+    assert st2 == O.OK
+    np.testing.assert_allclose(Hc, Hk, atol=1e-11 * np.abs(ref).max())
+    K, st3 = O.filter_kernel(lam, P, Q, B, disc["Ctilde"], dt, L)
+    assert st3 == O.OK
+    np.testing.assert_allclose(K, K_M[:L], atol=1e-11 * np.abs(K_M).max())
+
+
+def test_minus_one_root_formula():
+    """At z = -1 the value is (dt/2) C~^* B (the resolvent's limit); it equals the
+    alternating sum of the first M taps."""
+    lam, P, Q, B, C = _random_channel(5, 6, 2, 0.2)
+    disc = O.discretize_channel(lam, P, Q, B, C, 0.2, 16)
+    K_M = O.kernel_by_iteration(disc["Abar"], disc["Bbar"], C, 16)
+    Hk, _ = O.root_values(lam, P, Q, B, disc["Ctilde"], 0.2, 16)
+    alt = np.sum(K_M * (-1.0) ** np.arange(16))
+    assert abs(Hk[8] - alt) < 1e-12 * abs(alt) + 1e-14
+    assert abs(Hk[8] - 0.1 * np.vdot(disc["Ctilde"], B)) < 1e-15
+
+
+def test_s_form_roots():
+    """s(z_k) = (2/dt)(1-z)/(1+z) = i (2/dt) tan(pi k/M) and 2/(1+z) = 1 + i tan(pi k/M)."""
+    M, dt = 32, 0.37
+    z = O.roots_of_unity(M)
+    k = np.arange(M)
+    ok = k != M // 2
+    t = np.tan(np.pi * k[ok] / M)
+    np.testing.assert_allclose((2 / dt) * (1 - z[ok]) / (1 + z[ok]), 1j * (2 / dt) * t, atol=1e-12)
+    np.testing.assert_allclose(2 / (1 + z[ok]), 1 + 1j * t, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# recurrence vs convolution, against scipy's IIR filter and the FFT product
+# --------------------------------------------------------------------------
+def test_recurrence_matches_iir_filter_per_mode():
+    """For diagonal A each mode is a first-order IIR filter: scipy.signal.lfilter."""
+    N, dt, L = 4, 0.05, 50
+    lam, _, _, B, C = _random_channel(21, N, 1, dt)
+    zero = np.zeros((N, 1), complex)
+    Abar, Bbar, _ = O.bilinear(O.dplr_matrix(lam, zero, zero), B, dt)
+    u = np.random.default_rng(0).standard_normal((3, L))
+    y = O.recurrence(Abar, Bbar, C, 0.7, u)
+    ref = 0.7 * u.astype(complex)
+    for n in range(N):
+        ref = ref + np.conj(C[n]) * scipy.signal.lfilter([Bbar[n]], [1, -Abar[n, n]], u, axis=-1)
+    np.testing.assert_allclose(y, ref, atol=1e-12)
+
+
+@pytest.mark.parametrize("L", [1, 2, 17, 64])
+def test_recurrence_equals_causal_conv(L):
+    lam, P, Q, B, C = _random_channel(L, 6, 2, 0.1)
+    disc = O.discretize_channel(lam, P, Q, B, C, 0.1, L)
+    u = np.random.default_rng(L).standard_normal((2, L))
+    y = O.recurrence(disc["Abar"], disc["Bbar"], C, -0.4, u)
+    K = O.kernel_by_iteration(disc["Abar"], disc["Bbar"], C, L)
+    np.testing.assert_allclose(O.causal_conv(K, u, -0.4), y, atol=1e-12)
+    for t in [0, L // 2, L - 1]:
+        assert abs(O.causal_conv_at(K, u[1], -0.4, t) - y[1, t]) < 1e-12
+
+
+def test_zero_padded_fft_product_convention():
+    """Prior art on the LMU page: rfft with n = 2L, product, irfft, keep [:L] is the
+    causal (linear) convolution of real sequences."""
+    rng = np.random.default_rng(5)
+    L = 40
+    k, u = rng.standard_normal(L), rng.standard_normal((2, L))
+    n = O.conv_length(L)
+    assert n >= 2 * L - 1
+    y = np.fft.irfft(np.fft.rfft(u, n=n) * np.fft.rfft(k, n=n), n=n)[:, :L]
+    np.testing.assert_allclose(y, O.causal_conv(k, u, 0.0).real, atol=1e-12)
+
+
+def test_impulse_response_is_kernel_plus_skip():
+    lam, P, Q, B, C = _random_channel(8, 5, 1, 0.2)
+    disc = O.discretize_channel(lam, P, Q, B, C, 0.2, 30)
+    u = np.zeros((1, 30)); u[0, 0] = 1.0
+    y = O.recurrence(disc["Abar"], disc["Bbar"], C, 0.9, u)[0]
+    K = O.kernel_by_iteration(disc["Abar"], disc["Bbar"], C, 30)
+    np.testing.assert_allclose(y, K + 0.9 * (np.arange(30) == 0), atol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# integer sizes and statuses
+# --------------------------------------------------------------------------
+def test_transform_lengths():
+    table = {1: (1, 1), 2: (2, 4), 3: (4, 8), 64: (64, 128), 1024: (1024, 2048),
+             3000: (4096, 8192), 16384: (16384, 32768), 65536: (65536, 131072)}
+    for L, (M, Nf) in table.items():
+        assert O.transform_length(L) == M and O.conv_length(L) == Nf
+    with pytest.raises(ValueError):
+        O.transform_length(0)
+
+
+def _case(name):
+    g = _golden("status_cases.json")
+    c = [c for c in g["cases"] if c["name"] == name][0]
+    return dict(Lambda=_cplx(c["Lambda"]), P=_cplx(c["P"]), Q=_cplx(c["Q"]), B=_cplx(c["B"]),
+                C=_cplx(c["C"]), dt=c["dt"], L=c["L"]), c
+
+
+@pytest.mark.parametrize("name", ["resonant-diagonal", "resonant-correction", "singular-bilinear",
+                                  "bordered"])
+def test_status_constructions(name):
+    p, c = _case(name)
+    disc = O.discretize_channel(p["Lambda"], p["P"], p["Q"], p["B"], p["C"], p["dt"], p["L"])
+    assert disc["status"] == c["expect_bilinear"]
+    x, st = O.dplr_solve(p["Lambda"], p["P"], p["Q"], p["dt"], p["B"])
+    assert st == c["expect_bilinear"]
+    if c["expect_filter"] is None:
+        return
+    M = O.transform_length(p["L"])
+    _, st1 = O.root_values(p["Lambda"], p["P"], p["Q"], p["B"], p["C"], p["dt"], M)
+    _, st2 = O.root_values_cauchy(p["Lambda"], p["P"], p["Q"], p["B"], p["C"], p["dt"], M)
+    assert st1 == c["expect_filter"] and st2 == c["expect_filter"]
+    ref = O.channel_reference(p["Lambda"], p["P"], p["Q"], p["B"], p["C"], p["dt"], 0.5,
+                              np.ones((1, p["L"])), p["L"])
+    assert ref["status"] == c["expect_filter"]
+    assert np.isnan(ref["K"]).all() == (c["expect_filter"] != O.OK)
+
+
+def test_bordered_case_kernel_still_matches_dft():
+    p, _ = _case("bordered")
+    disc = O.discretize_channel(p["Lambda"], p["P"], p["Q"], p["B"], p["C"], p["dt"], p["L"])
+    K_M = O.kernel_by_iteration(disc["Abar"], disc["Bbar"], p["C"], disc["M"])
+    Hk, st = O.root_values(p["Lambda"], p["P"], p["Q"], p["B"], disc["Ctilde"], p["dt"], disc["M"])
+    assert st == O.OK
+    np.testing.assert_allclose(Hk, np.fft.fft(K_M), atol=1e-10 * np.abs(K_M).max())
+
+
+def test_status_precedence():
+    assert O.worst_status(O.OK, O.RESONANT_CORRECTION, O.RESONANT_DIAGONAL) == O.RESONANT_DIAGONAL
+    assert O.worst_status(O.RESONANT_DIAGONAL, O.SINGULAR_BILINEAR) == O.SINGULAR_BILINEAR
+
+
+# --------------------------------------------------------------------------
+# the workload generator keeps its documented recipe
+# --------------------------------------------------------------------------
+def test_workload_recipe():
+    w, p, u = I.workload(0)
+    assert (p.H, p.N, p.r, p.L, u.shape) == (1, 8, 1, 64, (1, 1, 64))
+    np.testing.assert_array_equal(p.Lambda[0], (-0.5 + 1j * np.pi * np.arange(8)).astype(np.complex64))
+    assert np.all(p.B == 1) and np.all(p.dt == np.float32(0.01))
+    assert u.dtype == np.float32 and p.C.dtype == np.complex64
+    w2, p2, _ = I.workload(0)
+    assert np.array_equal(p2.C, p.C)                      # seeded
+    p4, _ = I.make_params(I.WORKLOADS[3])
+    assert p4.P.shape == (1024, 64, 2) and np.all(p4.P[0] == p4.P[-1])
+    assert 1e-3 <= p4.dt.min() and p4.dt.max() <= 1e-1
+
+
+# --------------------------------------------------------------------------
+# planted mistakes: each must be caught by at least one pin above
+# --------------------------------------------------------------------------
+def _pins_pass():
+    checks = [
+        test_cumsum_example_golden,
+        lambda: test_diagonal_closed_form(0),
+        test_scalar_rank_one_closed_form,
+        lambda: test_bilinear_matches_matrix_exponential_to_third_order(0.01),
+        lambda: test_root_values_equal_dft_of_kernel(6, 2, 16, 0.3, "random"),
+        test_minus_one_root_formula,
+        lambda: test_recurrence_equals_causal_conv(17),
+        test_recurrence_matches_iir_filter_per_mode,
+        test_impulse_response_is_kernel_plus_skip,
+        lambda: test_dplr_solve_matches_dense(2),
+        test_bordered_branch_matches_dense,
+        lambda: test_radix2_matches_numpy_fft(64),
+    ]
+    for c in checks:
+        try:
+            c()
+        except AssertionError:
+            return False
+    return True
+
+
+def _mut_bilinear_sign(A, B, dt):
+    A = np.asarray(A, complex); I_ = np.eye(A.shape[0])
+    G = I_ + dt / 2 * A
+    return np.linalg.solve(G, I_ - dt / 2 * A), np.linalg.solve(G, dt * np.asarray(B, complex)), O.OK
+
+
+def _mut_truncated_no_conj(Abar, C, M):
+    return (np.eye(Abar.shape[0]) - np.linalg.matrix_power(Abar, M)) @ C
+
+
+def _mut_dplr_plus(Lambda, P, Q):
+    P = np.asarray(P, complex).reshape(len(Lambda), -1); Q = np.asarray(Q, complex).reshape(len(Lambda), -1)
+    return np.diag(np.asarray(Lambda, complex)) + P @ Q.conj().T
+
+
+def _mut_dplr_transposed(Lambda, P, Q):
+    P = np.asarray(P, complex).reshape(len(Lambda), -1); Q = np.asarray(Q, complex).reshape(len(Lambda), -1)
+    return np.diag(np.asarray(Lambda, complex)) - Q @ P.conj().T
+
+
+def _mut_kernel_no_conj(Abar, Bbar, C, length):
+    v = np.asarray(Bbar, complex).copy(); K = np.empty(length, complex)
+    for j in range(length):
+        K[j] = np.dot(C, v); v = Abar @ v
+    return K
+
+
+def _mut_recurrence_no_skip(Abar, Bbar, C, D, u):
+    return _orig["recurrence"](Abar, Bbar, C, 0.0, u)
+
+
+def _mut_radix2_sign(a, inverse=False):
+    return _orig["radix2_dft"](a, not inverse) * (len(a) if not inverse else 1 / len(a))
+
+
+_orig = {}
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("bilinear", _mut_bilinear_sign),
+    ("truncated_output", _mut_truncated_no_conj),
+    ("dplr_matrix", _mut_dplr_plus),
+    ("dplr_matrix", _mut_dplr_transposed),
+    ("kernel_by_iteration", _mut_kernel_no_conj),
+    ("recurrence", _mut_recurrence_no_skip),
+    ("radix2_dft", _mut_radix2_sign),
+])
+def test_planted_mistakes_are_caught(monkeypatch, name, mutant):
+    import oracle.ssm_oracle as mod
+    assert _pins_pass()
+    _orig[name] = getattr(mod, name)
+    monkeypatch.setattr(mod, name, mutant)
+    monkeypatch.setattr(O, name, mutant)
+    assert not _pins_pass(), f"no pin caught the planted mistake in {name}"
