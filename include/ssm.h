@@ -1,0 +1,163 @@
+/*
+ * ssm.h -- C ABI of the MI355X (gfx950) S4 DPLR filter library.
+ *
+ * The library computes, for H independent single-input single-output channels
+ * of a diagonal-plus-low-rank (DPLR) state-space model, the bilinear
+ * discretisation, the length-L convolution kernel by the filter-mode
+ * evaluation at the M roots of unity, and the causal convolution
+ * y = K * u + D u.  Passages defining each operation are cited by page title
+ * and block:
+ *   [RSS] "Recurrent, LSTM, and structured state-space models"
+ *         (blocks: continuous-time linear SSM; DPLR parameterisation;
+ *          radix-two DFT; Woodbury inverse; S4 Algorithm 1 / App. C)
+ *   [EX]  "Recurrent, LSTM, and structured state-space models -- Examples"
+ *         (the scalar example A = 0, B = C = 1, dt = 1)
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller; the library
+ *     never allocates, frees or retains them.  Complex numbers are interleaved
+ *     {float re, im} (ssm_c64, the layout of torch.complex64).  Arrays are
+ *     row-major with the last index fastest.  Complex arrays must be 8-byte
+ *     aligned, float/int arrays 4-byte aligned, the workspace 256-byte aligned.
+ *   - Per-channel parameters: Lambda [H,N], P [H,N,r], Q [H,N,r], B [H,N],
+ *     C or Ctilde [H,N] (ssm_c64); dt [H], D [H] (float).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *     Every call only enqueues work on `stream` and returns; results are ready
+ *     when the stream reaches that point.  Calls are reentrant; calls that
+ *     share a workspace must be ordered on one stream.
+ *   - The return value reports host-detectable errors only (SSM_ERR_*).  When
+ *     it is not SSM_OK nothing was enqueued.  Data-dependent conditions are
+ *     reported per channel through the optional device array `status` [H]
+ *     (int32, SSM_ST_*); a channel with a nonzero status has every one of its
+ *     outputs filled with NaN.
+ *   - Sizes: H >= 1, N >= 1, 1 <= r <= 4, 1 <= L <= 65536, Bsz >= 1;
+ *     ssm_discretize also needs N <= 4096.  Other sizes give
+ *     SSM_ERR_INVALID_ARGUMENT (non-positive) or SSM_ERR_UNSUPPORTED (above
+ *     these caps).
+ *   - M = least power of two >= L; the zero-padded product length is the least
+ *     power of two >= 2L - 1 ([RSS] filter-mode block; radix-two DFT block).
+ */
+#ifndef SSM_H
+#define SSM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ssm_c64 {
+    float re;
+    float im;
+} ssm_c64;
+
+/* Return codes (host side). */
+#define SSM_OK 0
+#define SSM_ERR_INVALID_ARGUMENT 1 /* null required pointer, bad size, misalignment */
+#define SSM_ERR_WORKSPACE 2        /* ws_bytes below ssm_workspace_bytes() */
+#define SSM_ERR_DEVICE 3           /* a HIP call or kernel launch failed */
+#define SSM_ERR_UNSUPPORTED 4      /* valid for the method, above this library's caps */
+
+/* Per-channel statuses (device int32).  When several hold, the largest code
+ * is reported. */
+#define SSM_ST_OK 0
+#define SSM_ST_RESONANT_CORRECTION 16 /* W(z_k) = I_r + Q^* R(z_k) P exactly singular, [RSS] Alg. 1 */
+#define SSM_ST_RESONANT_DIAGONAL 17   /* s(z_k) - lambda_j exactly zero, [RSS] Alg. 1 */
+#define SSM_ST_SINGULAR_BILINEAR 18   /* G = I - dt A/2 singular, [RSS] recurrent solver */
+#define SSM_ST_INVALID_STEP 19        /* dt not finite and positive ([RSS] requires dt > 0) */
+
+/* Operation ids for ssm_workspace_bytes. */
+#define SSM_OP_DISCRETIZE 0
+#define SSM_OP_KERNEL_GEN 1
+#define SSM_OP_FFTCONV 2
+#define SSM_OP_FORWARD 3
+
+/*
+ * Workspace size in bytes that entry point `op` needs for these sizes (Bsz is
+ * ignored by ops that take no batch; N and r are ignored by SSM_OP_FFTCONV).
+ * Writes *bytes and returns SSM_OK, or returns SSM_ERR_INVALID_ARGUMENT /
+ * SSM_ERR_UNSUPPORTED under the size rules above (then *bytes is untouched).
+ */
+int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
+                        size_t* bytes);
+
+/* Transform sizes for a kernel length L >= 1 ([RSS] filter-mode block):
+ * *M = least power of two >= L; *n_fft = least power of two >= 2L - 1.
+ * Pure integer host computation; SSM_ERR_INVALID_ARGUMENT for L < 1. */
+int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft);
+
+/* Static description of a return code or status code (never NULL). */
+const char* ssm_status_string(int code);
+
+/*
+ * Bilinear discretisation ([RSS] DPLR block; recurrent solver of Alg. 1).
+ * Per channel, with alpha = dt/2, G = I - alpha A, A = diag(Lambda) - P Q^*:
+ *   Bbar = G^{-1} dt B                      -> Bbar   [H,N]   (nullable)
+ *   Abar = G^{-1}(I + alpha A) = 2G^{-1} - I -> Abar   [H,N,N] (nullable, row-major)
+ *   Ctilde = (I - Abar^M)^* C, M from L      -> Ctilde [H,N]   (nullable)
+ * G is applied through the Woodbury core I_r + alpha Q^* D^{-1} P when every
+ * d_j = 1 - alpha lambda_j is nonzero, else through the pages' bordered system
+ * when at most r of them are zero; a singular core or bordered system, or more
+ * than r zero d_j, gives SSM_ST_SINGULAR_BILINEAR.  Arithmetic is float64
+ * inside; outputs are rounded to complex64.  Ctilde is formed by M adjoint
+ * steps c <- Abar^* c (latency-bound, one wavefront per channel).
+ * Workspace: none (pass ws = NULL, ws_bytes = 0).
+ */
+int ssm_discretize(int64_t H, int64_t N, int64_t r, int64_t L,
+                   const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                   const ssm_c64* B, const ssm_c64* C, const float* dt,
+                   ssm_c64* Bbar, ssm_c64* Abar, ssm_c64* Ctilde, int32_t* status,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Filter-mode kernel generation ([RSS] Alg. 1 filter mode).
+ * Ctilde is the supplied truncated-output vector (I - Abar^M)^* C.  For each
+ * root z_k = exp(-2 pi i k/M): at z_k = -1 the value is (dt/2) Ctilde^* B;
+ * otherwise H(z_k) = 2/(1+z_k) (Ctilde^* R B - Ctilde^* R P W^{-1} Q^* R B) with
+ * R = diag(1/(s(z_k) - lambda_j)), s(z) = (2/dt)(1-z)/(1+z), W = I_r + Q^* R P.
+ * The kernel is the first L coefficients of the inverse transform
+ * K_j = (1/M) sum_k H(z_k) exp(+2 pi i jk/M).
+ *   K         [H,L] complex64, nullable
+ *   roots_out [H,M] complex64, nullable: the root values H(z_k) themselves
+ *   status    [H] int32, nullable
+ * Workspace: ssm_workspace_bytes(SSM_OP_KERNEL_GEN, ...).
+ */
+int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L,
+                   const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                   const ssm_c64* B, const ssm_c64* Ctilde, const float* dt,
+                   ssm_c64* K, ssm_c64* roots_out, int32_t* status,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Causal convolution with skip term ([RSS] DPLR block: y_t = sum_{j<=t} K_j
+ * u_{t-j} + D u_t; radix-two DFT block: exact product by zero padding to
+ * length >= 2L - 1; [EX] convolution equals the recurrence).
+ *   K  real kernel: element (h, j) at K[(h*L + j) * k_stride]; k_stride = 1 for
+ *      a float [H,L] array, 2 to read the real parts of a complex64 [H,L] array
+ *   D  [H] float, nullable (= 0)
+ *   u  [Bsz,H,L] float, y [Bsz,H,L] float (y must not overlap u)
+ * Workspace: ssm_workspace_bytes(SSM_OP_FFTCONV, ...).
+ */
+int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_stride,
+                const float* D, const float* u, float* y,
+                void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole filter path: ssm_kernel_gen from the supplied Ctilde, then
+ * y = (Re K) * u + D u ([RSS] DPLR block: y_t = C^* x_t + D u_t, real part).
+ *   u, y [Bsz,H,L] float; D [H] float (nullable = 0)
+ *   K_out [H,L] complex64, nullable; status [H] int32, nullable
+ * Workspace: ssm_workspace_bytes(SSM_OP_FORWARD, ...).
+ */
+int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
+                const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                const float* u, float* y, ssm_c64* K_out, int32_t* status,
+                void* ws, size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_H */

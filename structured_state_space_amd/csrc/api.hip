@@ -1,0 +1,220 @@
+// C ABI entry points: argument checks, workspace layout, kernel launches.
+// Everything data-dependent happens on the device; the host only validates
+// sizes and pointers and enqueues work on the caller's stream.
+#include <string.h>
+
+#include "common.hpp"
+
+namespace ssm {
+int64_t cauchy_tiles(int64_t r, int64_t M);
+hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
+                         const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
+                         int32_t* tile_status, hipStream_t stream);
+hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                           const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
+                           float2* K_out, int32_t* status, float2* khat, hipStream_t stream);
+hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
+                       hipStream_t stream);
+hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
+                             const float2* Q, const float2* Bv, const float2* C, const float* dt, float2* Bbar,
+                             float2* Abar, float2* Ct, int32_t* status, hipStream_t stream);
+}  // namespace ssm
+
+using namespace ssm;
+
+namespace {
+
+constexpr int64_t kMaxL = 65536;
+constexpr int64_t kMaxR = 4;
+constexpr int64_t kMaxNDisc = 4096;
+constexpr int64_t kMaxDim = (int64_t)1 << 31;
+
+int64_t pow2_at_least(int64_t v) {
+    int64_t m = 1;
+    while (m < v) m <<= 1;
+    return m;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// size rules shared by all entry points; returns SSM_OK or an error code
+int check_sizes(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, bool needs_state, bool needs_batch) {
+    if (H < 1 || L < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (needs_state && (N < 1 || r < 1)) return SSM_ERR_INVALID_ARGUMENT;
+    if (needs_batch && Bsz < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (L > kMaxL) return SSM_ERR_UNSUPPORTED;
+    if (needs_state && r > kMaxR) return SSM_ERR_UNSUPPORTED;
+    if (H >= kMaxDim || (needs_state && N >= kMaxDim) || (needs_batch && Bsz >= kMaxDim))
+        return SSM_ERR_UNSUPPORTED;
+    if (needs_batch && (Bsz * H >= kMaxDim || Bsz * H > ((int64_t)1 << 62) / L)) return SSM_ERR_UNSUPPORTED;
+    return SSM_OK;
+}
+
+WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L) {
+    (void)Bsz;
+    (void)N;
+    WsLayout w;
+    const int64_t M = pow2_at_least(L);
+    size_t off = 0;
+    if (op == SSM_OP_KERNEL_GEN || op == SSM_OP_FORWARD) {
+        w.roots = off;
+        w.roots_bytes = (size_t)H * M * sizeof(float2);
+        off = align256(off + w.roots_bytes);
+        w.tstat = off;
+        w.tstat_bytes = (size_t)H * cauchy_tiles(r, M) * sizeof(int32_t);
+        off = align256(off + w.tstat_bytes);
+    }
+    if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {
+        w.khat = off;
+        w.khat_bytes = (size_t)H * 2 * M * sizeof(float2);
+        off = align256(off + w.khat_bytes);
+    }
+    w.total = off;
+    return w;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft) {
+    if (L < 1 || L > ((int64_t)1 << 61) || !M || !n_fft) return SSM_ERR_INVALID_ARGUMENT;
+    *M = pow2_at_least(L);
+    *n_fft = pow2_at_least(2 * L - 1);
+    return SSM_OK;
+}
+
+const char* ssm_status_string(int code) {
+    switch (code) {
+        case SSM_OK: return "ok";
+        case SSM_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case SSM_ERR_WORKSPACE: return "workspace too small";
+        case SSM_ERR_DEVICE: return "device error";
+        case SSM_ERR_UNSUPPORTED: return "unsupported size";
+        case SSM_ST_RESONANT_CORRECTION: return "resonant-correction";
+        case SSM_ST_RESONANT_DIAGONAL: return "resonant-diagonal";
+        case SSM_ST_SINGULAR_BILINEAR: return "singular-bilinear-matrix";
+        case SSM_ST_INVALID_STEP: return "invalid-step";
+        default: return "unknown code";
+    }
+}
+
+int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, size_t* bytes) {
+    if (!bytes) return SSM_ERR_INVALID_ARGUMENT;
+    int rc;
+    switch (op) {
+        case SSM_OP_DISCRETIZE: rc = check_sizes(1, H, N, r, L, true, false); break;
+        case SSM_OP_KERNEL_GEN: rc = check_sizes(1, H, N, r, L, true, false); break;
+        case SSM_OP_FFTCONV: rc = check_sizes(Bsz, H, 1, 1, L, false, true); break;
+        case SSM_OP_FORWARD: rc = check_sizes(Bsz, H, N, r, L, true, true); break;
+        default: return SSM_ERR_INVALID_ARGUMENT;
+    }
+    if (rc != SSM_OK) return rc;
+    if (op == SSM_OP_DISCRETIZE && N > kMaxNDisc) return SSM_ERR_UNSUPPORTED;
+    if (op != SSM_OP_DISCRETIZE && pow2_at_least(L) > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
+    *bytes = op == SSM_OP_DISCRETIZE ? 0 : layout(op, Bsz, H, N, r, L).total;
+    return SSM_OK;
+}
+
+int ssm_discretize(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
+                   const ssm_c64* Q, const ssm_c64* B, const ssm_c64* C, const float* dt, ssm_c64* Bbar,
+                   ssm_c64* Abar, ssm_c64* Ctilde, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int rc = check_sizes(1, H, N, r, L, true, false);
+    if (rc != SSM_OK) return rc;
+    if (N > kMaxNDisc) return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !Q || !B || !dt || (Ctilde && !C)) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, C, Bbar, Abar, Ctilde};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(status, 4)) return SSM_ERR_INVALID_ARGUMENT;
+    const int64_t M = pow2_at_least(L);
+    return device_status(launch_discretize(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                           (const float2*)B, (const float2*)C, dt, (float2*)Bbar, (float2*)Abar,
+                                           (float2*)Ctilde, status, (hipStream_t)stream));
+}
+
+int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
+                   const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, ssm_c64* K,
+                   ssm_c64* roots_out, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(1, H, N, r, L, true, false);
+    if (rc != SSM_OK) return rc;
+    const int64_t M = pow2_at_least(L);
+    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !Q || !B || !Ctilde || !dt) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, Ctilde, K, roots_out};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(status, 4) || !aligned(ws, 256)) return SSM_ERR_INVALID_ARGUMENT;
+    const WsLayout w = layout(SSM_OP_KERNEL_GEN, 1, H, N, r, L);
+    if (ws_bytes < w.total || (w.total && !ws)) return SSM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float2* roots = roots_out ? (float2*)roots_out : (float2*)(base + w.roots);
+    int32_t* tstat = (int32_t*)(base + w.tstat);
+    hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, s);
+    if (e != hipSuccess) return SSM_ERR_DEVICE;
+    if (K || status) {
+        // kernel transform only (spectra go to the workspace's unused tail: none needed here)
+        e = launch_spectrum(true, H, L, M, cauchy_tiles(r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
+                            status, nullptr, s);
+        if (e != hipSuccess) return SSM_ERR_DEVICE;
+    }
+    return SSM_OK;
+}
+
+int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_stride, const float* D, const float* u,
+                float* y, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(Bsz, H, 1, 1, L, false, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t M = pow2_at_least(L);
+    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
+    if (!K || !u || !y || (k_stride != 1 && k_stride != 2)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(K, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(ws, 256))
+        return SSM_ERR_INVALID_ARGUMENT;
+    const WsLayout w = layout(SSM_OP_FFTCONV, Bsz, H, 1, 1, L);
+    if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    float2* khat = (float2*)((char*)ws + w.khat);
+    hipError_t e = launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, s);
+    if (e != hipSuccess) return SSM_ERR_DEVICE;
+    return device_status(launch_conv(Bsz, H, L, M, u, y, khat, s));
+}
+
+int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
+                const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(Bsz, H, N, r, L, true, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t M = pow2_at_least(L);
+    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !Q || !B || !Ctilde || !dt || !u || !y) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, Ctilde, K_out};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(status, 4) ||
+        !aligned(ws, 256))
+        return SSM_ERR_INVALID_ARGUMENT;
+    const WsLayout w = layout(SSM_OP_FORWARD, Bsz, H, N, r, L);
+    if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float2* roots = (float2*)(base + w.roots);
+    int32_t* tstat = (int32_t*)(base + w.tstat);
+    float2* khat = (float2*)(base + w.khat);
+    hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, s);
+    if (e != hipSuccess) return SSM_ERR_DEVICE;
+    e = launch_spectrum(true, H, L, M, cauchy_tiles(r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status, khat,
+                        s);
+    if (e != hipSuccess) return SSM_ERR_DEVICE;
+    return device_status(launch_conv(Bsz, H, L, M, u, y, khat, s));
+}
+
+}  // extern "C"

@@ -1,0 +1,313 @@
+// Root values H(z_k) of the S4 filter mode on VALU.
+//
+// Source: "Recurrent, LSTM, and structured state-space models", block for S4
+// Algorithm 1 / App. C (filter mode).  For z = z_k = exp(-2 pi i k/M), k != M/2,
+//   s(z) = (2/dt)(1-z)/(1+z) = i a tan(pi k/M),   2/(1+z) = 1 + i tan(pi k/M),
+// with a = 2/dt, so each denominator s(z_k) - lambda_n = -Re(lambda_n) + i(a t_k -
+// Im(lambda_n)).  The (r+1)^2 sums
+//   rho_uv(k) = sum_n conj(u_n) v_n / (s(z_k) - lambda_n),  u in {C~, Q_a}, v in {B, P_b}
+// are the resolvent products u^* R(z_k) v of the page; then
+//   W = I_r + rho_QP,  H = (1 + i t_k) (rho_C~B - rho_C~P W^{-1} rho_QB),
+// and z = -1 (k = M/2) takes the page's finite value (dt/2) C~^* B.  This is the
+// resolvent expression itself; it equals the page's mu-form Cauchy products
+// S_uv(z) = (2/(1+z)) u^* R v term by term, but keeps the denominators' real part
+// exactly -Re(lambda_n), which float32 needs when a = 2/dt is large.
+//
+// Work split: one workgroup per (channel, tile of 256*RPT roots).  Per chunk of
+// 64 states the workgroup stages lambda and the weights conj(u_n) v_n (times
+// -Re(lambda_n), see below) in LDS; every thread then sweeps the chunk for its
+// RPT roots: one reciprocal and (r+1)^2 complex multiply-adds per (root, state).
+// With d = x + i y (x = -Re lambda, y = a t_k - Im lambda), 1/d = (x - i y)/|d|^2,
+//   w/d = (w x) inv + (-i w) (y inv),  inv = 1/|d|^2,
+// so the table keeps (w x) and w and the loop needs inv and p = y*inv only.
+// Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
+// with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
+// flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
+// |re|+|im| order) is flagged resonant-correction.
+#include <float.h>
+
+#include "common.hpp"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kChunk = 64;
+
+template <int RK>
+struct Fam {
+    static constexpr int F = (RK + 1) * (RK + 1);
+    static constexpr int ROW = 1 + F;  // float4 per state: header + one per family
+};
+
+__device__ __forceinline__ float2 cdivf(float2 a, float2 b) {
+    const float den = fmaf(b.x, b.x, b.y * b.y);
+    const float inv = 1.0f / den;
+    return make_float2(fmaf(a.x, b.x, a.y * b.y) * inv, fmaf(a.y, b.x, -a.x * b.y) * inv);
+}
+
+__device__ __forceinline__ float cabs1(float2 a) { return fabsf(a.x) + fabsf(a.y); }
+
+// Solve W x = rhs in place (x returned in rhs), W r x r complex.  Gaussian
+// elimination with partial pivoting; false when a pivot is exactly zero.
+template <int RK>
+__device__ __forceinline__ bool small_solve(float2 (&W)[RK][RK], float2 (&rhs)[RK]) {
+#pragma unroll
+    for (int c = 0; c < RK; ++c) {
+#pragma unroll
+        for (int r = c + 1; r < RK; ++r) {
+            const bool sw = cabs1(W[r][c]) > cabs1(W[c][c]);
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                const float2 a = W[c][j], b = W[r][j];
+                W[c][j] = sw ? b : a;
+                W[r][j] = sw ? a : b;
+            }
+            const float2 a = rhs[c], b = rhs[r];
+            rhs[c] = sw ? b : a;
+            rhs[r] = sw ? a : b;
+        }
+        if (W[c][c].x == 0.0f && W[c][c].y == 0.0f) return false;
+#pragma unroll
+        for (int r = c + 1; r < RK; ++r) {
+            const float2 f = cdivf(W[r][c], W[c][c]);
+#pragma unroll
+            for (int j = c + 1; j < RK; ++j) W[r][j] = c_sub(W[r][j], c_mul(f, W[c][j]));
+            rhs[r] = c_sub(rhs[r], c_mul(f, rhs[c]));
+        }
+    }
+#pragma unroll
+    for (int c = RK - 1; c >= 0; --c) {
+        float2 s = rhs[c];
+#pragma unroll
+        for (int j = c + 1; j < RK; ++j) s = c_sub(s, c_mul(W[c][j], rhs[j]));
+        rhs[c] = cdivf(s, W[c][c]);
+    }
+    return true;
+}
+
+// u vector of family row iu (0: C~, 1+a: Q_a), v vector of column iv (0: B, 1+b: P_b)
+template <int RK>
+__device__ __forceinline__ float2 fam_u(const float2* Ct, const float2* Q, size_t hn, int iu) {
+    return iu == 0 ? Ct[hn] : Q[hn * RK + (iu - 1)];
+}
+template <int RK>
+__device__ __forceinline__ float2 fam_v(const float2* Bv, const float2* P, size_t hn, int iv) {
+    return iv == 0 ? Bv[hn] : P[hn * RK + (iv - 1)];
+}
+
+// Slow path for one root whose fast sums are not finite: exact resonance test,
+// else the sums again with a scaled complex reciprocal.
+template <int RK>
+__device__ __forceinline__ bool root_recheck(int N, size_t hbase, float st, const float2* Lambda, const float2* P,
+                                          const float2* Q, const float2* Bv, const float2* Ct,
+                                          float2 (&acc)[Fam<RK>::F]) {
+    for (int n = 0; n < N; ++n) {
+        const float2 lam = Lambda[hbase + n];
+        const float x = -lam.x, y = st - lam.y;
+        if (x == 0.0f && y == 0.0f) return false;
+    }
+#pragma unroll
+    for (int f = 0; f < Fam<RK>::F; ++f) acc[f] = make_float2(0.f, 0.f);
+    for (int n = 0; n < N; ++n) {
+        const float2 lam = Lambda[hbase + n];
+        const float2 g = cdivf(make_float2(1.f, 0.f), make_float2(-lam.x, st - lam.y));
+        const float2 gs = (isfinite(g.x) && isfinite(g.y))
+                              ? g
+                              : c_from(z_inv(make_double2(-(double)lam.x, (double)st - (double)lam.y)));
+#pragma unroll
+        for (int iu = 0; iu <= RK; ++iu)
+#pragma unroll
+            for (int iv = 0; iv <= RK; ++iv) {
+                const float2 w = c_mul(c_conj(fam_u<RK>(Ct, Q, hbase + n, iu)), fam_v<RK>(Bv, P, hbase + n, iv));
+                acc[iu * (RK + 1) + iv] = c_add(acc[iu * (RK + 1) + iv], c_mul(w, gs));
+            }
+    }
+    return true;
+}
+
+template <int RK, int RPT>
+__global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
+    int M, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
+    const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
+    const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status) {
+    constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW;
+    __shared__ float4 tbl[kChunk * ROW];
+    __shared__ int blk_status;
+
+    const int h = blockIdx.x / tiles;
+    const int tile = blockIdx.x - h * tiles;
+    const int tid = threadIdx.x;
+    const size_t hbase = (size_t)h * N;
+    const float dtv = dt[h];
+
+    if (!(dtv > 0.0f) || !(dtv <= FLT_MAX)) {  // uniform over the workgroup
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int k = tile * (kCauchyThreads * RPT) + i * kCauchyThreads + tid;
+            if (k < M) roots[(size_t)h * M + k] = c_nan();
+        }
+        if (tid == 0) tile_status[blockIdx.x] = SSM_ST_INVALID_STEP;
+        return;
+    }
+    if (tid == 0) blk_status = 0;
+
+    const double a = 2.0 / (double)dtv;
+    float st[RPT], tf[RPT];
+    int kk[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int k = tile * (kCauchyThreads * RPT) + i * kCauchyThreads + tid;
+        kk[i] = k;
+        st[i] = 0.0f;
+        tf[i] = 0.0f;
+        if (k < M && 2 * k != M) {
+            double s, c;
+            sincospi((double)k / (double)M, &s, &c);
+            const double t = s / c;
+            st[i] = (float)(a * t);
+            tf[i] = (float)t;
+        }
+    }
+
+    float2 acc[RPT][F];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+#pragma unroll
+        for (int f = 0; f < F; ++f) acc[i][f] = make_float2(0.f, 0.f);
+
+    for (int n0 = 0; n0 < N; n0 += kChunk) {
+        const int nch = min(kChunk, N - n0);
+        __syncthreads();
+        if (tid < nch) {
+            const size_t hn = hbase + n0 + tid;
+            const float2 lam = Lambda[hn];
+            const float x = -lam.x;
+            tbl[tid * ROW] = make_float4(x * x, lam.y, x, 0.f);
+            float2 uu[RK + 1], vv[RK + 1];
+            uu[0] = Ct[hn];
+            vv[0] = Bv[hn];
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                uu[1 + j] = Q[hn * RK + j];
+                vv[1 + j] = P[hn * RK + j];
+            }
+#pragma unroll
+            for (int iu = 0; iu <= RK; ++iu)
+#pragma unroll
+                for (int iv = 0; iv <= RK; ++iv) {
+                    const float2 w = c_mul(c_conj(uu[iu]), vv[iv]);
+                    tbl[tid * ROW + 1 + iu * (RK + 1) + iv] = make_float4(w.x * x, w.y * x, w.y, -w.x);
+                }
+        }
+        __syncthreads();
+        for (int n = 0; n < nch; ++n) {
+            const float4 hd = tbl[n * ROW];
+            float inv[RPT], p[RPT];
+#pragma unroll
+            for (int i = 0; i < RPT; ++i) {
+                const float y = st[i] - hd.y;
+                const float den = fmaf(y, y, hd.x);
+                inv[i] = __builtin_amdgcn_rcpf(den);
+                p[i] = y * inv[i];
+            }
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const float4 w = tbl[n * ROW + 1 + f];
+#pragma unroll
+                for (int i = 0; i < RPT; ++i) {
+                    acc[i][f].x = fmaf(w.x, inv[i], acc[i][f].x);
+                    acc[i][f].x = fmaf(w.z, p[i], acc[i][f].x);
+                    acc[i][f].y = fmaf(w.y, inv[i], acc[i][f].y);
+                    acc[i][f].y = fmaf(w.w, p[i], acc[i][f].y);
+                }
+            }
+        }
+    }
+
+    int my_status = 0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int k = kk[i];
+        if (k >= M) continue;
+        float2 H;
+        if (2 * k == M) {
+            // z = -1: (dt/2) C~^* B
+            double sx = 0.0, sy = 0.0;
+            for (int n = 0; n < N; ++n) {
+                const float2 c = Ct[hbase + n], b = Bv[hbase + n];
+                sx += (double)c.x * b.x + (double)c.y * b.y;
+                sy += (double)c.x * b.y - (double)c.y * b.x;
+            }
+            H = make_float2((float)(0.5 * dtv * sx), (float)(0.5 * dtv * sy));
+        } else {
+            bool finite = true;
+#pragma unroll
+            for (int f = 0; f < F; ++f) finite = finite && isfinite(acc[i][f].x) && isfinite(acc[i][f].y);
+            bool resonant = false;
+            if (!finite) resonant = !root_recheck<RK>(N, hbase, st[i], Lambda, P, Q, Bv, Ct, acc[i]);
+            if (resonant) {
+                my_status = max(my_status, SSM_ST_RESONANT_DIAGONAL);
+                H = c_nan();
+            } else {
+                float2 W[RK][RK], rhs[RK];
+#pragma unroll
+                for (int r1 = 0; r1 < RK; ++r1) {
+                    rhs[r1] = acc[i][(1 + r1) * (RK + 1)];
+#pragma unroll
+                    for (int c1 = 0; c1 < RK; ++c1) {
+                        W[r1][c1] = acc[i][(1 + r1) * (RK + 1) + 1 + c1];
+                        if (r1 == c1) W[r1][c1].x += 1.0f;
+                    }
+                }
+                if (!small_solve<RK>(W, rhs)) {
+                    my_status = max(my_status, SSM_ST_RESONANT_CORRECTION);
+                    H = c_nan();
+                } else {
+                    float2 s = acc[i][0];
+#pragma unroll
+                    for (int b1 = 0; b1 < RK; ++b1) s = c_sub(s, c_mul(acc[i][1 + b1], rhs[b1]));
+                    H = c_mul(make_float2(1.0f, tf[i]), s);
+                }
+            }
+        }
+        roots[(size_t)h * M + k] = H;
+    }
+    if (my_status) atomicMax(&blk_status, my_status);
+    __syncthreads();
+    if (tid == 0) tile_status[blockIdx.x] = blk_status;
+}
+
+template <int RK, int RPT>
+hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, const float2* P, const float2* Q,
+                     const float2* Bv, const float2* Ct, const float* dt, float2* roots, int32_t* tstat,
+                     hipStream_t stream) {
+    const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
+    const int64_t blocks = H * tiles;
+    hipLaunchKernelGGL((cauchy_roots_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream,
+                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int cauchy_rpt(int64_t r) { return r == 1 ? 4 : r == 2 ? 2 : 1; }
+
+int64_t cauchy_tiles(int64_t r, int64_t M) {
+    const int64_t per = (int64_t)kCauchyThreads * cauchy_rpt(r);
+    return (M + per - 1) / per;
+}
+
+hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
+                         const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
+                         int32_t* tile_status, hipStream_t stream) {
+    switch (r) {
+        case 1: return launch_rk<1, 4>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+        case 2: return launch_rk<2, 2>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+        case 3: return launch_rk<3, 1>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+        case 4: return launch_rk<4, 1>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssm

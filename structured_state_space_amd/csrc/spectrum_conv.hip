@@ -1,0 +1,253 @@
+// Kernel transform and long causal convolution, LDS-resident (M <= 16384).
+//
+// Sources: "Recurrent, LSTM, and structured state-space models" -- filter-mode
+// block (the kernel is the first L coefficients of the inverse radix-two
+// transform of the root values), DPLR block (y_t = C^* x_t + D u_t, the skip term
+// is separate) and radix-two DFT block (an exact polynomial product by zero
+// padding to a radix-two length >= 2n - 1).
+//
+// Convolution by the zero-padded length-2M product, split into its even and odd
+// frequencies.  With k the length-M real kernel (taps j >= L zero, D added at
+// j = 0) and z a zero-padded input row, let tw_j = exp(-i pi j/M):
+//   cyclic:   c = IFFT_M(FFT_M(z) . FFT_M(k))
+//   twisted:  n = conj(tw) . IFFT_M(FFT_M(tw . z) . FFT_M(tw . k))
+// (the even and odd bins of the 2M-point transform), and the linear product is
+// (c + n)/2 on j < M.  Both inverse transforms are left unscaled; the spectra
+// carry the factor 1/(2M).  Two batch rows of one channel are convolved at once
+// as z = u_b + i u_{b+1}: the kernel is real, so the real and imaginary parts of
+// the result are the two rows' outputs.
+#include "common.hpp"
+#include "fft.hpp"
+
+namespace ssm {
+
+namespace {
+
+template <int LOGM>
+struct Geo {
+    static constexpr int M = 1 << LOGM;
+    static constexpr int LOGE = fft_loge(LOGM);
+    static constexpr int E = 1 << LOGE;
+    static constexpr int T = M >> LOGE;  // threads per transform
+    static constexpr int LDS = lds_padded_size(M);
+    // transforms per conv workgroup: about 256 threads, within 160 KB of LDS
+    static constexpr int G = T >= 256 ? 1 : 256 / T;
+    // register budget: 128 VGPRs (4 waves per SIMD) up to M = 8192, 256 above
+    static constexpr int WAVES = LOGM >= 14 ? 2 : 4;
+};
+
+// Spectra of the kernel: khat[h][0] = FFT_M(k)/(2M), khat[h][1] = FFT_M(tw k)/(2M).
+// FROM_ROOTS: k comes from the inverse transform of the root values (and is also
+// written to K_out); otherwise k is read from a caller's real kernel.
+template <int LOGM, bool FROM_ROOTS>
+__global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void spectrum_kernel(
+    int L, int tiles, const float2* __restrict__ roots, const int32_t* __restrict__ tile_status,
+    const float* __restrict__ Kin, int64_t kstride, const float* __restrict__ D, float2* __restrict__ K_out,
+    int32_t* __restrict__ status, float2* __restrict__ khat) {
+    using Gm = Geo<LOGM>;
+    constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE;
+    __shared__ float2 lds[Gm::LDS];
+    __shared__ int sst;
+    const int h = blockIdx.x;
+    const int t = threadIdx.x;
+    float2* kh0 = khat ? khat + (size_t)h * 2 * M : nullptr;  // null: kernel transform only
+    float2* kh1 = khat ? kh0 + M : nullptr;
+    float kr[E];
+
+    if constexpr (FROM_ROOTS) {
+        if (t == 0) sst = 0;
+        __syncthreads();
+        int mx = 0;
+        for (int i = t; i < tiles; i += T) mx = max(mx, tile_status[(size_t)h * tiles + i]);
+        if (mx) atomicMax(&sst, mx);
+        __syncthreads();
+        const int st = sst;
+        if (t == 0 && status) status[h] = st;
+        if (st != 0) {  // uniform: NaN-fill this channel's outputs
+            for (int j = t; j < L; j += T)
+                if (K_out) K_out[(size_t)h * L + j] = c_nan();
+            if (khat)
+                for (int j = t; j < M; j += T) {
+                    kh0[j] = c_nan();
+                    kh1[j] = c_nan();
+                }
+            return;
+        }
+        float2 v[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[e] = roots[(size_t)h * M + t + T * e];
+        fft_block<LOGM, LOGE, true>(v, lds, t);
+        const float invM = 1.0f / (float)M;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            v[e] = c_scale(v[e], invM);
+            if (K_out && j < L) K_out[(size_t)h * L + j] = v[e];
+            kr[e] = j < L ? v[e].x : 0.0f;
+        }
+        if (!khat) return;  // uniform
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            kr[e] = j < L ? Kin[((size_t)h * L + j) * kstride] : 0.0f;
+        }
+    }
+    if (t == 0 && D) kr[0] += D[h];
+
+    const float sc = 1.0f / (float)(2 * M);
+    float2 v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = make_float2(kr[e] * sc, 0.0f);
+    fft_block<LOGM, LOGE, false>(v, lds, t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) kh0[t + T * e] = v[e];
+
+    const float2 step = root_of_unity<false>(T, 2 * M);
+    float2 tw = root_of_unity<false>(t, 2 * M);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        v[e] = c_scale(tw, kr[e] * sc);
+        tw = c_mul(tw, step);
+    }
+    fft_block<LOGM, LOGE, false>(v, lds, t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) kh1[t + T * e] = v[e];
+}
+
+// One transform group per pair of batch rows (b, b+1) of one channel.
+template <int LOGM>
+__global__ __launch_bounds__(Geo<LOGM>::G * Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
+    int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
+    float* __restrict__ y, const float2* __restrict__ khat) {
+    using Gm = Geo<LOGM>;
+    constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE, G = Gm::G;
+    __shared__ float2 lds[G * Gm::LDS];
+    const int grp = threadIdx.x / T;
+    const int t = threadIdx.x - grp * T;
+
+    int64_t wg = blockIdx.x;
+    if (remap_bpc > 0) {  // keep the blocks of one channel on one XCD (dispatch is round-robin over 8)
+        const int64_t x = wg & 7, s = wg >> 3;
+        wg = ((s / remap_bpc) * 8 + x) * remap_bpc + s % remap_bpc;
+    }
+    const int64_t pair = wg * G + grp;
+    const bool active = pair < npairs;
+    const int h = active ? (int)(pair / npb) : 0;
+    const int b1 = active ? 2 * (int)(pair - (int64_t)h * npb) : 0;
+    const bool has2 = active && (b1 + 1 < Bsz);
+    const size_t row1 = ((size_t)b1 * H + h) * (size_t)L;
+    const size_t row2 = row1 + (size_t)H * L;
+    float2* my = lds + grp * Gm::LDS;
+    const float2* kh0 = khat + (size_t)h * 2 * M;
+    const float2* kh1 = kh0 + M;
+
+    // cyclic half
+    float2 v[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        const bool in = active && j < L;
+        v[e] = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+    }
+    fft_block<LOGM, LOGE, false>(v, my, t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = c_mul(v[e], kh0[t + T * e]);
+    fft_block<LOGM, LOGE, true>(v, my, t);
+    float2 acc[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] = v[e];
+
+    // twisted half (the input row is read again: it is still in cache)
+    const float2 step = root_of_unity<false>(T, 2 * M);
+    const float2 tw0 = root_of_unity<false>(t, 2 * M);
+    float2 tw = tw0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        const bool in = active && j < L;
+        const float2 zz = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+        v[e] = c_mul(zz, tw);
+        tw = c_mul(tw, step);
+    }
+    fft_block<LOGM, LOGE, false>(v, my, t);
+#pragma unroll
+    for (int e = 0; e < E; ++e) v[e] = c_mul(v[e], kh1[t + T * e]);
+    fft_block<LOGM, LOGE, true>(v, my, t);
+    tw = tw0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        acc[e] = c_add(acc[e], c_mul(v[e], c_conj(tw)));
+        tw = c_mul(tw, step);
+    }
+
+    if (active) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            if (j < L) {
+                y[row1 + j] = acc[e].x;
+                if (has2) y[row2 + j] = acc[e].y;
+            }
+        }
+    }
+}
+
+template <int LOGM>
+hipError_t spectrum_launch(bool from_roots, int64_t H, int64_t L, int64_t tiles, const float2* roots,
+                           const int32_t* tstat, const float* Kin, int64_t kstride, const float* D, float2* K_out,
+                           int32_t* status, float2* khat, hipStream_t stream) {
+    using Gm = Geo<LOGM>;
+    if (from_roots)
+        hipLaunchKernelGGL((spectrum_kernel<LOGM, true>), dim3((unsigned)H), dim3(Gm::T), 0, stream, (int)L,
+                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat);
+    else
+        hipLaunchKernelGGL((spectrum_kernel<LOGM, false>), dim3((unsigned)H), dim3(Gm::T), 0, stream, (int)L,
+                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat);
+    return hipGetLastError();
+}
+
+template <int LOGM>
+hipError_t conv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y, const float2* khat,
+                       hipStream_t stream) {
+    using Gm = Geo<LOGM>;
+    const int64_t npb = (Bsz + 1) / 2;
+    const int64_t npairs = npb * H;
+    const int64_t blocks = (npairs + Gm::G - 1) / Gm::G;
+    int remap = 0;
+    if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
+    hipLaunchKernelGGL((conv_kernel<LOGM>), dim3((unsigned)blocks), dim3(Gm::G * Gm::T), 0, stream, (int)Bsz,
+                       (int)H, (int)L, (int)npb, npairs, remap, u, y, khat);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                           const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
+                           float2* K_out, int32_t* status, float2* khat, hipStream_t stream) {
+    switch (ilog2_exact(M)) {
+#define SSM_SPEC_CASE(LG) \
+    case LG: return spectrum_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat, stream);
+        SSM_SPEC_CASE(0) SSM_SPEC_CASE(1) SSM_SPEC_CASE(2) SSM_SPEC_CASE(3) SSM_SPEC_CASE(4)
+        SSM_SPEC_CASE(5) SSM_SPEC_CASE(6) SSM_SPEC_CASE(7) SSM_SPEC_CASE(8) SSM_SPEC_CASE(9)
+        SSM_SPEC_CASE(10) SSM_SPEC_CASE(11) SSM_SPEC_CASE(12) SSM_SPEC_CASE(13) SSM_SPEC_CASE(14)
+#undef SSM_SPEC_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
+                       hipStream_t stream) {
+    switch (ilog2_exact(M)) {
+#define SSM_CONV_CASE(LG) \
+    case LG: return conv_launch<LG>(Bsz, H, L, u, y, khat, stream);
+        SSM_CONV_CASE(0) SSM_CONV_CASE(1) SSM_CONV_CASE(2) SSM_CONV_CASE(3) SSM_CONV_CASE(4)
+        SSM_CONV_CASE(5) SSM_CONV_CASE(6) SSM_CONV_CASE(7) SSM_CONV_CASE(8) SSM_CONV_CASE(9)
+        SSM_CONV_CASE(10) SSM_CONV_CASE(11) SSM_CONV_CASE(12) SSM_CONV_CASE(13) SSM_CONV_CASE(14)
+#undef SSM_CONV_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace ssm

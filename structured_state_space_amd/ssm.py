@@ -1,0 +1,215 @@
+"""Python binding of the C ABI in include/ssm.h (argument marshalling only).
+
+Every step of the filter path runs in the HIP library; this module only checks
+tensor shapes and dtypes, allocates workspaces with torch, and passes device
+pointers plus torch's current HIP stream.  Importing it loads the in-tree
+library built by structured_state_space_amd/build.py and raises ImportError
+when it is missing: there is no CPU fallback.
+
+torch is imported first so that the library binds to the HIP runtime torch has
+already loaded (both use the libamdhip64.so.7 soname).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "_lib", "libssm_hip.so")
+
+# return codes and statuses, as declared in include/ssm.h
+OK = 0
+ERR_INVALID_ARGUMENT = 1
+ERR_WORKSPACE = 2
+ERR_DEVICE = 3
+ERR_UNSUPPORTED = 4
+ST_OK = 0
+ST_RESONANT_CORRECTION = 16
+ST_RESONANT_DIAGONAL = 17
+ST_SINGULAR_BILINEAR = 18
+ST_INVALID_STEP = 19
+OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD = 0, 1, 2, 3
+
+EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_status_string", "ssm_discretize",
+           "ssm_kernel_gen", "ssm_fftconv", "ssm_forward")
+
+
+class SSMError(RuntimeError):
+    def __init__(self, fn, code):
+        super().__init__(f"{fn} failed: {status_string(code)} (code {code})")
+        self.code = code
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"HIP library not built: {_LIB_PATH} is missing "
+                          "(run `python -c 'import __graft_entry__ as g; g.build()'`)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, vp, sz, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.ssm_workspace_bytes.argtypes = [i32, i64, i64, i64, i64, i64, ctypes.POINTER(sz)]
+    lib.ssm_workspace_bytes.restype = i32
+    lib.ssm_transform_lengths.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
+    lib.ssm_transform_lengths.restype = i32
+    lib.ssm_status_string.argtypes = [i32]
+    lib.ssm_status_string.restype = ctypes.c_char_p
+    lib.ssm_discretize.argtypes = [i64, i64, i64, i64] + [vp] * 10 + [vp, sz, vp]
+    lib.ssm_discretize.restype = i32
+    lib.ssm_kernel_gen.argtypes = [i64, i64, i64, i64] + [vp] * 9 + [vp, sz, vp]
+    lib.ssm_kernel_gen.restype = i32
+    lib.ssm_fftconv.argtypes = [i64, i64, i64, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.ssm_fftconv.restype = i32
+    lib.ssm_forward.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp]
+    lib.ssm_forward.restype = i32
+    return lib
+
+
+lib = _load()
+
+
+def status_string(code: int) -> str:
+    return lib.ssm_status_string(int(code)).decode()
+
+
+def transform_lengths(L: int):
+    M, n = ctypes.c_int64(), ctypes.c_int64()
+    rc = lib.ssm_transform_lengths(int(L), ctypes.byref(M), ctypes.byref(n))
+    if rc != OK:
+        raise SSMError("ssm_transform_lengths", rc)
+    return M.value, n.value
+
+
+def workspace_bytes(op: int, Bsz: int, H: int, N: int, r: int, L: int) -> int:
+    out = ctypes.c_size_t()
+    rc = lib.ssm_workspace_bytes(int(op), int(Bsz), int(H), int(N), int(r), int(L), ctypes.byref(out))
+    if rc != OK:
+        raise SSMError("ssm_workspace_bytes", rc)
+    return out.value
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or tuple(t.shape) != tuple(shape):
+        got = (None if not isinstance(t, torch.Tensor) else (t.dtype, tuple(t.shape)))
+        raise ValueError(f"{name}: expected {dtype} {tuple(shape)}, got {got}")
+    if not t.is_cuda or t.device != device:
+        raise ValueError(f"{name}: must be on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _params(Lambda, P, Q, B, Cv, dt):
+    H, N = Lambda.shape
+    r = P.shape[2]
+    dev = Lambda.device
+    _check(Lambda, "Lambda", torch.complex64, (H, N), dev)
+    _check(P, "P", torch.complex64, (H, N, r), dev)
+    _check(Q, "Q", torch.complex64, (H, N, r), dev)
+    _check(B, "B", torch.complex64, (H, N), dev)
+    _check(Cv, "C", torch.complex64, (H, N), dev)
+    _check(dt, "dt", torch.float32, (H,), dev)
+    return H, N, r, dev
+
+
+def _workspace(nbytes, device, workspace=None):
+    if workspace is not None:
+        if workspace.numel() * workspace.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return workspace
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def discretize(Lambda, P, Q, B, C, dt, L, want_bbar=True, want_abar=False, want_ctilde=True):
+    """ssm_discretize: returns dict(Bbar, Abar, Ctilde, status) (None where not asked)."""
+    H, N, r, dev = _params(Lambda, P, Q, B, C, dt)
+    Bbar = torch.empty((H, N), dtype=torch.complex64, device=dev) if want_bbar else None
+    Abar = torch.empty((H, N, N), dtype=torch.complex64, device=dev) if want_abar else None
+    Ct = torch.empty((H, N), dtype=torch.complex64, device=dev) if want_ctilde else None
+    status = torch.empty((H,), dtype=torch.int32, device=dev)
+    rc = lib.ssm_discretize(H, N, r, int(L), _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(C), _ptr(dt),
+                            _ptr(Bbar), _ptr(Abar), _ptr(Ct), _ptr(status), None, 0, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_discretize", rc)
+    return dict(Bbar=Bbar, Abar=Abar, Ctilde=Ct, status=status)
+
+
+def kernel_gen(Lambda, P, Q, B, Ctilde, dt, L, want_kernel=True, want_roots=False, workspace=None):
+    """ssm_kernel_gen: returns dict(K [H,L] c64, roots [H,M] c64, status [H] i32)."""
+    H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
+    M, _ = transform_lengths(L)
+    K = torch.empty((H, L), dtype=torch.complex64, device=dev) if want_kernel else None
+    roots = torch.empty((H, M), dtype=torch.complex64, device=dev) if want_roots else None
+    status = torch.empty((H,), dtype=torch.int32, device=dev)
+    nbytes = workspace_bytes(OP_KERNEL_GEN, 1, H, N, r, L)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.ssm_kernel_gen(H, N, r, int(L), _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt),
+                            _ptr(K), _ptr(roots), _ptr(status), _ptr(ws), nbytes, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_kernel_gen", rc)
+    return dict(K=K, roots=roots, status=status)
+
+
+def fftconv(K, u, D=None, y=None, workspace=None):
+    """ssm_fftconv: y = K * u + D u.  K: float32 [H,L] or complex64 [H,L] (real part used)."""
+    Bsz, H, L = u.shape
+    dev = u.device
+    _check(u, "u", torch.float32, (Bsz, H, L), dev)
+    if K.dtype == torch.complex64:
+        _check(K, "K", torch.complex64, (H, L), dev)
+        stride = 2
+    else:
+        _check(K, "K", torch.float32, (H, L), dev)
+        stride = 1
+    _check(D, "D", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", torch.float32, (Bsz, H, L), dev)
+    nbytes = workspace_bytes(OP_FFTCONV, Bsz, H, 1, 1, L)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.ssm_fftconv(Bsz, H, L, _ptr(K), stride, _ptr(D), _ptr(u), _ptr(y), _ptr(ws), nbytes, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_fftconv", rc)
+    return y
+
+
+def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=None, status=None,
+            workspace=None):
+    """ssm_forward: returns dict(y [Bsz,H,L] f32, K [H,L] c64 or None, status [H] i32)."""
+    H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
+    Bsz, H2, L = u.shape
+    if H2 != H:
+        raise ValueError("u: channel count does not match the parameters")
+    _check(u, "u", torch.float32, (Bsz, H, L), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", torch.float32, (Bsz, H, L), dev)
+    if K_out is None and want_kernel:
+        K_out = torch.empty((H, L), dtype=torch.complex64, device=dev)
+    _check(K_out, "K_out", torch.complex64, (H, L), dev)
+    if status is None:
+        status = torch.empty((H,), dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, (H,), dev)
+    nbytes = workspace_bytes(OP_FORWARD, Bsz, H, N, r, L)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.ssm_forward(Bsz, H, N, r, L, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt),
+                         _ptr(D), _ptr(u), _ptr(y), _ptr(K_out), _ptr(status), _ptr(ws), nbytes, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_forward", rc)
+    return dict(y=y, K=K_out, status=status)
+
+
+def to_device(params, device="cuda:0"):
+    """Move an inputs.Params (numpy) to torch device tensors (a plain copy)."""
+    f = lambda a: torch.from_numpy(a).to(device)
+    return dict(Lambda=f(params.Lambda), P=f(params.P), Q=f(params.Q), B=f(params.B), C=f(params.C),
+                dt=f(params.dt), D=f(params.D))

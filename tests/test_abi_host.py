@@ -1,0 +1,115 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it loads, exports
+every function include/ssm.h declares, sizes transforms bit-exactly, and
+rejects bad arguments before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssm.h")
+
+ssm = pytest.importorskip("structured_state_space_amd.ssm", reason="HIP library not built")
+import oracle as O  # noqa: E402
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert set(declared) == set(ssm.EXPORTS)
+    for name in declared:
+        assert hasattr(ssm.lib, name), name
+    out = os.popen(f"nm -D --defined-only {ssm._LIB_PATH}").read()
+    for name in declared:
+        assert re.search(rf"\bT {name}\b", out), f"{name} not exported"
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 5, 64, 100, 1000, 1024, 1025, 3000, 16384, 65536, 65537, 10**6])
+def test_transform_lengths_bit_exact(L):
+    assert ssm.transform_lengths(L) == (O.transform_length(L), O.conv_length(L))
+
+
+def test_transform_lengths_rejects_nonpositive():
+    with pytest.raises(ssm.SSMError):
+        ssm.transform_lengths(0)
+
+
+def test_status_strings():
+    assert ssm.status_string(ssm.ST_RESONANT_DIAGONAL) == O.RESONANT_DIAGONAL
+    assert ssm.status_string(ssm.ST_RESONANT_CORRECTION) == O.RESONANT_CORRECTION
+    assert ssm.status_string(ssm.ST_SINGULAR_BILINEAR) == O.SINGULAR_BILINEAR
+    assert ssm.status_string(ssm.OK) == "ok"
+    assert ssm.status_string(12345) == "unknown code"
+
+
+def test_workspace_sizes():
+    # forward: roots [H,M] c64 + tile statuses + spectra [H,2,M] c64, each 256-aligned
+    H, M = 256, 1024
+    ws = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 1024)
+    assert ws >= H * M * 8 + H * 2 * M * 8
+    assert ws % 256 == 0
+    assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8
+    # ragged L uses M = next power of two
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 3000) == 3 * 2 * 4096 * 8
+
+
+@pytest.mark.parametrize("args,code", [
+    ((ssm.OP_FORWARD, 8, 0, 64, 1, 1024), ssm.ERR_INVALID_ARGUMENT),
+    ((ssm.OP_FORWARD, 0, 4, 64, 1, 1024), ssm.ERR_INVALID_ARGUMENT),
+    ((ssm.OP_FORWARD, 8, 4, 0, 1, 1024), ssm.ERR_INVALID_ARGUMENT),
+    ((ssm.OP_FORWARD, 8, 4, 64, 0, 1024), ssm.ERR_INVALID_ARGUMENT),
+    ((ssm.OP_FORWARD, 8, 4, 64, 5, 1024), ssm.ERR_UNSUPPORTED),
+    ((ssm.OP_FORWARD, 8, 4, 64, 1, 0), ssm.ERR_INVALID_ARGUMENT),
+    ((ssm.OP_FORWARD, 8, 4, 64, 1, 65537), ssm.ERR_UNSUPPORTED),
+    ((ssm.OP_DISCRETIZE, 1, 4, 5000, 1, 16), ssm.ERR_UNSUPPORTED),
+    ((7, 1, 4, 64, 1, 16), ssm.ERR_INVALID_ARGUMENT),
+])
+def test_workspace_query_rejects(args, code):
+    out = ctypes.c_size_t(123)
+    assert ssm.lib.ssm_workspace_bytes(*args, ctypes.byref(out)) == code
+    assert out.value == 123
+
+
+FAKE = 0x10000000  # aligned dummy address: validation fails before any use
+
+
+def _fwd(**kw):
+    a = dict(Bsz=2, H=3, N=4, r=1, L=16, Lambda=FAKE, P=FAKE, Q=FAKE, B=FAKE, Ct=FAKE, dt=FAKE, D=None,
+             u=FAKE, y=FAKE, K=None, status=None, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return ssm.lib.ssm_forward(a["Bsz"], a["H"], a["N"], a["r"], a["L"], a["Lambda"], a["P"], a["Q"], a["B"],
+                               a["Ct"], a["dt"], a["D"], a["u"], a["y"], a["K"], a["status"], a["ws"],
+                               a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(L=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(r=9), ssm.ERR_UNSUPPORTED),
+    (dict(Lambda=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(u=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(Ct=FAKE + 4), ssm.ERR_INVALID_ARGUMENT),    # complex array not 8-byte aligned
+    (dict(u=FAKE + 2), ssm.ERR_INVALID_ARGUMENT),     # float array not 4-byte aligned
+    (dict(ws=FAKE + 64), ssm.ERR_INVALID_ARGUMENT),   # workspace not 256-byte aligned
+    (dict(ws_bytes=16), ssm.ERR_WORKSPACE),
+    (dict(ws=None), ssm.ERR_WORKSPACE),
+])
+def test_forward_rejects_before_launch(kw, code):
+    assert _fwd(**kw) == code
+
+
+def test_fftconv_and_kernel_gen_reject():
+    lib = ssm.lib
+    assert lib.ssm_fftconv(1, 1, 16, FAKE, 3, None, FAKE, FAKE, FAKE, 1 << 20, None) == ssm.ERR_INVALID_ARGUMENT
+    assert lib.ssm_fftconv(1, 1, 16, FAKE, 1, None, FAKE, FAKE, FAKE, 8, None) == ssm.ERR_WORKSPACE
+    assert lib.ssm_kernel_gen(1, 4, 1, 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, None, FAKE, 1 << 20,
+                              None) == ssm.ERR_INVALID_ARGUMENT
+    assert lib.ssm_discretize(1, 4, 1, 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None, None, 0,
+                              None) == ssm.ERR_INVALID_ARGUMENT
