@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Throughput of the S4 filter path on one MI355X (gfx950).
+
+A step is one call of ssm_forward on one batch of synthetic input: root values
+by the Cauchy/Woodbury kernel, inverse transform to the kernel and its
+convolution spectra, and the fused FFT convolution y = K * u + D u.  The
+truncated-output vector C~ is formed once beforehand by ssm_discretize, off the
+timer (the pages count filter evaluation from a supplied C~); its time is
+reported separately.  All inputs are resident in HBM before timing starts.
+
+Prints one JSON line: the headline metric (channel-steps/s = Bsz*H*L per
+second), the roofline of the dominant kernel measured live with HIP events on
+the launch stream, and the complex128 CPU oracle timed on a bounded sample on
+this host.  --gpus N > 1 exits: this build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "channel-steps/sec (B·H·L) for S4 kernel-gen+FFT conv; % HBM/VALU roofline"
+UNIT = "channel-steps/s"
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed issue)
+DEFAULT_WORKLOAD = "s4-h256-l1k"
+
+KERNEL_SOURCES = {
+    "cauchy": ["cauchy.hip", "common.hpp"],
+    "spectrum": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
+    "conv": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
+}
+
+
+def source_hash(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "structured_state_space_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic(w, M):
+    """Per-launch algorithmic work of each kernel (definitions in the design notes)."""
+    H, N, r, L, B = w.H, w.N, w.r, w.L, w.Bsz
+    roots = M - 1 if M >= 2 else M                      # z = -1 takes its finite formula
+    return {
+        "cauchy": dict(bound="alu", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
+                       peak=PEAK_FP32_TFLOPS),
+        "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * 2 * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
+        "conv": dict(bound="hbm", unit="GB/s", work=8 * B * H * L + 4 * H * L + 4 * H, scale=1e-9,
+                     peak=PEAK_HBM_GBS),
+    }
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, scaled by
+    the copy-kernel calibration; None when absent or taken on other sources."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    def val(key):
+        m = re.search(rf"^{key}:\s*([0-9.eE+-]+|[0-9a-f]+)\s*$", text, re.M)
+        return m.group(1) if m else None
+    if val("source_sha") != source_hash(kernel):
+        return None
+    try:
+        fetch = float(val("fetch_kib_per_dispatch")) * float(val("copy_scale_fetch"))
+        write = float(val("write_kib_per_dispatch")) * float(val("copy_scale_write"))
+    except (TypeError, ValueError):
+        return None
+    return (fetch + write) * 1024.0
+
+
+def cpu_baseline(w, p, u, seconds):
+    """The oracle as it stands, one thread, on a bounded channel sample."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < w.H and time.perf_counter() - t0 < seconds:
+            c = p.channel(done)
+            O.channel_reference(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], c["D"], u[:, done, :], p.L)
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done * w.Bsz * w.L / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.H} channels x {w.Bsz} rows x {w.L} steps of workload {w.name}: "
+                      f"complex128 dense discretisation, kernel by matrix iteration, time-stepped recurrence "
+                      f"({dt:.1f} s, one thread)"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration) and exit")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the S4 filter path shards over channels with no exchange, "
+              "and this build measures the one-GPU share (use --gpus 1).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_each_way": n * 4, "launches": 5}))
+        return 0
+
+    from structured_state_space_amd import inputs as I
+    from structured_state_space_amd import ssm
+
+    w, p, u = I.workload(args.workload)
+    M, n_fft = ssm.transform_lengths(w.L)
+    d = ssm.to_device(p, dev)
+    ut = torch.from_numpy(u).to(dev)
+
+    # C~ once, off the timer
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    disc = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], w.L, want_bbar=False)
+    e1.record()
+    torch.cuda.synchronize()
+    discretize_ms = e0.elapsed_time(e1)
+    if int(disc["status"].abs().max()) != 0:
+        raise RuntimeError("discretisation reported a nonzero status")
+    Ct = disc["Ctilde"]
+
+    y = torch.empty_like(ut)
+    status = torch.empty(w.H, dtype=torch.int32, device=dev)
+    ws = torch.empty(ssm.workspace_bytes(ssm.OP_FORWARD, w.Bsz, w.H, w.N, w.r, w.L), dtype=torch.uint8,
+                     device=dev)
+
+    def step(events=None):
+        ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut, y=y, status=status,
+                    workspace=ws, events=events)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_events = start.elapsed_time(end) / args.steps
+    ms_per_step = max(ms_events, 1e3 * t_wall / args.steps)
+    if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
+        raise RuntimeError("forward produced a nonzero status or non-finite output")
+
+    # per-kernel durations, live, on the launch stream
+    names = ("cauchy", "spectrum", "conv")
+    acc = {k: 0.0 for k in names}
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(events=evs[i])
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for j, k in enumerate(names):
+            acc[k] += evs[i][j].elapsed_time(evs[i][j + 1])
+    phase_ms = {k: acc[k] / args.steps for k in names}
+
+    alg = algorithmic(w, M)
+    phases = {}
+    for k in names:
+        a = alg[k]
+        achieved = a["work"] * a["scale"] / (phase_ms[k] * 1e-3)
+        phases[k] = {"bound": a["bound"], "achieved": achieved, "peak": a["peak"], "unit": a["unit"],
+                     "frac": achieved / a["peak"], "ms": phase_ms[k], "work_per_launch": a["work"]}
+    dom = max(names, key=lambda k: phase_ms[k])
+    traffic = read_traffic(dom, w.name)
+    roofline = {"bound": phases[dom]["bound"], "achieved": phases[dom]["achieved"], "peak": phases[dom]["peak"],
+                "unit": phases[dom]["unit"], "frac": phases[dom]["frac"], "traffic": traffic, "kernel": dom}
+    troof_ms = (alg["cauchy"]["work"] / (PEAK_FP32_TFLOPS * 1e12) + alg["conv"]["work"] / (PEAK_HBM_GBS * 1e9)) * 1e3
+
+    value = w.Bsz * w.H * w.L / (ms_per_step * 1e-3)
+    out = {
+        "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "H": w.H, "N": w.N, "r": w.r, "L": w.L, "M": M, "n_fft": n_fft,
+                   "batch": w.Bsz},
+        "roofline": roofline,
+        "phases": phases,
+        "composite_roofline_frac": troof_ms / ms_per_step,
+        "ms_per_step_events": ms_events,
+        "discretize_ms_off_timer": discretize_ms,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, p, u, args.cpu_seconds)
+        out["cpu_baseline"]["cores_on_host"] = os.cpu_count()
+    print(json.dumps(out))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -6,15 +6,15 @@
 #include "common.hpp"
 
 namespace ssm {
-int64_t cauchy_tiles(int64_t r, int64_t M);
+int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, hipStream_t stream);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                           float2* K_out, int32_t* status, float2* khat, hipStream_t stream);
+                           float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
-                       hipStream_t stream);
+                       const float2* twtab, hipStream_t stream);
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                              const float2* Q, const float2* Bv, const float2* C, const float* dt, float2* Bbar,
                              float2* Abar, float2* Ct, int32_t* status, hipStream_t stream);
@@ -63,13 +63,16 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.roots_bytes = (size_t)H * M * sizeof(float2);
         off = align256(off + w.roots_bytes);
         w.tstat = off;
-        w.tstat_bytes = (size_t)H * cauchy_tiles(r, M) * sizeof(int32_t);
+        w.tstat_bytes = (size_t)H * cauchy_tiles(H, r, M) * sizeof(int32_t);
         off = align256(off + w.tstat_bytes);
     }
     if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {
         w.khat = off;
         w.khat_bytes = (size_t)H * 2 * M * sizeof(float2);
         off = align256(off + w.khat_bytes);
+        w.tw = off;
+        w.tw_bytes = (size_t)M * sizeof(float2);
+        off = align256(off + w.tw_bytes);
     }
     w.total = off;
     return w;
@@ -162,8 +165,8 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {
         // kernel transform only (spectra go to the workspace's unused tail: none needed here)
-        e = launch_spectrum(true, H, L, M, cauchy_tiles(r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
-                            status, nullptr, s);
+        e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
+                            status, nullptr, nullptr, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
     }
     return SSM_OK;
@@ -182,14 +185,21 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
     if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     float2* khat = (float2*)((char*)ws + w.khat);
-    hipError_t e = launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, s);
+    float2* twtab = (float2*)((char*)ws + w.tw);
+    hipError_t e =
+        launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
-    return device_status(launch_conv(Bsz, H, L, M, u, y, khat, s));
+    return device_status(launch_conv(Bsz, H, L, M, u, y, khat, twtab, s));
 }
 
-int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
-                const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
-                const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
+                 const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                 const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream,
+                 void* const* ev) {
     int rc = check_sizes(Bsz, H, N, r, L, true, true);
     if (rc != SSM_OK) return rc;
     const int64_t M = pow2_at_least(L);
@@ -208,13 +218,38 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const s
     float2* roots = (float2*)(base + w.roots);
     int32_t* tstat = (int32_t*)(base + w.tstat);
     float2* khat = (float2*)(base + w.khat);
+    float2* twtab = (float2*)(base + w.tw);
+    auto mark = [&](int i) { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
+    if (mark(0) != hipSuccess) return SSM_ERR_DEVICE;
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, s);
-    if (e != hipSuccess) return SSM_ERR_DEVICE;
-    e = launch_spectrum(true, H, L, M, cauchy_tiles(r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status, khat,
-                        s);
-    if (e != hipSuccess) return SSM_ERR_DEVICE;
-    return device_status(launch_conv(Bsz, H, L, M, u, y, khat, s));
+    if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
+    e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status, khat,
+                        twtab, s);
+    if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
+    e = launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
+    if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
+    return SSM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
+                const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
+    return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
+                        nullptr);
+}
+
+int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda,
+                         const ssm_c64* P, const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt,
+                         const float* D, const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws,
+                         size_t ws_bytes, void* stream, void* const* events) {
+    if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return SSM_ERR_INVALID_ARGUMENT;
+    return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
+                        events);
 }
 
 }  // extern "C"

@@ -291,23 +291,31 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, cons
 
 }  // namespace
 
-int cauchy_rpt(int64_t r) { return r == 1 ? 4 : r == 2 ? 2 : 1; }
+// roots per thread: the most this rank allows (more sums share each LDS row)
+// while the grid keeps at least 1024 workgroups (four waves per SIMD)
+int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
+    const int max_rpt = r == 1 ? 4 : r == 2 ? 2 : 1;
+    int rpt = max_rpt;
+    while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
+        rpt >>= 1;
+    return rpt;
+}
 
-int64_t cauchy_tiles(int64_t r, int64_t M) {
-    const int64_t per = (int64_t)kCauchyThreads * cauchy_rpt(r);
+int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
+    const int64_t per = (int64_t)kCauchyThreads * cauchy_rpt(H, r, M);
     return (M + per - 1) / per;
 }
 
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, hipStream_t stream) {
-    switch (r) {
-        case 1: return launch_rk<1, 4>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
-        case 2: return launch_rk<2, 2>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
-        case 3: return launch_rk<3, 1>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
-        case 4: return launch_rk<4, 1>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
-        default: return hipErrorInvalidValue;
-    }
+    const int rpt = cauchy_rpt(H, r, M);
+#define SSM_CAUCHY(RK, RPT) \
+    if (r == RK && rpt == RPT) return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
+    SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
+#undef SSM_CAUCHY
+    return hipErrorInvalidValue;
 }
 
 }  // namespace ssm

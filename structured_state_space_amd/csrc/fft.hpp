@@ -3,7 +3,7 @@
 // The transform follows the radix-two DFT of the pages' definition block
 // ("Radix-two discrete Fourier transform": forward root exp(-2 pi i/M), the
 // inverse uses the conjugate root; scaling is left to the caller), computed
-// as a self-sorting Stockham FFT with radix-2^LOGE passes:
+// as a self-sorting Stockham FFT with radix <= 16 passes:
 //
 //   * N = 2^LOGN points, E = 2^LOGE points per thread, T = N/E threads.
 //   * Register layout before and after the transform: thread t holds
@@ -14,8 +14,11 @@
 //     (b/Ns)*Ns*R + k + q*Ns.  Between passes the data goes through LDS; the
 //     last pass's outputs land in the thread's own register slots, so it needs
 //     no exchange.  A transform with P passes does P-1 LDS round trips.
-//   * The first pass takes the remainder radix (LOGN mod LOGE), so it carries
-//     no twiddles.
+//   * The first pass takes the remainder radix, so it carries no twiddles.
+//   * NV independent vectors of the same size can be transformed together:
+//     they share the twiddles and the workgroup barriers of every exchange.
+//   * Twiddles come from a functor tw(k, n) = exp(-2 pi i k/n) (forward sign);
+//     the inverse conjugates it.  Powers w^q are formed by repeated products.
 //
 // LDS addresses are padded by one complex every 16 to spread the strided
 // writes of the early passes over more banks.
@@ -74,66 +77,114 @@ __device__ __forceinline__ void dft_reg(float2 (&x)[R]) {
     }
 }
 
-template <int LOGN, int LOGE, bool INV, int LR, int LS, bool LAST>
-__device__ __forceinline__ void stockham_pass(float2 (&v)[1 << LOGE], float2* lds, int t) {
+// exact sin/cos of pi*num/den (den a power of two): the default twiddle source
+struct TwiddleSincos {
+    __device__ __forceinline__ float2 operator()(int k, int n) const { return root_of_unity<false>(k, n); }
+};
+
+// twiddles from a table tab[j] = exp(-i pi j/M), j < M (the 2M-th roots), for
+// transforms of length n dividing M: exp(-2 pi i k/n) = tab-entry 2kM/n,
+// using exp(-i pi (j + M)/M) = -exp(-i pi j/M) for the upper half
+struct TwiddleTable {
+    const float2* tab;
+    int logm;
+    __device__ __forceinline__ float2 operator()(int k, int n) const {
+        const int i = (k << (logm + 1)) >> ilog2_exact(n);  // 2kM/n < 2M
+        const int m = 1 << logm;
+        const float2 w = tab[i & (m - 1)];
+        return i >= m ? make_float2(-w.x, -w.y) : w;
+    }
+};
+
+template <int NV, int LOGN, int LOGE, bool INV, int LR, int LS, bool LAST, bool SHARED, class TW>
+__device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
+                                              const TW& tw) {
     constexpr int E = 1 << LOGE, N = 1 << LOGN, T = N >> LOGE, R = 1 << LR, NB = E / R, NS = 1 << LS;
+    if constexpr (NS > 1) {  // twiddles, shared by the NV vectors
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
-        const int b = t + i * T;
-        float2 x[R];
-#pragma unroll
-        for (int q = 0; q < R; ++q) x[q] = v[i + q * NB];
-        if constexpr (NS > 1) {
-            const int k = b & (NS - 1);
-            const float2 w = root_of_unity<INV>(k, NS * R);
+        for (int i = 0; i < NB; ++i) {
+            const int k = (t + i * T) & (NS - 1);
+            float2 w = tw(k, NS * R);
+            if (INV) w.y = -w.y;
             float2 wq = w;
 #pragma unroll
             for (int q = 1; q < R; ++q) {
-                x[q] = c_mul(x[q], wq);
+#pragma unroll
+                for (int s = 0; s < NV; ++s) v[s][i + q * NB] = c_mul(v[s][i + q * NB], wq);
                 if (q + 1 < R) wq = c_mul(wq, w);
             }
         }
-        dft_reg<R, INV>(x);
-        if constexpr (LAST) {
+    }
 #pragma unroll
-            for (int q = 0; q < R; ++q) v[i + q * NB] = x[q];
-        } else {
-            const int base = ((b >> LS) << (LS + LR)) + (b & (NS - 1));
+    for (int s = 0; s < NV; ++s) {
 #pragma unroll
-            for (int q = 0; q < R; ++q) lds[lds_pad(base + q * NS)] = x[q];
+        for (int i = 0; i < NB; ++i) {
+            const int b = t + i * T;
+            float2 x[R];
+#pragma unroll
+            for (int q = 0; q < R; ++q) x[q] = v[s][i + q * NB];
+            dft_reg<R, INV>(x);
+            if constexpr (LAST) {
+#pragma unroll
+                for (int q = 0; q < R; ++q) v[s][i + q * NB] = x[q];
+            } else {
+                const int base = ((b >> LS) << (LS + LR)) + (b & (NS - 1));
+#pragma unroll
+                for (int q = 0; q < R; ++q) lds[s][lds_pad(base + q * NS)] = x[q];
+            }
+        }
+        if constexpr (!LAST && SHARED) {  // one buffer for all vectors: exchange them in turn
+            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[s][e] = lds[s][lds_pad(t + T * e)];
+            __syncthreads();
         }
     }
-    if constexpr (!LAST) {
+    if constexpr (!LAST && !SHARED) {
         __syncthreads();
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = lds[lds_pad(t + T * e)];
+        for (int s = 0; s < NV; ++s)
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[s][e] = lds[s][lds_pad(t + T * e)];
         __syncthreads();
     }
 }
 
 // passes of radix 2^LRMAX, the remainder radix first
-template <int LOGN, int LOGE, int LRMAX, bool INV, int P = 0, int LS = 0>
-__device__ __forceinline__ void fft_passes(float2 (&v)[1 << LOGE], float2* lds, int t) {
+template <int NV, int LOGN, int LOGE, int LRMAX, bool INV, bool SHARED, class TW, int P = 0, int LS = 0>
+__device__ __forceinline__ void fft_passes(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
+                                           const TW& tw) {
     if constexpr (LOGN > 0) {
         constexpr int REM = LOGN % LRMAX;
         constexpr int NP = LOGN / LRMAX + (REM ? 1 : 0);
         if constexpr (P < NP) {
             constexpr int LR = (P == 0 && REM) ? REM : LRMAX;
-            stockham_pass<LOGN, LOGE, INV, LR, LS, P == NP - 1>(v, lds, t);
-            fft_passes<LOGN, LOGE, LRMAX, INV, P + 1, LS + LR>(v, lds, t);
+            stockham_pass<NV, LOGN, LOGE, INV, LR, LS, P == NP - 1, SHARED>(v, lds, t, tw);
+            fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, TW, P + 1, LS + LR>(v, lds, t, tw);
         }
     }
 }
 
-// Unscaled forward (INV=false) or inverse (INV=true) transform of N = 2^LOGN
-// points held as v[e] = x[t + T e]; every thread of the workgroup must call it
-// (it contains workgroup barriers).  lds: lds_padded_size(N) complex per
-// transform.  Requires LOGE <= LOGN (or LOGN == 0).  Butterflies are at most
-// radix 16; a thread with E > 16 points runs E/16 butterflies per pass.
+// Unscaled forward (INV=false) or inverse (INV=true) transforms of NV vectors of
+// N = 2^LOGN points, each held as v[s][e] = x_s[t + T e]; every thread of the
+// workgroup must call it (it contains workgroup barriers).  lds[s]:
+// lds_padded_size(N) complex per vector; SHARED: all lds[s] are one buffer and
+// the vectors are exchanged in turn.  Requires LOGE <= LOGN (or LOGN == 0).
+// Butterflies are at most radix 16; a thread with E > 16 points runs E/16
+// butterflies per pass.
+template <int NV, int LOGN, int LOGE, bool INV, bool SHARED = false, class TW>
+__device__ __forceinline__ void fft_multi(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
+                                          const TW& tw) {
+    static_assert(LOGN == 0 || (LOGE >= 1 && LOGE <= LOGN), "bad FFT split");
+    fft_passes<NV, LOGN, LOGE, (LOGE < 4 ? LOGE : 4), INV, SHARED, TW>(v, lds, t, tw);
+}
+
+// single vector, sin/cos twiddles
 template <int LOGN, int LOGE, bool INV>
 __device__ __forceinline__ void fft_block(float2 (&v)[1 << LOGE], float2* lds, int t) {
-    static_assert(LOGN == 0 || (LOGE >= 1 && LOGE <= LOGN), "bad FFT split");
-    fft_passes<LOGN, LOGE, (LOGE < 4 ? LOGE : 4), INV>(v, lds, t);
+    float2(&vv)[1][1 << LOGE] = *reinterpret_cast<float2(*)[1][1 << LOGE]>(&v);
+    float2* const l[1] = {lds};
+    fft_multi<1, LOGN, LOGE, INV>(vv, l, t, TwiddleSincos{});
 }
 
 // elements per thread used for an M-point transform: 16, or 32 at M = 16384 so

@@ -30,20 +30,28 @@ struct Geo {
     static constexpr int E = 1 << LOGE;
     static constexpr int T = M >> LOGE;  // threads per transform
     static constexpr int LDS = lds_padded_size(M);
-    // transforms per conv workgroup: about 256 threads, within 160 KB of LDS
-    static constexpr int G = T >= 256 ? 1 : 256 / T;
-    // register budget: 128 VGPRs (4 waves per SIMD) up to M = 8192, 256 above
-    static constexpr int WAVES = LOGM >= 14 ? 2 : 4;
+    // conv: both halves at once up to M = 4096 (sharing twiddles and barriers);
+    // above, the halves run one after the other through one LDS buffer
+    static constexpr bool CONC = LOGM <= 12;
+    // groups of T threads (one row pair each) per workgroup: a single wave up to
+    // M = 1024, where the two halves take turns in one LDS buffer
+    static constexpr bool ONE_WAVE = T <= 64;
+    static constexpr int G = ONE_WAVE ? 64 / T : 1;
+    static constexpr int THREADS = G * T;
+    static constexpr int NBUF = (CONC && !ONE_WAVE) ? 2 : 1;
+    static constexpr int WAVES = 2;  // register budget: 256 VGPRs
 };
 
-// Spectra of the kernel: khat[h][0] = FFT_M(k)/(2M), khat[h][1] = FFT_M(tw k)/(2M).
-// FROM_ROOTS: k comes from the inverse transform of the root values (and is also
-// written to K_out); otherwise k is read from a caller's real kernel.
+// Spectra of the kernel: khat[h][0] = FFT_M(k)/(2M), khat[h][1] = FFT_M(tw k)/(2M),
+// tw_j = exp(-i pi j/M).  FROM_ROOTS: k comes from the inverse transform of the
+// root values (and is also written to K_out); otherwise k is read from a
+// caller's real kernel.  Block 0 also writes the table tab[j] = exp(-i pi j/M)
+// (float64 sin/cos, rounded) that the convolution takes its twiddles from.
 template <int LOGM, bool FROM_ROOTS>
 __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void spectrum_kernel(
     int L, int tiles, const float2* __restrict__ roots, const int32_t* __restrict__ tile_status,
     const float* __restrict__ Kin, int64_t kstride, const float* __restrict__ D, float2* __restrict__ K_out,
-    int32_t* __restrict__ status, float2* __restrict__ khat) {
+    int32_t* __restrict__ status, float2* __restrict__ khat, float2* __restrict__ twtab) {
     using Gm = Geo<LOGM>;
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE;
     __shared__ float2 lds[Gm::LDS];
@@ -53,6 +61,13 @@ __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Ge
     float2* kh0 = khat ? khat + (size_t)h * 2 * M : nullptr;  // null: kernel transform only
     float2* kh1 = khat ? kh0 + M : nullptr;
     float kr[E];
+
+    if (h == 0 && twtab)
+        for (int j = t; j < M; j += T) {
+            double sn, cs;
+            sincospi((double)j / (double)M, &sn, &cs);
+            twtab[j] = make_float2((float)cs, (float)-sn);
+        }
 
     if constexpr (FROM_ROOTS) {
         if (t == 0) sst = 0;
@@ -103,26 +118,22 @@ __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Ge
 #pragma unroll
     for (int e = 0; e < E; ++e) kh0[t + T * e] = v[e];
 
-    const float2 step = root_of_unity<false>(T, 2 * M);
-    float2 tw = root_of_unity<false>(t, 2 * M);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        v[e] = c_scale(tw, kr[e] * sc);
-        tw = c_mul(tw, step);
-    }
+    for (int e = 0; e < E; ++e) v[e] = c_scale(root_of_unity<false>(t + T * e, 2 * M), kr[e] * sc);
     fft_block<LOGM, LOGE, false>(v, lds, t);
 #pragma unroll
     for (int e = 0; e < E; ++e) kh1[t + T * e] = v[e];
 }
 
-// One transform group per pair of batch rows (b, b+1) of one channel.
+// One group of T threads per pair of batch rows (b, b+1) of one channel:
+// z = u_b + i u_{b+1};  y = IFFT(FFT(z) khat0) + conj(tw) IFFT(FFT(tw z) khat1).
 template <int LOGM>
-__global__ __launch_bounds__(Geo<LOGM>::G * Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
+__global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
-    float* __restrict__ y, const float2* __restrict__ khat) {
+    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab) {
     using Gm = Geo<LOGM>;
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE, G = Gm::G;
-    __shared__ float2 lds[G * Gm::LDS];
+    __shared__ float2 lds[G * Gm::NBUF * Gm::LDS];
     const int grp = threadIdx.x / T;
     const int t = threadIdx.x - grp * T;
 
@@ -138,47 +149,56 @@ __global__ __launch_bounds__(Geo<LOGM>::G * Geo<LOGM>::T) __attribute__((amdgpu_
     const bool has2 = active && (b1 + 1 < Bsz);
     const size_t row1 = ((size_t)b1 * H + h) * (size_t)L;
     const size_t row2 = row1 + (size_t)H * L;
-    float2* my = lds + grp * Gm::LDS;
+    float2* my = lds + grp * Gm::NBUF * Gm::LDS;
     const float2* kh0 = khat + (size_t)h * 2 * M;
     const float2* kh1 = kh0 + M;
+    const TwiddleTable tw{twtab, LOGM};
 
-    // cyclic half
-    float2 v[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
+    auto load = [&](int e) {
         const int j = t + T * e;
         const bool in = active && j < L;
-        v[e] = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
-    }
-    fft_block<LOGM, LOGE, false>(v, my, t);
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = c_mul(v[e], kh0[t + T * e]);
-    fft_block<LOGM, LOGE, true>(v, my, t);
-    float2 acc[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) acc[e] = v[e];
+        return make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+    };
 
-    // twisted half (the input row is read again: it is still in cache)
-    const float2 step = root_of_unity<false>(T, 2 * M);
-    const float2 tw0 = root_of_unity<false>(t, 2 * M);
-    float2 tw = tw0;
+    float2 out[E];
+    if constexpr (Gm::CONC) {
+        float2 v[2][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = t + T * e;
-        const bool in = active && j < L;
-        const float2 zz = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
-        v[e] = c_mul(zz, tw);
-        tw = c_mul(tw, step);
-    }
-    fft_block<LOGM, LOGE, false>(v, my, t);
+        for (int e = 0; e < E; ++e) {
+            const float2 z = load(e);
+            v[0][e] = z;
+            v[1][e] = c_mul(z, twtab[t + T * e]);
+        }
+        float2* const bufs[2] = {my, my + (Gm::NBUF - 1) * Gm::LDS};
+        fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1>(v, bufs, t, tw);
 #pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = c_mul(v[e], kh1[t + T * e]);
-    fft_block<LOGM, LOGE, true>(v, my, t);
-    tw = tw0;
+        for (int e = 0; e < E; ++e) {
+            v[0][e] = c_mul(v[0][e], kh0[t + T * e]);
+            v[1][e] = c_mul(v[1][e], kh1[t + T * e]);
+        }
+        fft_multi<2, LOGM, LOGE, true, Gm::NBUF == 1>(v, bufs, t, tw);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        acc[e] = c_add(acc[e], c_mul(v[e], c_conj(tw)));
-        tw = c_mul(tw, step);
+        for (int e = 0; e < E; ++e) out[e] = c_add(v[0][e], c_mul(v[1][e], c_conj(twtab[t + T * e])));
+    } else {
+        float2 v[1][E];
+        float2* const bufs[1] = {my};
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[0][e] = load(e);
+        fft_multi<1, LOGM, LOGE, false>(v, bufs, t, tw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[0][e] = c_mul(v[0][e], kh0[t + T * e]);
+        fft_multi<1, LOGM, LOGE, true>(v, bufs, t, tw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = v[0][e];
+        // twisted half (the input row is read again: it is still in cache)
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[0][e] = c_mul(load(e), twtab[t + T * e]);
+        fft_multi<1, LOGM, LOGE, false>(v, bufs, t, tw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) v[0][e] = c_mul(v[0][e], kh1[t + T * e]);
+        fft_multi<1, LOGM, LOGE, true>(v, bufs, t, tw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) out[e] = c_add(out[e], c_mul(v[0][e], c_conj(twtab[t + T * e])));
     }
 
     if (active) {
@@ -186,8 +206,8 @@ __global__ __launch_bounds__(Geo<LOGM>::G * Geo<LOGM>::T) __attribute__((amdgpu_
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
             if (j < L) {
-                y[row1 + j] = acc[e].x;
-                if (has2) y[row2 + j] = acc[e].y;
+                y[row1 + j] = out[e].x;
+                if (has2) y[row2 + j] = out[e].y;
             }
         }
     }
@@ -196,28 +216,28 @@ __global__ __launch_bounds__(Geo<LOGM>::G * Geo<LOGM>::T) __attribute__((amdgpu_
 template <int LOGM>
 hipError_t spectrum_launch(bool from_roots, int64_t H, int64_t L, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D, float2* K_out,
-                           int32_t* status, float2* khat, hipStream_t stream) {
+                           int32_t* status, float2* khat, float2* twtab, hipStream_t stream) {
     using Gm = Geo<LOGM>;
     if (from_roots)
         hipLaunchKernelGGL((spectrum_kernel<LOGM, true>), dim3((unsigned)H), dim3(Gm::T), 0, stream, (int)L,
-                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat);
+                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat, twtab);
     else
         hipLaunchKernelGGL((spectrum_kernel<LOGM, false>), dim3((unsigned)H), dim3(Gm::T), 0, stream, (int)L,
-                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat);
+                           (int)tiles, roots, tstat, Kin, kstride, D, K_out, status, khat, twtab);
     return hipGetLastError();
 }
 
 template <int LOGM>
 hipError_t conv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y, const float2* khat,
-                       hipStream_t stream) {
+                       const float2* twtab, hipStream_t stream) {
     using Gm = Geo<LOGM>;
     const int64_t npb = (Bsz + 1) / 2;
     const int64_t npairs = npb * H;
     const int64_t blocks = (npairs + Gm::G - 1) / Gm::G;
     int remap = 0;
     if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
-    hipLaunchKernelGGL((conv_kernel<LOGM>), dim3((unsigned)blocks), dim3(Gm::G * Gm::T), 0, stream, (int)Bsz,
-                       (int)H, (int)L, (int)npb, npairs, remap, u, y, khat);
+    hipLaunchKernelGGL((conv_kernel<LOGM>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream, (int)Bsz,
+                       (int)H, (int)L, (int)npb, npairs, remap, u, y, khat, twtab);
     return hipGetLastError();
 }
 
@@ -225,10 +245,12 @@ hipError_t conv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float*
 
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                           float2* K_out, int32_t* status, float2* khat, hipStream_t stream) {
+                           float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream) {
     switch (ilog2_exact(M)) {
-#define SSM_SPEC_CASE(LG) \
-    case LG: return spectrum_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat, stream);
+#define SSM_SPEC_CASE(LG)                                                                                       \
+    case LG:                                                                                                    \
+        return spectrum_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat, \
+                                   twtab, stream);
         SSM_SPEC_CASE(0) SSM_SPEC_CASE(1) SSM_SPEC_CASE(2) SSM_SPEC_CASE(3) SSM_SPEC_CASE(4)
         SSM_SPEC_CASE(5) SSM_SPEC_CASE(6) SSM_SPEC_CASE(7) SSM_SPEC_CASE(8) SSM_SPEC_CASE(9)
         SSM_SPEC_CASE(10) SSM_SPEC_CASE(11) SSM_SPEC_CASE(12) SSM_SPEC_CASE(13) SSM_SPEC_CASE(14)
@@ -238,10 +260,10 @@ hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int
 }
 
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
-                       hipStream_t stream) {
+                       const float2* twtab, hipStream_t stream) {
     switch (ilog2_exact(M)) {
 #define SSM_CONV_CASE(LG) \
-    case LG: return conv_launch<LG>(Bsz, H, L, u, y, khat, stream);
+    case LG: return conv_launch<LG>(Bsz, H, L, u, y, khat, twtab, stream);
         SSM_CONV_CASE(0) SSM_CONV_CASE(1) SSM_CONV_CASE(2) SSM_CONV_CASE(3) SSM_CONV_CASE(4)
         SSM_CONV_CASE(5) SSM_CONV_CASE(6) SSM_CONV_CASE(7) SSM_CONV_CASE(8) SSM_CONV_CASE(9)
         SSM_CONV_CASE(10) SSM_CONV_CASE(11) SSM_CONV_CASE(12) SSM_CONV_CASE(13) SSM_CONV_CASE(14)

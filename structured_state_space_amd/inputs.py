@@ -111,9 +111,9 @@ def make_params(w: Workload) -> tuple:
         dt = np.exp(rng.uniform(np.log(lo), np.log(hi), H)).astype(np.float32)
     D = rng.standard_normal(H).astype(np.float32)
     params = Params(
-        Lambda=np.array(np.broadcast_to(lam, (H, N))),
-        P=np.array(np.broadcast_to(P, (H, N, r))),
-        Q=np.array(np.broadcast_to(Q, (H, N, r))),
+        Lambda=np.array(np.broadcast_to(lam, (H, N)), order="C"),
+        P=np.array(np.broadcast_to(P, (H, N, r)), order="C"),
+        Q=np.array(np.broadcast_to(Q, (H, N, r)), order="C"),
         B=np.ones((H, N), dtype=np.complex64),
         C=C, dt=dt, D=D, L=w.L)
     return params, rng
@@ -152,7 +152,7 @@ def random_params(seed: int, H: int, N: int, r: int, L: int, dt_range=(1e-3, 1e-
     lo, hi = dt_range
     dt = np.exp(rng.uniform(np.log(lo), np.log(hi), H))
     D = rng.standard_normal(H)
-    return Params(np.array(lam, dtype=np.complex64), P.astype(np.complex64),
+    return Params(np.array(lam, dtype=np.complex64, order="C"), P.astype(np.complex64),
                   Q.astype(np.complex64), B.astype(np.complex64), C.astype(np.complex64),
                   dt.astype(np.float32), D.astype(np.float32), L)
 

@@ -32,7 +32,7 @@ ST_INVALID_STEP = 19
 OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_status_string", "ssm_discretize",
-           "ssm_kernel_gen", "ssm_fftconv", "ssm_forward")
+           "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled")
 
 
 class SSMError(RuntimeError):
@@ -61,6 +61,8 @@ def _load():
     lib.ssm_fftconv.restype = i32
     lib.ssm_forward.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp]
     lib.ssm_forward.restype = i32
+    lib.ssm_forward_profiled.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp, vp]
+    lib.ssm_forward_profiled.restype = i32
     return lib
 
 
@@ -182,8 +184,11 @@ def fftconv(K, u, D=None, y=None, workspace=None):
 
 
 def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=None, status=None,
-            workspace=None):
-    """ssm_forward: returns dict(y [Bsz,H,L] f32, K [H,L] c64 or None, status [H] i32)."""
+            workspace=None, events=None):
+    """ssm_forward: returns dict(y [Bsz,H,L] f32, K [H,L] c64 or None, status [H] i32).
+
+    events: optional four torch.cuda.Event(enable_timing=True); then the call goes
+    through ssm_forward_profiled, which records them around its three kernels."""
     H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
     Bsz, H2, L = u.shape
     if H2 != H:
@@ -201,10 +206,21 @@ def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=
     _check(status, "status", torch.int32, (H,), dev)
     nbytes = workspace_bytes(OP_FORWARD, Bsz, H, N, r, L)
     ws = _workspace(nbytes, dev, workspace)
-    rc = lib.ssm_forward(Bsz, H, N, r, L, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt),
-                         _ptr(D), _ptr(u), _ptr(y), _ptr(K_out), _ptr(status), _ptr(ws), nbytes, _stream(dev))
+    args = (Bsz, H, N, r, L, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt), _ptr(D), _ptr(u),
+            _ptr(y), _ptr(K_out), _ptr(status), _ptr(ws), nbytes, _stream(dev))
+    if events is None:
+        rc = lib.ssm_forward(*args)
+        name = "ssm_forward"
+    else:
+        # torch creates its events lazily; record once so each has a handle
+        for e in events:
+            if e.cuda_event == 0:
+                e.record()
+        arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+        rc = lib.ssm_forward_profiled(*args, arr)
+        name = "ssm_forward_profiled"
     if rc != OK:
-        raise SSMError("ssm_forward", rc)
+        raise SSMError(name, rc)
     return dict(y=y, K=K_out, status=status)
 
 

@@ -49,15 +49,16 @@ def test_status_strings():
 
 
 def test_workspace_sizes():
-    # forward: roots [H,M] c64 + tile statuses + spectra [H,2,M] c64, each 256-aligned
+    # forward: roots [H,M] c64 + tile statuses + spectra [H,2,M] c64 + twiddle table [M] c64,
+    # each region 256-byte aligned
     H, M = 256, 1024
     ws = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 1024)
-    assert ws >= H * M * 8 + H * 2 * M * 8
+    assert ws >= H * M * 8 + H * 2 * M * 8 + M * 8
     assert ws % 256 == 0
     assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
-    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8 + M * 8
     # ragged L uses M = next power of two
-    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 3000) == 3 * 2 * 4096 * 8
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 3000) == 3 * 2 * 4096 * 8 + 4096 * 8
 
 
 @pytest.mark.parametrize("args,code", [

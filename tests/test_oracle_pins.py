@@ -425,3 +425,14 @@ def test_planted_mistakes_are_caught(monkeypatch, name, mutant):
     monkeypatch.setattr(mod, name, mutant)
     monkeypatch.setattr(O, name, mutant)
     assert not _pins_pass(), f"no pin caught the planted mistake in {name}"
+
+
+def test_generated_arrays_are_c_contiguous_and_writable():
+    for idx in range(4):
+        p, rng = I.make_params(I.WORKLOADS[idx])
+        for name in ("Lambda", "P", "Q", "B", "C", "dt", "D"):
+            a = getattr(p, name)
+            assert a.flags["C_CONTIGUOUS"] and a.flags["WRITEABLE"], (idx, name)
+    p = I.random_params(0, 3, 5, 2, 9)
+    for name in ("Lambda", "P", "Q", "B", "C", "dt", "D"):
+        assert getattr(p, name).flags["C_CONTIGUOUS"]
