@@ -9,7 +9,7 @@ namespace ssm {
 int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, hipStream_t stream);
+                         int32_t* tile_status, float2* twtab, hipStream_t stream);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -70,10 +70,10 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.khat = off;
         w.khat_bytes = (size_t)H * 2 * M * sizeof(float2);
         off = align256(off + w.khat_bytes);
-        w.tw = off;
-        w.tw_bytes = (size_t)M * sizeof(float2);
-        off = align256(off + w.tw_bytes);
     }
+    w.tw = off;  // every op but the discretisation keeps the twiddle table
+    w.tw_bytes = (size_t)M * sizeof(float2);
+    off = align256(off + w.tw_bytes);
     w.total = off;
     return w;
 }
@@ -155,18 +155,18 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
         if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
     if (!aligned(dt, 4) || !aligned(status, 4) || !aligned(ws, 256)) return SSM_ERR_INVALID_ARGUMENT;
     const WsLayout w = layout(SSM_OP_KERNEL_GEN, 1, H, N, r, L);
-    if (ws_bytes < w.total || (w.total && !ws)) return SSM_ERR_WORKSPACE;
+    if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
     char* base = (char*)ws;
     float2* roots = roots_out ? (float2*)roots_out : (float2*)(base + w.roots);
     int32_t* tstat = (int32_t*)(base + w.tstat);
+    float2* twtab = (float2*)(base + w.tw);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, s);
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
-    if (K || status) {
-        // kernel transform only (spectra go to the workspace's unused tail: none needed here)
+    if (K || status) {  // kernel transform only: no spectra
         e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
-                            status, nullptr, nullptr, s);
+                            status, nullptr, twtab, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
     }
     return SSM_OK;
@@ -222,7 +222,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     auto mark = [&](int i) { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (mark(0) != hipSuccess) return SSM_ERR_DEVICE;
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, s);
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status, khat,
                         twtab, s);

@@ -130,7 +130,8 @@ template <int RK, int RPT>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     int M, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
-    const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status) {
+    const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
+    float2* __restrict__ twtab) {
     constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW;
     __shared__ float4 tbl[kChunk * ROW];
     __shared__ int blk_status;
@@ -140,6 +141,14 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     const int tid = threadIdx.x;
     const size_t hbase = (size_t)h * N;
     const float dtv = dt[h];
+
+    // the table exp(-i pi j/M), j < M, used by the later transforms (spread over the grid)
+    if (twtab)
+        for (int j = blockIdx.x * kCauchyThreads + tid; j < M; j += gridDim.x * kCauchyThreads) {
+            double sn, cs;
+            sincospi((double)j / (double)M, &sn, &cs);
+            twtab[j] = make_float2((float)cs, (float)-sn);
+        }
 
     if (!(dtv > 0.0f) || !(dtv <= FLT_MAX)) {  // uniform over the workgroup
 #pragma unroll
@@ -281,11 +290,11 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
 template <int RK, int RPT>
 hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, const float2* P, const float2* Q,
                      const float2* Bv, const float2* Ct, const float* dt, float2* roots, int32_t* tstat,
-                     hipStream_t stream) {
+                     float2* twtab, hipStream_t stream) {
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
     const int64_t blocks = H * tiles;
     hipLaunchKernelGGL((cauchy_roots_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream,
-                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat);
+                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat, twtab);
     return hipGetLastError();
 }
 
@@ -308,10 +317,11 @@ int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
 
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, hipStream_t stream) {
+                         int32_t* tile_status, float2* twtab, hipStream_t stream) {
     const int rpt = cauchy_rpt(H, r, M);
-#define SSM_CAUCHY(RK, RPT) \
-    if (r == RK && rpt == RPT) return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, stream);
+#define SSM_CAUCHY(RK, RPT)                                                                                   \
+    if (r == RK && rpt == RPT)                                                                                \
+        return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, stream);
     SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY

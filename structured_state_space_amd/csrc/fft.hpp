@@ -77,34 +77,58 @@ __device__ __forceinline__ void dft_reg(float2 (&x)[R]) {
     }
 }
 
-// exact sin/cos of pi*num/den (den a power of two): the default twiddle source
+// Twiddle sources: get<P, n>(i, k) = exp(-2 pi i k/n) for butterfly i of pass P.
+
+// exact sin/cos of pi*num/den (den a power of two), computed where used
 struct TwiddleSincos {
-    __device__ __forceinline__ float2 operator()(int k, int n) const { return root_of_unity<false>(k, n); }
+    template <int P, int n>
+    __device__ __forceinline__ float2 get(int, int k) const { return root_of_unity<false>(k, n); }
 };
 
-// twiddles from a table tab[j] = exp(-i pi j/M), j < M (the 2M-th roots), for
-// transforms of length n dividing M: exp(-2 pi i k/n) = tab-entry 2kM/n,
-// using exp(-i pi (j + M)/M) = -exp(-i pi j/M) for the upper half
-struct TwiddleTable {
-    const float2* tab;
-    int logm;
-    __device__ __forceinline__ float2 operator()(int k, int n) const {
-        const int i = (k << (logm + 1)) >> ilog2_exact(n);  // 2kM/n < 2M
-        const int m = 1 << logm;
-        const float2 w = tab[i & (m - 1)];
-        return i >= m ? make_float2(-w.x, -w.y) : w;
+// lookup in tab[j] = exp(-i pi j/M), j < M (the 2M-th roots), for lengths n
+// dividing M: exp(-2 pi i k/n) is entry 2kM/n, and the upper half follows
+// from exp(-i pi (j + M)/M) = -exp(-i pi j/M)
+__device__ __forceinline__ float2 table_root(const float2* tab, int logm, int k, int logn) {
+    const int i = (k << (logm + 1)) >> logn;  // 2kM/n < 2M
+    const int m = 1 << logm;
+    const float2 w = tab[i & (m - 1)];
+    return i >= m ? make_float2(-w.x, -w.y) : w;
+}
+
+// all pass twiddles of one thread, read from the table once and kept in
+// registers: every transform of the same plan (forward or inverse) reuses them
+template <int LOGN, int LOGE, int LRMAX = (LOGE < 4 ? LOGE : 4)>
+struct TwiddleRegs {
+    static constexpr int E = 1 << LOGE, T = (1 << LOGN) >> LOGE;
+    static constexpr int REM = LOGN > 0 ? LOGN % LRMAX : 0;
+    static constexpr int NP = LOGN > 0 ? LOGN / LRMAX + (REM ? 1 : 0) : 0;
+    static constexpr int NBMAX = E >= 2 ? E / 2 : 1;
+    float2 w[NP > 0 ? NP : 1][NBMAX];
+
+    __device__ __forceinline__ TwiddleRegs(const float2* tab, int logm, int t) {
+        int ls = 0;
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int lr = (p == 0 && REM) ? REM : LRMAX;
+            const int ns = 1 << ls;
+#pragma unroll
+            for (int i = 0; i < NBMAX; ++i)
+                if (i < (E >> lr) && ns > 1) w[p][i] = table_root(tab, logm, (t + i * T) & (ns - 1), ls + lr);
+            ls += lr;
+        }
     }
+    template <int P, int n>
+    __device__ __forceinline__ float2 get(int i, int) const { return w[P][i]; }
 };
 
-template <int NV, int LOGN, int LOGE, bool INV, int LR, int LS, bool LAST, bool SHARED, class TW>
+template <int NV, int LOGN, int LOGE, bool INV, int P, int LR, int LS, bool LAST, bool SHARED, class TW>
 __device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
                                               const TW& tw) {
     constexpr int E = 1 << LOGE, N = 1 << LOGN, T = N >> LOGE, R = 1 << LR, NB = E / R, NS = 1 << LS;
     if constexpr (NS > 1) {  // twiddles, shared by the NV vectors
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            const int k = (t + i * T) & (NS - 1);
-            float2 w = tw(k, NS * R);
+            float2 w = tw.template get<P, NS * R>(i, (t + i * T) & (NS - 1));
             if (INV) w.y = -w.y;
             float2 wq = w;
 #pragma unroll
@@ -159,7 +183,7 @@ __device__ __forceinline__ void fft_passes(float2 (&v)[NV][1 << LOGE], float2* c
         constexpr int NP = LOGN / LRMAX + (REM ? 1 : 0);
         if constexpr (P < NP) {
             constexpr int LR = (P == 0 && REM) ? REM : LRMAX;
-            stockham_pass<NV, LOGN, LOGE, INV, LR, LS, P == NP - 1, SHARED>(v, lds, t, tw);
+            stockham_pass<NV, LOGN, LOGE, INV, P, LR, LS, P == NP - 1, SHARED>(v, lds, t, tw);
             fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, TW, P + 1, LS + LR>(v, lds, t, tw);
         }
     }
@@ -172,11 +196,12 @@ __device__ __forceinline__ void fft_passes(float2 (&v)[NV][1 << LOGE], float2* c
 // the vectors are exchanged in turn.  Requires LOGE <= LOGN (or LOGN == 0).
 // Butterflies are at most radix 16; a thread with E > 16 points runs E/16
 // butterflies per pass.
-template <int NV, int LOGN, int LOGE, bool INV, bool SHARED = false, class TW>
+template <int NV, int LOGN, int LOGE, bool INV, bool SHARED = false, int LRMAX = (LOGE < 4 ? LOGE : 4), class TW>
 __device__ __forceinline__ void fft_multi(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
                                           const TW& tw) {
     static_assert(LOGN == 0 || (LOGE >= 1 && LOGE <= LOGN), "bad FFT split");
-    fft_passes<NV, LOGN, LOGE, (LOGE < 4 ? LOGE : 4), INV, SHARED, TW>(v, lds, t, tw);
+    static_assert(LOGN == 0 || (LRMAX >= 1 && LRMAX <= LOGE && LRMAX <= 4), "bad radix");
+    fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, TW>(v, lds, t, tw);
 }
 
 // single vector, sin/cos twiddles

@@ -23,30 +23,39 @@ namespace ssm {
 
 namespace {
 
+// points per thread: 8 up to M = 1024 (more waves per row for the small
+// transforms), 16 above (M = 16384 takes 1024 threads)
+__host__ __device__ constexpr int conv_loge(int logm) { return logm <= 3 ? logm : logm <= 10 ? 3 : 4; }
+
 template <int LOGM>
 struct Geo {
     static constexpr int M = 1 << LOGM;
-    static constexpr int LOGE = fft_loge(LOGM);
+    static constexpr int LOGE = conv_loge(LOGM);
     static constexpr int E = 1 << LOGE;
     static constexpr int T = M >> LOGE;  // threads per transform
     static constexpr int LDS = lds_padded_size(M);
-    // conv: both halves at once up to M = 4096 (sharing twiddles and barriers);
-    // above, the halves run one after the other through one LDS buffer
-    static constexpr bool CONC = LOGM <= 12;
-    // groups of T threads (one row pair each) per workgroup: a single wave up to
-    // M = 1024, where the two halves take turns in one LDS buffer
+    // conv: the cyclic and twisted halves are transformed together (sharing
+    // twiddles and barriers).  Groups of T threads (one row pair each) per
+    // workgroup: one wave holds several small transforms.  The halves have an
+    // LDS buffer each for multi-wave groups up to M = 4096; otherwise they take
+    // turns in one buffer.
     static constexpr bool ONE_WAVE = T <= 64;
     static constexpr int G = ONE_WAVE ? 64 / T : 1;
     static constexpr int THREADS = G * T;
-    static constexpr int NBUF = (CONC && !ONE_WAVE) ? 2 : 1;
-    static constexpr int WAVES = 2;  // register budget: 256 VGPRs
+    static constexpr int NBUF = (!ONE_WAVE && LOGM <= 12) ? 2 : 1;
+    // spectrum kernel: its two forward transforms share one buffer above M = 4096
+    static constexpr int SPEC_NBUF = LOGM <= 12 ? 2 : 1;
+    static constexpr int WAVES = LOGM >= 14 ? 4 : 2;  // register budget: 128 / 256 VGPRs
+    static constexpr bool PREFETCH = LOGM <= 13;
+    static constexpr int LRMAX = LOGE < 4 ? LOGE : 4;  // largest butterfly radix (log2)
 };
 
 // Spectra of the kernel: khat[h][0] = FFT_M(k)/(2M), khat[h][1] = FFT_M(tw k)/(2M),
 // tw_j = exp(-i pi j/M).  FROM_ROOTS: k comes from the inverse transform of the
-// root values (and is also written to K_out); otherwise k is read from a
-// caller's real kernel.  Block 0 also writes the table tab[j] = exp(-i pi j/M)
-// (float64 sin/cos, rounded) that the convolution takes its twiddles from.
+// root values (and is also written to K_out), and the twiddles come from the
+// table tab[j] = exp(-i pi j/M) that the root-value kernel wrote; otherwise k
+// is read from a caller's real kernel, the twiddles are computed here, and
+// block 0 writes the table for the convolution.
 template <int LOGM, bool FROM_ROOTS>
 __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void spectrum_kernel(
     int L, int tiles, const float2* __restrict__ roots, const int32_t* __restrict__ tile_status,
@@ -54,20 +63,15 @@ __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Ge
     int32_t* __restrict__ status, float2* __restrict__ khat, float2* __restrict__ twtab) {
     using Gm = Geo<LOGM>;
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE;
-    __shared__ float2 lds[Gm::LDS];
+    __shared__ float2 lds[Gm::SPEC_NBUF * Gm::LDS];
     __shared__ int sst;
     const int h = blockIdx.x;
     const int t = threadIdx.x;
     float2* kh0 = khat ? khat + (size_t)h * 2 * M : nullptr;  // null: kernel transform only
     float2* kh1 = khat ? kh0 + M : nullptr;
     float kr[E];
-
-    if (h == 0 && twtab)
-        for (int j = t; j < M; j += T) {
-            double sn, cs;
-            sincospi((double)j / (double)M, &sn, &cs);
-            twtab[j] = make_float2((float)cs, (float)-sn);
-        }
+    float2* const one[1] = {lds};
+    float2* const two[2] = {lds, lds + (Gm::SPEC_NBUF - 1) * Gm::LDS};
 
     if constexpr (FROM_ROOTS) {
         if (t == 0) sst = 0;
@@ -88,41 +92,61 @@ __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Ge
                 }
             return;
         }
-        float2 v[E];
+        const TwiddleRegs<LOGM, LOGE> tw(twtab, LOGM, t);
+        float2 v[1][E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) v[e] = roots[(size_t)h * M + t + T * e];
-        fft_block<LOGM, LOGE, true>(v, lds, t);
+        for (int e = 0; e < E; ++e) v[0][e] = roots[(size_t)h * M + t + T * e];
+        fft_multi<1, LOGM, LOGE, true>(v, one, t, tw);
         const float invM = 1.0f / (float)M;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
-            v[e] = c_scale(v[e], invM);
-            if (K_out && j < L) K_out[(size_t)h * L + j] = v[e];
-            kr[e] = j < L ? v[e].x : 0.0f;
+            v[0][e] = c_scale(v[0][e], invM);
+            if (K_out && j < L) K_out[(size_t)h * L + j] = v[0][e];
+            kr[e] = j < L ? v[0][e].x : 0.0f;
         }
         if (!khat) return;  // uniform
+        if (t == 0 && D) kr[0] += D[h];
+        const float sc = 1.0f / (float)(2 * M);
+        float2 w[2][E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            w[0][e] = make_float2(kr[e] * sc, 0.0f);
+            w[1][e] = c_scale(twtab[t + T * e], kr[e] * sc);
+        }
+        fft_multi<2, LOGM, LOGE, false, Gm::SPEC_NBUF == 1>(w, two, t, tw);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            kh0[t + T * e] = w[0][e];
+            kh1[t + T * e] = w[1][e];
+        }
     } else {
+        if (h == 0)
+            for (int j = t; j < M; j += T) {
+                double sn, cs;
+                sincospi((double)j / (double)M, &sn, &cs);
+                twtab[j] = make_float2((float)cs, (float)-sn);
+            }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
             kr[e] = j < L ? Kin[((size_t)h * L + j) * kstride] : 0.0f;
         }
+        if (t == 0 && D) kr[0] += D[h];
+        const float sc = 1.0f / (float)(2 * M);
+        float2 w[2][E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            w[0][e] = make_float2(kr[e] * sc, 0.0f);
+            w[1][e] = c_scale(root_of_unity<false>(t + T * e, 2 * M), kr[e] * sc);
+        }
+        fft_multi<2, LOGM, LOGE, false, Gm::SPEC_NBUF == 1>(w, two, t, TwiddleSincos{});
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            kh0[t + T * e] = w[0][e];
+            kh1[t + T * e] = w[1][e];
+        }
     }
-    if (t == 0 && D) kr[0] += D[h];
-
-    const float sc = 1.0f / (float)(2 * M);
-    float2 v[E];
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = make_float2(kr[e] * sc, 0.0f);
-    fft_block<LOGM, LOGE, false>(v, lds, t);
-#pragma unroll
-    for (int e = 0; e < E; ++e) kh0[t + T * e] = v[e];
-
-#pragma unroll
-    for (int e = 0; e < E; ++e) v[e] = c_scale(root_of_unity<false>(t + T * e, 2 * M), kr[e] * sc);
-    fft_block<LOGM, LOGE, false>(v, lds, t);
-#pragma unroll
-    for (int e = 0; e < E; ++e) kh1[t + T * e] = v[e];
 }
 
 // One group of T threads per pair of batch rows (b, b+1) of one channel:
@@ -152,7 +176,7 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
     float2* my = lds + grp * Gm::NBUF * Gm::LDS;
     const float2* kh0 = khat + (size_t)h * 2 * M;
     const float2* kh1 = kh0 + M;
-    const TwiddleTable tw{twtab, LOGM};
+    const TwiddleRegs<LOGM, LOGE, Gm::LRMAX> tw(twtab, LOGM, t);
 
     auto load = [&](int e) {
         const int j = t + T * e;
@@ -161,44 +185,35 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
     };
 
     float2 out[E];
-    if constexpr (Gm::CONC) {
-        float2 v[2][E];
+    {
+        // spectra and twist factors are fetched up front (and held) unless registers are short
+        constexpr bool PRE = Gm::PREFETCH;
+        float2 v[2][E], tws[PRE ? E : 1], k0[PRE ? E : 1], k1[PRE ? E : 1];
+        if constexpr (PRE) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                tws[e] = twtab[t + T * e];
+                k0[e] = kh0[t + T * e];
+                k1[e] = kh1[t + T * e];
+            }
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const float2 z = load(e);
             v[0][e] = z;
-            v[1][e] = c_mul(z, twtab[t + T * e]);
+            v[1][e] = c_mul(z, PRE ? tws[PRE ? e : 0] : twtab[t + T * e]);
         }
         float2* const bufs[2] = {my, my + (Gm::NBUF - 1) * Gm::LDS};
-        fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1>(v, bufs, t, tw);
+        fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-            v[0][e] = c_mul(v[0][e], kh0[t + T * e]);
-            v[1][e] = c_mul(v[1][e], kh1[t + T * e]);
+            v[0][e] = c_mul(v[0][e], PRE ? k0[PRE ? e : 0] : kh0[t + T * e]);
+            v[1][e] = c_mul(v[1][e], PRE ? k1[PRE ? e : 0] : kh1[t + T * e]);
         }
-        fft_multi<2, LOGM, LOGE, true, Gm::NBUF == 1>(v, bufs, t, tw);
+        fft_multi<2, LOGM, LOGE, true, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
 #pragma unroll
-        for (int e = 0; e < E; ++e) out[e] = c_add(v[0][e], c_mul(v[1][e], c_conj(twtab[t + T * e])));
-    } else {
-        float2 v[1][E];
-        float2* const bufs[1] = {my};
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[0][e] = load(e);
-        fft_multi<1, LOGM, LOGE, false>(v, bufs, t, tw);
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[0][e] = c_mul(v[0][e], kh0[t + T * e]);
-        fft_multi<1, LOGM, LOGE, true>(v, bufs, t, tw);
-#pragma unroll
-        for (int e = 0; e < E; ++e) out[e] = v[0][e];
-        // twisted half (the input row is read again: it is still in cache)
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[0][e] = c_mul(load(e), twtab[t + T * e]);
-        fft_multi<1, LOGM, LOGE, false>(v, bufs, t, tw);
-#pragma unroll
-        for (int e = 0; e < E; ++e) v[0][e] = c_mul(v[0][e], kh1[t + T * e]);
-        fft_multi<1, LOGM, LOGE, true>(v, bufs, t, tw);
-#pragma unroll
-        for (int e = 0; e < E; ++e) out[e] = c_add(out[e], c_mul(v[0][e], c_conj(twtab[t + T * e])));
+        for (int e = 0; e < E; ++e)
+            out[e] = c_add(v[0][e], c_mul(v[1][e], c_conj(PRE ? tws[PRE ? e : 0] : twtab[t + T * e])));
     }
 
     if (active) {

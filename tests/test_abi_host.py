@@ -54,6 +54,7 @@ def test_workspace_sizes():
     H, M = 256, 1024
     ws = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 1024)
     assert ws >= H * M * 8 + H * 2 * M * 8 + M * 8
+    assert ssm.workspace_bytes(ssm.OP_KERNEL_GEN, 1, H, 64, 1, 1024) >= H * M * 8 + M * 8
     assert ws % 256 == 0
     assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
     assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8 + M * 8
