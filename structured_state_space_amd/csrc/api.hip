@@ -15,6 +15,11 @@ hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                        const float2* twtab, hipStream_t stream);
+hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                                 float2* B1, const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
+                                 float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
+hipError_t launch_conv_large(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y,
+                             const float2* khat, float2* Z, const float2* twtab, hipStream_t stream);
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                              const float2* Q, const float2* Bv, const float2* C, const float* dt, float2* Bbar,
                              float2* Abar, float2* Ct, int32_t* status, hipStream_t stream);
@@ -53,7 +58,6 @@ int check_sizes(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, bool ne
 }
 
 WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L) {
-    (void)Bsz;
     (void)N;
     WsLayout w;
     const int64_t M = pow2_at_least(L);
@@ -74,6 +78,13 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
     w.tw = off;  // every op but the discretisation keeps the twiddle table
     w.tw_bytes = (size_t)M * sizeof(float2);
     off = align256(off + w.tw_bytes);
+    if (M > ((int64_t)1 << kMaxLdsLogM)) {  // multi-pass transforms
+        w.big = off;
+        if (op == SSM_OP_KERNEL_GEN) w.big_bytes = (size_t)H * M * sizeof(float2);  // first-pass output
+        if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD)
+            w.big_bytes = (size_t)((Bsz + 1) / 2) * H * 2 * M * sizeof(float2);  // conv intermediate
+        off = align256(off + w.big_bytes);
+    }
     w.total = off;
     return w;
 }
@@ -118,7 +129,6 @@ int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, in
     }
     if (rc != SSM_OK) return rc;
     if (op == SSM_OP_DISCRETIZE && N > kMaxNDisc) return SSM_ERR_UNSUPPORTED;
-    if (op != SSM_OP_DISCRETIZE && pow2_at_least(L) > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
     *bytes = op == SSM_OP_DISCRETIZE ? 0 : layout(op, Bsz, H, N, r, L).total;
     return SSM_OK;
 }
@@ -148,7 +158,6 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     int rc = check_sizes(1, H, N, r, L, true, false);
     if (rc != SSM_OK) return rc;
     const int64_t M = pow2_at_least(L);
-    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
     if (!Lambda || !P || !Q || !B || !Ctilde || !dt) return SSM_ERR_INVALID_ARGUMENT;
     const void* c64s[] = {Lambda, P, Q, B, Ctilde, K, roots_out};
     for (const void* p : c64s)
@@ -165,8 +174,12 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {  // kernel transform only: no spectra
-        e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
-                            status, nullptr, twtab, s);
+        if (M > ((int64_t)1 << kMaxLdsLogM))
+            e = launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, (float2*)(base + w.big), tstat,
+                                      nullptr, 1, nullptr, (float2*)K, status, nullptr, twtab, s);
+        else
+            e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
+                                status, nullptr, twtab, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
     }
     return SSM_OK;
@@ -177,7 +190,6 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
     int rc = check_sizes(Bsz, H, 1, 1, L, false, true);
     if (rc != SSM_OK) return rc;
     const int64_t M = pow2_at_least(L);
-    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
     if (!K || !u || !y || (k_stride != 1 && k_stride != 2)) return SSM_ERR_INVALID_ARGUMENT;
     if (!aligned(K, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(ws, 256))
         return SSM_ERR_INVALID_ARGUMENT;
@@ -186,6 +198,12 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
     hipStream_t s = (hipStream_t)stream;
     float2* khat = (float2*)((char*)ws + w.khat);
     float2* twtab = (float2*)((char*)ws + w.tw);
+    if (M > ((int64_t)1 << kMaxLdsLogM)) {
+        hipError_t e = launch_spectrum_large(false, H, L, M, 0, nullptr, nullptr, nullptr, K, k_stride, D, nullptr,
+                                             nullptr, khat, twtab, s);
+        if (e != hipSuccess) return SSM_ERR_DEVICE;
+        return device_status(launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)((char*)ws + w.big), twtab, s));
+    }
     hipError_t e =
         launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
@@ -203,7 +221,6 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     int rc = check_sizes(Bsz, H, N, r, L, true, true);
     if (rc != SSM_OK) return rc;
     const int64_t M = pow2_at_least(L);
-    if (M > ((int64_t)1 << kMaxLdsLogM)) return SSM_ERR_UNSUPPORTED;
     if (!Lambda || !P || !Q || !B || !Ctilde || !dt || !u || !y) return SSM_ERR_INVALID_ARGUMENT;
     const void* c64s[] = {Lambda, P, Q, B, Ctilde, K_out};
     for (const void* p : c64s)
@@ -224,10 +241,16 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
-    e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status, khat,
-                        twtab, s);
+    const bool large = M > ((int64_t)1 << kMaxLdsLogM);
+    if (large)
+        e = launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
+                                  (float2*)K_out, status, khat, twtab, s);
+    else
+        e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status,
+                            khat, twtab, s);
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
-    e = launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
+    e = large ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
+              : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
     if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
     return SSM_OK;
 }

@@ -89,7 +89,7 @@ struct TwiddleSincos {
 // dividing M: exp(-2 pi i k/n) is entry 2kM/n, and the upper half follows
 // from exp(-i pi (j + M)/M) = -exp(-i pi j/M)
 __device__ __forceinline__ float2 table_root(const float2* tab, int logm, int k, int logn) {
-    const int i = (k << (logm + 1)) >> logn;  // 2kM/n < 2M
+    const int i = k << (logm + 1 - logn);  // 2kM/n < 2M (n divides M)
     const int m = 1 << logm;
     const float2 w = tab[i & (m - 1)];
     return i >= m ? make_float2(-w.x, -w.y) : w;

@@ -81,10 +81,28 @@ def test_root_values_match_resolvent(idx, nsample):
     assert_rows_close(K, Kref, what="kernel")
 
 
+@pytest.mark.parametrize("L", [16385, 40000])
+def test_root_values_multipass_lengths(L):
+    """M = 32768 and 65536 (the multi-pass transforms): root values against the DFT of
+    the first M taps of the matrix-power kernel, and the first L taps."""
+    ssm = _ssm()
+    p = I.random_params(L, 2, 8, 2, L, dt_range=(1e-3, 1e-2))
+    M = O.transform_length(L)
+    refs = [_oracle_channel(p, h, None, taps=M) for h in range(p.H)]
+    sub = I.Params(p.Lambda, p.P, p.Q, p.B, np.stack([r["Ctilde"] for r in refs]).astype(np.complex64),
+                   p.dt, p.D, L)
+    d = _dev(sub)
+    out = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_kernel=True, want_roots=True)
+    assert np.all(_np(out["status"]) == 0)
+    roots, K = _np(out["roots"]), _np(out["K"])
+    assert_rows_close(roots, np.array([np.fft.fft(r["K"]) for r in refs]), what="root values")
+    assert_rows_close(K, np.array([r["K"][:L] for r in refs]), what="kernel")
+
+
 # ---------------------------------------------------------------------------
 # discretisation
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 8), (2, 4), (3, 4)])
+@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 8), (2, 4), (3, 4), (4, 2)])
 def test_discretize_matches_dense(idx, nsample):
     ssm = _ssm()
     w, p, u = _workload(idx)
@@ -105,7 +123,7 @@ def test_discretize_matches_dense(idx, nsample):
 # ---------------------------------------------------------------------------
 # the whole path from the conventional C: discretize -> forward
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 12), (2, 3), (3, 3)])
+@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 12), (2, 3), (3, 3), (4, 2)])
 def test_forward_end_to_end(idx, nsample):
     ssm = _ssm()
     w, p, u = _workload(idx)
@@ -131,7 +149,8 @@ def test_forward_end_to_end(idx, nsample):
 # the convolution on its own
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("Bsz,H,L", [(1, 1, 1), (1, 1, 2), (3, 2, 3), (2, 3, 17), (5, 4, 100), (2, 9, 1000),
-                                     (4, 8, 1024), (3, 5, 3000), (2, 3, 8192), (1, 2, 16384)])
+                                     (4, 8, 1024), (3, 5, 3000), (2, 3, 8192), (1, 2, 16384), (3, 2, 20000),
+                                     (2, 1, 65536)])
 def test_fftconv_matches_direct_sum(Bsz, H, L):
     ssm = _ssm()
     rng = np.random.default_rng(L * 7 + H)
@@ -236,7 +255,7 @@ def test_invalid_step_status():
 @pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
     (1, 1, 1, 1, 1, "random"), (2, 3, 1, 2, 3, "random"), (3, 5, 2, 3, 1, "random"),
     (5, 100, 1, 100, 3, "s4"), (4, 17, 3, 257, 2, "random"), (3, 9, 4, 64, 2, "random"),
-    (9, 64, 2, 1000, 5, "s4"), (2, 130, 1, 4097, 2, "random"),
+    (9, 64, 2, 1000, 5, "s4"), (2, 130, 1, 4097, 2, "random"), (2, 16, 1, 20000, 3, "random"),
 ])
 def test_edge_cases_end_to_end(H, N, r, L, Bsz, kind):
     ssm = _ssm()
