@@ -158,16 +158,18 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
 
 /*
  * ssm_forward with per-kernel timing marks for benchmarks and profilers.
- * Identical work and results; in addition it records four caller-created
- * hipEvent_t (passed as void*) on `stream`: events[0] before the root-value
- * kernel, events[1] after it, events[2] after the kernel-transform/spectra
- * kernel, events[3] after the convolution.  events must not be NULL.
+ * Same results; the three stages (root values; kernel transform and spectra;
+ * convolution) are each launched `repeat` >= 1 times in a row (every stage is
+ * idempotent), and four caller-created hipEvent_t (passed as void*) are
+ * recorded on `stream`: events[0] before the first stage, events[i] after
+ * stage i.  (events[i] - events[i-1]) / repeat is then a stage's duration per
+ * launch with the dispatch gaps amortised.  events must not be NULL.
  */
 int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
                          const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
                          const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
                          const float* u, float* y, ssm_c64* K_out, int32_t* status,
-                         void* ws, size_t ws_bytes, void* stream, void* const* events);
+                         void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t repeat);
 
 #ifdef __cplusplus
 }

@@ -217,7 +217,7 @@ namespace {
 int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda, const ssm_c64* P,
                  const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
                  const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream,
-                 void* const* ev) {
+                 void* const* ev, int repeat) {
     int rc = check_sizes(Bsz, H, N, r, L, true, true);
     if (rc != SSM_OK) return rc;
     const int64_t M = pow2_at_least(L);
@@ -238,19 +238,28 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     float2* twtab = (float2*)(base + w.tw);
     auto mark = [&](int i) { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (mark(0) != hipSuccess) return SSM_ERR_DEVICE;
-    hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < repeat && e == hipSuccess; ++i)
+        e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
+                          (const float2*)Ctilde, dt, roots, tstat, twtab, s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
-    if (large)
-        e = launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
-                                  (float2*)K_out, status, khat, twtab, s);
-    else
-        e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D, (float2*)K_out, status,
-                            khat, twtab, s);
+    // the multi-pass kernel transform works in place on the root values, so a
+    // repeated stage first regenerates them (the repeat count is a timing aid)
+    for (int i = 0; i < repeat && e == hipSuccess; ++i) {
+        if (large && i > 0)
+            e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
+        if (e != hipSuccess) break;
+        e = large ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
+                                          (float2*)K_out, status, khat, twtab, s)
+                  : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
+                                    (float2*)K_out, status, khat, twtab, s);
+    }
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
-    e = large ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
-              : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
+    for (int i = 0; i < repeat && e == hipSuccess; ++i)
+        e = large ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
+                  : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
     if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
     return SSM_OK;
 }
@@ -263,16 +272,17 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const s
                 const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
                 const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws, size_t ws_bytes, void* stream) {
     return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
-                        nullptr);
+                        nullptr, 1);
 }
 
 int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda,
                          const ssm_c64* P, const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt,
                          const float* D, const float* u, float* y, ssm_c64* K_out, int32_t* status, void* ws,
-                         size_t ws_bytes, void* stream, void* const* events) {
-    if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return SSM_ERR_INVALID_ARGUMENT;
+                         size_t ws_bytes, void* stream, void* const* events, int32_t repeat) {
+    if (!events || !events[0] || !events[1] || !events[2] || !events[3] || repeat < 1)
+        return SSM_ERR_INVALID_ARGUMENT;
     return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
-                        events);
+                        events, repeat);
 }
 
 }  // extern "C"

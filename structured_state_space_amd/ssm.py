@@ -61,7 +61,7 @@ def _load():
     lib.ssm_fftconv.restype = i32
     lib.ssm_forward.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp]
     lib.ssm_forward.restype = i32
-    lib.ssm_forward_profiled.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp, vp]
+    lib.ssm_forward_profiled.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp, vp, ctypes.c_int32]
     lib.ssm_forward_profiled.restype = i32
     return lib
 
@@ -184,11 +184,12 @@ def fftconv(K, u, D=None, y=None, workspace=None):
 
 
 def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=None, status=None,
-            workspace=None, events=None):
+            workspace=None, events=None, repeat=1):
     """ssm_forward: returns dict(y [Bsz,H,L] f32, K [H,L] c64 or None, status [H] i32).
 
     events: optional four torch.cuda.Event(enable_timing=True); then the call goes
-    through ssm_forward_profiled, which records them around its three kernels."""
+    through ssm_forward_profiled, which launches each of its three stages
+    `repeat` times and records the events around them."""
     H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
     Bsz, H2, L = u.shape
     if H2 != H:
@@ -217,7 +218,7 @@ def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=
             if e.cuda_event == 0:
                 e.record()
         arr = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
-        rc = lib.ssm_forward_profiled(*args, arr)
+        rc = lib.ssm_forward_profiled(*args, arr, int(repeat))
         name = "ssm_forward_profiled"
     if rc != OK:
         raise SSMError(name, rc)
