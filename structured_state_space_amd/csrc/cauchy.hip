@@ -32,12 +32,12 @@ namespace ssm {
 
 namespace {
 
-constexpr int kChunk = 64;
-
 template <int RK>
 struct Fam {
     static constexpr int F = (RK + 1) * (RK + 1);
     static constexpr int ROW = 1 + F;  // float4 per state: header + one per family
+    // states staged in LDS at a time (<= 26 KB): the whole state vector for N up to this
+    static constexpr int CHUNK = RK == 1 ? 256 : RK == 2 ? 128 : 64;
 };
 
 __device__ __forceinline__ float2 cdivf(float2 a, float2 b) {
@@ -132,9 +132,10 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
     float2* __restrict__ twtab) {
-    constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW;
+    constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW, kChunk = Fam<RK>::CHUNK;
     __shared__ float4 tbl[kChunk * ROW];
     __shared__ int blk_status;
+    __shared__ double2 red[kCauchyThreads / 64];
 
     const int h = blockIdx.x / tiles;
     const int tile = blockIdx.x - h * tiles;
@@ -185,17 +186,21 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
 #pragma unroll
         for (int f = 0; f < F; ++f) acc[i][f] = make_float2(0.f, 0.f);
 
+    double m1x = 0.0, m1y = 0.0;
     for (int n0 = 0; n0 < N; n0 += kChunk) {
         const int nch = min(kChunk, N - n0);
         __syncthreads();
-        if (tid < nch) {
-            const size_t hn = hbase + n0 + tid;
+        for (int nn = tid; nn < nch; nn += kCauchyThreads) {
+            const size_t hn = hbase + n0 + nn;
             const float2 lam = Lambda[hn];
             const float x = -lam.x;
-            tbl[tid * ROW] = make_float4(x * x, lam.y, x, 0.f);
+            tbl[nn * ROW] = make_float4(x * x, lam.y, x, 0.f);
             float2 uu[RK + 1], vv[RK + 1];
             uu[0] = Ct[hn];
             vv[0] = Bv[hn];
+            // z = -1 takes (dt/2) C~^* B: partial sums in float64, reduced after the sweep
+            m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
+            m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
 #pragma unroll
             for (int j = 0; j < RK; ++j) {
                 uu[1 + j] = Q[hn * RK + j];
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
 #pragma unroll
                 for (int iv = 0; iv <= RK; ++iv) {
                     const float2 w = c_mul(c_conj(uu[iu]), vv[iv]);
-                    tbl[tid * ROW + 1 + iu * (RK + 1) + iv] = make_float4(w.x * x, w.y * x, w.y, -w.x);
+                    tbl[nn * ROW + 1 + iu * (RK + 1) + iv] = make_float4(w.x * x, w.y * x, w.y, -w.x);
                 }
         }
         __syncthreads();
@@ -234,6 +239,25 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         }
     }
 
+    // reduce the z = -1 partial sums when this tile holds k = M/2 (uniform test)
+    const int k_lo = tile * (kCauchyThreads * RPT);
+    const bool has_m1 = M >= 2 && k_lo <= M / 2 && M / 2 < k_lo + kCauchyThreads * RPT;
+    double2 m1 = make_double2(0.0, 0.0);
+    if (has_m1) {
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            m1x += __shfl_xor(m1x, o, 64);
+            m1y += __shfl_xor(m1y, o, 64);
+        }
+        if ((tid & 63) == 0) red[tid >> 6] = make_double2(m1x, m1y);
+        __syncthreads();
+#pragma unroll
+        for (int wv = 0; wv < kCauchyThreads / 64; ++wv) {
+            m1.x += red[wv].x;
+            m1.y += red[wv].y;
+        }
+    }
+
     int my_status = 0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -242,13 +266,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         float2 H;
         if (2 * k == M) {
             // z = -1: (dt/2) C~^* B
-            double sx = 0.0, sy = 0.0;
-            for (int n = 0; n < N; ++n) {
-                const float2 c = Ct[hbase + n], b = Bv[hbase + n];
-                sx += (double)c.x * b.x + (double)c.y * b.y;
-                sy += (double)c.x * b.y - (double)c.y * b.x;
-            }
-            H = make_float2((float)(0.5 * dtv * sx), (float)(0.5 * dtv * sy));
+            H = make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y));
         } else {
             bool finite = true;
 #pragma unroll
@@ -303,7 +321,7 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, cons
 // roots per thread: the most this rank allows (more sums share each LDS row)
 // while the grid keeps at least 1024 workgroups (four waves per SIMD)
 int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
-    const int max_rpt = r == 1 ? 4 : r == 2 ? 2 : 1;
+    const int max_rpt = r == 1 ? 8 : r == 2 ? 4 : 1;
     int rpt = max_rpt;
     while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
         rpt >>= 1;
@@ -322,7 +340,8 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
     if (r == RK && rpt == RPT)                                                                                \
         return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, stream);
-    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
+    SSM_CAUCHY(1, 8) SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 4) SSM_CAUCHY(2, 2)
+    SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY
     return hipErrorInvalidValue;
