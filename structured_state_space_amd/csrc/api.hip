@@ -9,7 +9,7 @@ namespace ssm {
 int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, hipStream_t stream);
+                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -69,6 +69,9 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.tstat = off;
         w.tstat_bytes = (size_t)H * cauchy_tiles(H, r, M) * sizeof(int32_t);
         off = align256(off + w.tstat_bytes);
+        w.tant = off;
+        w.tant_bytes = (size_t)M * sizeof(double);
+        off = align256(off + w.tant_bytes);
     }
     if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {
         w.khat = off;
@@ -171,7 +174,7 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     int32_t* tstat = (int32_t*)(base + w.tstat);
     float2* twtab = (float2*)(base + w.tw);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {  // kernel transform only: no spectra
         if (M > ((int64_t)1 << kMaxLdsLogM))
@@ -241,7 +244,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     hipError_t e = hipSuccess;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
-                          (const float2*)Ctilde, dt, roots, tstat, twtab, s);
+                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
     // the multi-pass kernel transform works in place on the root values, so a
@@ -249,7 +252,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     for (int i = 0; i < repeat && e == hipSuccess; ++i) {
         if (large && i > 0)
             e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, s);
+                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
         if (e != hipSuccess) break;
         e = large ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
                                           (float2*)K_out, status, khat, twtab, s)

@@ -126,13 +126,34 @@ __device__ __forceinline__ bool root_recheck(int N, size_t hbase, float st, cons
     return true;
 }
 
+// Per-root tables, once per call: tan(pi k/M) in float64 (0 at k = M/2, which
+// takes the finite z = -1 formula) and exp(-i pi k/M) for the later transforms.
+__global__ __launch_bounds__(256) void root_tables_kernel(int M, double* __restrict__ tant,
+                                                          float2* __restrict__ twtab) {
+    const int k = blockIdx.x * 256 + threadIdx.x;
+    if (k >= M) return;
+    double sn, cs;
+    sincospi((double)k / (double)M, &sn, &cs);
+    tant[k] = (2 * k == M) ? 0.0 : sn / cs;
+    twtab[k] = make_float2((float)cs, (float)-sn);
+}
+
 template <int RK, int RPT>
 __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     int M, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
-    float2* __restrict__ twtab) {
+    const double* __restrict__ tant, float2* __restrict__ twtab) {
     constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW, kChunk = Fam<RK>::CHUNK;
+    // tan(pi k/M) from the per-call table when each thread has several roots;
+    // otherwise computed here, and this grid also writes the twiddle table
+    constexpr bool TAB = RPT >= 4;
+    if constexpr (!TAB)
+        for (int j = blockIdx.x * kCauchyThreads + threadIdx.x; j < M; j += gridDim.x * kCauchyThreads) {
+            double sn, cs;
+            sincospi((double)j / (double)M, &sn, &cs);
+            twtab[j] = make_float2((float)cs, (float)-sn);
+        }
     __shared__ float4 tbl[kChunk * ROW];
     __shared__ int blk_status;
     __shared__ double2 red[kCauchyThreads / 64];
@@ -143,13 +164,6 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     const size_t hbase = (size_t)h * N;
     const float dtv = dt[h];
 
-    // the table exp(-i pi j/M), j < M, used by the later transforms (spread over the grid)
-    if (twtab)
-        for (int j = blockIdx.x * kCauchyThreads + tid; j < M; j += gridDim.x * kCauchyThreads) {
-            double sn, cs;
-            sincospi((double)j / (double)M, &sn, &cs);
-            twtab[j] = make_float2((float)cs, (float)-sn);
-        }
 
     if (!(dtv > 0.0f) || !(dtv <= FLT_MAX)) {  // uniform over the workgroup
 #pragma unroll
@@ -171,10 +185,15 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         kk[i] = k;
         st[i] = 0.0f;
         tf[i] = 0.0f;
-        if (k < M && 2 * k != M) {
-            double s, c;
-            sincospi((double)k / (double)M, &s, &c);
-            const double t = s / c;
+        if (k < M) {
+            double t;
+            if constexpr (TAB) {
+                t = tant[k];
+            } else {
+                double sn, cs;
+                sincospi((double)k / (double)M, &sn, &cs);
+                t = (2 * k == M) ? 0.0 : sn / cs;
+            }
             st[i] = (float)(a * t);
             tf[i] = (float)t;
         }
@@ -308,11 +327,16 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
 template <int RK, int RPT>
 hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, const float2* P, const float2* Q,
                      const float2* Bv, const float2* Ct, const float* dt, float2* roots, int32_t* tstat,
-                     float2* twtab, hipStream_t stream) {
+                     float2* twtab, double* tant, hipStream_t stream) {
+    if (RPT >= 4) {
+        hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M, tant,
+                           twtab);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
     const int64_t blocks = H * tiles;
     hipLaunchKernelGGL((cauchy_roots_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream,
-                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat, twtab);
+                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat, tant, twtab);
     return hipGetLastError();
 }
 
@@ -335,11 +359,11 @@ int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
 
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, hipStream_t stream) {
+                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream) {
     const int rpt = cauchy_rpt(H, r, M);
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
     if (r == RK && rpt == RPT)                                                                                \
-        return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, stream);
+        return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, stream);
     SSM_CAUCHY(1, 8) SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 4) SSM_CAUCHY(2, 2)
     SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)

@@ -65,6 +65,7 @@ __host__ __device__ constexpr int ilog2_exact(long long v) {
 struct WsLayout {
     size_t roots = 0, roots_bytes = 0;     // [H, M] complex64: root values H(z_k)
     size_t tstat = 0, tstat_bytes = 0;     // [H, tiles] int32: per-root-tile statuses
+    size_t tant = 0, tant_bytes = 0;       // [M] float64: tan(pi k/M)
     size_t khat = 0, khat_bytes = 0;       // [H, 2, M] complex64: conv spectra (cyclic, twisted)
     size_t tw = 0, tw_bytes = 0;           // [M] complex64: exp(-i pi j/M), the conv's twiddles
     size_t big = 0, big_bytes = 0;         // scratch of the multi-pass transforms (M > 16384)
