@@ -14,12 +14,17 @@
 // exactly -Re(lambda_n), which float32 needs when a = 2/dt is large.
 //
 // Work split: one workgroup per (channel, tile of 256*RPT roots).  Per chunk of
-// 64 states the workgroup stages lambda and the weights conj(u_n) v_n (times
-// -Re(lambda_n), see below) in LDS; every thread then sweeps the chunk for its
-// RPT roots: one reciprocal and (r+1)^2 complex multiply-adds per (root, state).
-// With d = x + i y (x = -Re lambda, y = a t_k - Im lambda), 1/d = (x - i y)/|d|^2,
-//   w/d = (w x) inv + (-i w) (y inv),  inv = 1/|d|^2,
-// so the table keeps (w x) and w and the loop needs inv and p = y*inv only.
+// states the workgroup stages lambda and the weights w = conj(u_n) v_n in LDS;
+// every thread then sweeps the chunk for its RPT roots: one reciprocal and
+// (r+1)^2 complex multiply-adds per (root, state).  With d = x + i y
+// (x = -Re lambda, y = a t_k - Im lambda), 1/d = (x - i y)/|d|^2 and
+//   w/d = (w x) inv + (-i w) (y inv),  inv = 1/|d|^2.
+// Every lane reads the same table row, so the sweep moves 64 copies of each row
+// from LDS per wave: with several roots per thread the row is amortised and the
+// table keeps (w x) and w (wide rows: no per-family products beyond the four
+// multiply-adds); with one or two roots per thread the LDS read rate is the
+// limit, so the table keeps w alone (narrow rows, 8 instead of 16 bytes per
+// family) and the loop forms x inv once per (root, state).
 // Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
 // with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
 // flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
@@ -35,7 +40,8 @@ namespace {
 template <int RK>
 struct Fam {
     static constexpr int F = (RK + 1) * (RK + 1);
-    static constexpr int ROW = 1 + F;  // float4 per state: header + one per family
+    static constexpr int ROW = 1 + F;  // float4 per state, wide rows: header + one per family
+    static constexpr int ROWN = 1 + (F + 1) / 2;  // narrow rows: header + a float2 per family
     // states staged in LDS at a time (<= 26 KB): the whole state vector for N up to this
     static constexpr int CHUNK = RK == 1 ? 256 : RK == 2 ? 128 : 64;
 };
@@ -144,7 +150,9 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
     const double* __restrict__ tant, float2* __restrict__ twtab) {
-    constexpr int F = Fam<RK>::F, ROW = Fam<RK>::ROW, kChunk = Fam<RK>::CHUNK;
+    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK;
+    constexpr bool NARROW = RPT <= 2;
+    constexpr int RW = NARROW ? Fam<RK>::ROWN : Fam<RK>::ROW;
     // tan(pi k/M) from the per-call table when each thread has several roots;
     // otherwise computed here, and this grid also writes the twiddle table
     constexpr bool TAB = RPT >= 4;
@@ -154,7 +162,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
             sincospi((double)j / (double)M, &sn, &cs);
             twtab[j] = make_float2((float)cs, (float)-sn);
         }
-    __shared__ float4 tbl[kChunk * ROW];
+    __shared__ float4 tbl[kChunk * RW];
     __shared__ int blk_status;
     __shared__ double2 red[kCauchyThreads / 64];
 
@@ -213,7 +221,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
             const size_t hn = hbase + n0 + nn;
             const float2 lam = Lambda[hn];
             const float x = -lam.x;
-            tbl[nn * ROW] = make_float4(x * x, lam.y, x, 0.f);
+            tbl[nn * RW] = make_float4(x * x, lam.y, x, 0.f);
             float2 uu[RK + 1], vv[RK + 1];
             uu[0] = Ct[hn];
             vv[0] = Bv[hn];
@@ -230,29 +238,54 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
 #pragma unroll
                 for (int iv = 0; iv <= RK; ++iv) {
                     const float2 w = c_mul(c_conj(uu[iu]), vv[iv]);
-                    tbl[nn * ROW + 1 + iu * (RK + 1) + iv] = make_float4(w.x * x, w.y * x, w.y, -w.x);
+                    const int f = iu * (RK + 1) + iv;
+                    if constexpr (NARROW)
+                        reinterpret_cast<float2*>(tbl + nn * RW + 1)[f] = w;
+                    else
+                        tbl[nn * RW + 1 + f] = make_float4(w.x * x, w.y * x, w.y, -w.x);
                 }
+            if constexpr (NARROW && (F & 1))  // pad the last float4 of the row
+                reinterpret_cast<float2*>(tbl + nn * RW + 1)[F] = make_float2(0.f, 0.f);
         }
         __syncthreads();
         for (int n = 0; n < nch; ++n) {
-            const float4 hd = tbl[n * ROW];
-            float inv[RPT], p[RPT];
+            const float4 hd = tbl[n * RW];
+            float inv[RPT], p[RPT], q[RPT], pn[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const float y = st[i] - hd.y;
                 const float den = fmaf(y, y, hd.x);
                 inv[i] = __builtin_amdgcn_rcpf(den);
                 p[i] = y * inv[i];
+                if constexpr (NARROW) {
+                    q[i] = hd.z * inv[i];           // x inv
+                    pn[i] = (hd.y - st[i]) * inv[i];  // -y inv, kept as its own product
+                }
             }
+            if constexpr (NARROW) {
+                const float2* wrow = reinterpret_cast<const float2*>(tbl + n * RW + 1);
 #pragma unroll
-            for (int f = 0; f < F; ++f) {
-                const float4 w = tbl[n * ROW + 1 + f];
+                for (int f = 0; f < F; ++f) {
+                    const float2 w = wrow[f];
 #pragma unroll
-                for (int i = 0; i < RPT; ++i) {
-                    acc[i][f].x = fmaf(w.x, inv[i], acc[i][f].x);
-                    acc[i][f].x = fmaf(w.z, p[i], acc[i][f].x);
-                    acc[i][f].y = fmaf(w.y, inv[i], acc[i][f].y);
-                    acc[i][f].y = fmaf(w.w, p[i], acc[i][f].y);
+                    for (int i = 0; i < RPT; ++i) {
+                        acc[i][f].x = fmaf(w.x, q[i], acc[i][f].x);
+                        acc[i][f].x = fmaf(w.y, p[i], acc[i][f].x);
+                        acc[i][f].y = fmaf(w.y, q[i], acc[i][f].y);
+                        acc[i][f].y = fmaf(w.x, pn[i], acc[i][f].y);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int f = 0; f < F; ++f) {
+                    const float4 w = tbl[n * RW + 1 + f];
+#pragma unroll
+                    for (int i = 0; i < RPT; ++i) {
+                        acc[i][f].x = fmaf(w.x, inv[i], acc[i][f].x);
+                        acc[i][f].x = fmaf(w.z, p[i], acc[i][f].x);
+                        acc[i][f].y = fmaf(w.y, inv[i], acc[i][f].y);
+                        acc[i][f].y = fmaf(w.w, p[i], acc[i][f].y);
+                    }
                 }
             }
         }
