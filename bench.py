@@ -47,17 +47,23 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
-def algorithmic(w, M):
-    """Per-launch algorithmic work of each kernel (definitions in the design notes)."""
+def algorithmic(w, M, fused):
+    """Per-launch algorithmic work of each kernel (definitions in the design notes).
+    fused: the kernel transform runs inside the convolution, which then reads
+    the root values instead of the spectra."""
     H, N, r, L, B = w.H, w.N, w.r, w.L, w.Bsz
     roots = M - 1 if M >= 2 else M                      # z = -1 takes its finite formula
-    return {
+    out = {
         "cauchy": dict(bound="alu", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
                        peak=PEAK_FP32_TFLOPS),
         "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * 2 * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
         "conv": dict(bound="hbm", unit="GB/s", work=8 * B * H * L + 4 * H * L + 4 * H, scale=1e-9,
                      peak=PEAK_HBM_GBS),
     }
+    if fused:
+        del out["spectrum"]
+        out["conv"]["work"] = 8 * B * H * L + 8 * H * M + 4 * H
+    return out
 
 
 def read_traffic(kernel, workload):
@@ -137,6 +143,7 @@ def main():
 
     w, p, u = I.workload(args.workload)
     M, n_fft = ssm.transform_lengths(w.L)
+    fused = ssm.forward_fused(w.Bsz, w.L)
     d = ssm.to_device(p, dev)
     ut = torch.from_numpy(u).to(dev)
 
@@ -179,8 +186,8 @@ def main():
 
     # per-kernel durations, live, on the launch stream: each stage launched
     # `repeat` times back to back between events (dispatch gaps amortised)
-    names = ("cauchy", "spectrum", "conv")
-    acc = {k: 0.0 for k in names}
+    stages = ("cauchy", "spectrum", "conv")
+    acc = {k: 0.0 for k in stages}
     reps = max(1, args.stage_repeat)
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
@@ -188,14 +195,16 @@ def main():
                     workspace=ws, events=evs[i], repeat=reps)
     torch.cuda.synchronize()
     for i in range(args.steps):
-        for j, k in enumerate(names):
+        for j, k in enumerate(stages):
             acc[k] += evs[i][j].elapsed_time(evs[i][j + 1]) / reps
-    phase_ms = {k: acc[k] / args.steps for k in names}
+    phase_ms = {k: acc[k] / args.steps for k in stages}
+    # fused: stage 2 launches nothing and the convolution kernel includes it
+    names = ("cauchy", "conv") if fused else stages
     if M > 16384:
         # the repeated multi-pass kernel transform regenerates the root values each time
         phase_ms["spectrum"] -= phase_ms["cauchy"] * (reps - 1) / reps
 
-    alg = algorithmic(w, M)
+    alg = algorithmic(w, M, fused)
     phases = {}
     for k in names:
         a = alg[k]
@@ -214,7 +223,7 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "N": w.N, "r": w.r, "L": w.L, "M": M, "n_fft": n_fft,
-                   "batch": w.Bsz},
+                   "batch": w.Bsz, "spectrum_fused_into_conv": fused},
         "roofline": roofline,
         "phases": phases,
         "composite_roofline_frac": troof_ms / ms_per_step,

@@ -87,6 +87,13 @@ int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, in
  * Pure integer host computation; SSM_ERR_INVALID_ARGUMENT for L < 1. */
 int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft);
 
+/* Whether ssm_forward forms the kernel spectra inside its convolution kernel
+ * (*fused = 1: two launches, no spectra in the workspace) or in a separate
+ * kernel-transform launch (*fused = 0) for a batch of Bsz rows and kernel
+ * length L.  Informational only: the results are the same either way.  Pure
+ * host computation; SSM_ERR_INVALID_ARGUMENT for Bsz < 1, L < 1 or null. */
+int ssm_forward_fused(int64_t Bsz, int64_t L, int32_t* fused);
+
 /* Static description of a return code or status code (never NULL). */
 const char* ssm_status_string(int code);
 
@@ -163,7 +170,9 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
  * idempotent), and four caller-created hipEvent_t (passed as void*) are
  * recorded on `stream`: events[0] before the first stage, events[i] after
  * stage i.  (events[i] - events[i-1]) / repeat is then a stage's duration per
- * launch with the dispatch gaps amortised.  events must not be NULL.
+ * launch with the dispatch gaps amortised.  Where ssm_forward_fused reports 1,
+ * stage 2 launches nothing and stage 3 includes the kernel transform.  events
+ * must not be NULL.
  */
 int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
                          const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,

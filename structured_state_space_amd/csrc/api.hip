@@ -15,6 +15,10 @@ hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                        const float2* twtab, hipStream_t stream);
+bool conv_fuses_spectrum(int64_t Bsz, int64_t M);
+hipError_t launch_conv_fused(int64_t Bsz, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                             const int32_t* tstat, const float* D, float2* K_out, int32_t* status, const float* u,
+                             float* y, const float2* twtab, hipStream_t stream);
 hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                                  float2* B1, const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                                  float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -102,6 +106,13 @@ int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft) {
     if (L < 1 || L > ((int64_t)1 << 61) || !M || !n_fft) return SSM_ERR_INVALID_ARGUMENT;
     *M = pow2_at_least(L);
     *n_fft = pow2_at_least(2 * L - 1);
+    return SSM_OK;
+}
+
+int ssm_forward_fused(int64_t Bsz, int64_t L, int32_t* fused) {
+    if (Bsz < 1 || L < 1 || L > ((int64_t)1 << 61) || !fused) return SSM_ERR_INVALID_ARGUMENT;
+    const int64_t M = pow2_at_least(L);
+    *fused = (M <= ((int64_t)1 << kMaxLdsLogM) && conv_fuses_spectrum(Bsz, M)) ? 1 : 0;
     return SSM_OK;
 }
 
@@ -247,9 +258,10 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
                           (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
+    const bool fused = !large && conv_fuses_spectrum(Bsz, M);
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
-    for (int i = 0; i < repeat && e == hipSuccess; ++i) {
+    for (int i = 0; i < repeat && e == hipSuccess && !fused; ++i) {
         if (large && i > 0)
             e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                               (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
@@ -261,8 +273,10 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     }
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
-        e = large ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
-                  : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
+        e = large   ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
+            : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out,
+                                        status, u, y, twtab, s)
+                    : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
     if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
     return SSM_OK;
 }

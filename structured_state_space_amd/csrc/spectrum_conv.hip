@@ -149,12 +149,28 @@ __global__ __launch_bounds__(Geo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(Ge
     }
 }
 
+// Inputs of the fused form: the spectra are formed from the root values inside
+// the convolution (no separate kernel-transform launch, no spectra in HBM).
+struct FusedSpec {
+    const float2* roots;         // [H][M] root values
+    const int32_t* tile_status;  // [H][tiles] root-value kernel status
+    int tiles;
+    const float* D;   // [H] or null
+    float2* K_out;    // [H][L] or null
+    int32_t* status;  // [H] or null
+};
+
 // One group of T threads per pair of batch rows (b, b+1) of one channel:
 // z = u_b + i u_{b+1};  y = IFFT(FFT(z) khat0) + conj(tw) IFFT(FFT(tw z) khat1).
-template <int LOGM>
+// FUSED: each group first computes its channel's khat0/khat1 from the root values
+// (inverse transform, truncation to L taps, D at tap 0, two forward transforms)
+// while its input rows load; the group of the channel's first row pair also
+// writes K_out and the channel status.  This repeats the kernel transform once
+// per row pair, which pays only where the grid is small and latency-bound.
+template <int LOGM, bool FUSED>
 __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
-    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab) {
+    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab, FusedSpec fs) {
     using Gm = Geo<LOGM>;
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE, G = Gm::G;
     __shared__ float2 lds[G * Gm::NBUF * Gm::LDS];
@@ -185,25 +201,65 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
     };
 
     float2 out[E];
+    int chst = 0;
     {
         // spectra and twist factors are fetched up front (and held) unless registers are short
-        constexpr bool PRE = Gm::PREFETCH;
+        constexpr bool PRE = Gm::PREFETCH || FUSED;
         float2 v[2][E], tws[PRE ? E : 1], k0[PRE ? E : 1], k1[PRE ? E : 1];
-        if constexpr (PRE) {
+        float2* const bufs[2] = {my, my + (Gm::NBUF - 1) * Gm::LDS};
+        if constexpr (FUSED) {
+            float2 rv[1][E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) rv[0][e] = fs.roots[(size_t)h * M + t + T * e];
+#pragma unroll
+            for (int e = 0; e < E; ++e) tws[e] = twtab[t + T * e];
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[0][e] = load(e);
+            for (int i = 0; i < fs.tiles; ++i) chst = max(chst, fs.tile_status[(size_t)h * fs.tiles + i]);
+            const bool lead = active && b1 == 0;
+            if (lead && t == 0 && fs.status) fs.status[h] = chst;
+            float2* const one[1] = {my};
+            fft_multi<1, LOGM, LOGE, true, false, Gm::LRMAX>(rv, one, t, tw);
+            const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                tws[e] = twtab[t + T * e];
-                k0[e] = kh0[t + T * e];
-                k1[e] = kh1[t + T * e];
+                const int j = t + T * e;
+                const float2 kv = c_scale(rv[0][e], invM);
+                if (lead && fs.K_out && j < L) fs.K_out[(size_t)h * L + j] = chst ? c_nan() : kv;
+                float kr = j < L ? kv.x : 0.0f;
+                if (j == 0 && fs.D) kr += fs.D[h];
+                k0[e] = make_float2(kr * sc, 0.0f);
+                k1[e] = c_scale(tws[e], kr * sc);
+            }
+            float2 w[2][E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                w[0][e] = k0[e];
+                w[1][e] = k1[e];
+            }
+            fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(w, bufs, t, tw);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                k0[e] = w[0][e];
+                k1[e] = w[1][e];
+                v[1][e] = c_mul(v[0][e], tws[e]);
+            }
+        } else {
+            if constexpr (PRE) {
+#pragma unroll
+                for (int e = 0; e < E; ++e) {
+                    tws[e] = twtab[t + T * e];
+                    k0[e] = kh0[t + T * e];
+                    k1[e] = kh1[t + T * e];
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const float2 z = load(e);
+                v[0][e] = z;
+                v[1][e] = c_mul(z, PRE ? tws[PRE ? e : 0] : twtab[t + T * e]);
             }
         }
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const float2 z = load(e);
-            v[0][e] = z;
-            v[1][e] = c_mul(z, PRE ? tws[PRE ? e : 0] : twtab[t + T * e]);
-        }
-        float2* const bufs[2] = {my, my + (Gm::NBUF - 1) * Gm::LDS};
         fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -221,6 +277,7 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
             if (j < L) {
+                if (FUSED && chst) out[e] = c_nan();
                 y[row1 + j] = out[e].x;
                 if (has2) y[row2 + j] = out[e].y;
             }
@@ -251,8 +308,22 @@ hipError_t conv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float*
     const int64_t blocks = (npairs + Gm::G - 1) / Gm::G;
     int remap = 0;
     if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
-    hipLaunchKernelGGL((conv_kernel<LOGM>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream, (int)Bsz,
-                       (int)H, (int)L, (int)npb, npairs, remap, u, y, khat, twtab);
+    hipLaunchKernelGGL((conv_kernel<LOGM, false>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream, (int)Bsz,
+                       (int)H, (int)L, (int)npb, npairs, remap, u, y, khat, twtab, FusedSpec{});
+    return hipGetLastError();
+}
+
+template <int LOGM>
+hipError_t conv_fused_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y, const float2* twtab,
+                             const FusedSpec& fs, hipStream_t stream) {
+    using Gm = Geo<LOGM>;
+    const int64_t npb = (Bsz + 1) / 2;
+    const int64_t npairs = npb * H;
+    const int64_t blocks = (npairs + Gm::G - 1) / Gm::G;
+    int remap = 0;
+    if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
+    hipLaunchKernelGGL((conv_kernel<LOGM, true>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream, (int)Bsz,
+                       (int)H, (int)L, (int)npb, npairs, remap, u, y, nullptr, twtab, fs);
     return hipGetLastError();
 }
 
@@ -283,6 +354,25 @@ hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float
         SSM_CONV_CASE(5) SSM_CONV_CASE(6) SSM_CONV_CASE(7) SSM_CONV_CASE(8) SSM_CONV_CASE(9)
         SSM_CONV_CASE(10) SSM_CONV_CASE(11) SSM_CONV_CASE(12) SSM_CONV_CASE(13) SSM_CONV_CASE(14)
 #undef SSM_CONV_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// The kernel transform runs inside the convolution for transforms of at most
+// 1024 points and at most four row pairs per channel (the repeated transform
+// then costs less than a separate launch and the spectra's HBM round trip).
+bool conv_fuses_spectrum(int64_t Bsz, int64_t M) { return M >= 16 && M <= 1024 && (Bsz + 1) / 2 <= 4; }
+
+hipError_t launch_conv_fused(int64_t Bsz, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                             const int32_t* tstat, const float* D, float2* K_out, int32_t* status, const float* u,
+                             float* y, const float2* twtab, hipStream_t stream) {
+    const FusedSpec fs{roots, tstat, (int)tiles, D, K_out, status};
+    switch (ilog2_exact(M)) {
+#define SSM_FUSED_CASE(LG) \
+    case LG: return conv_fused_launch<LG>(Bsz, H, L, u, y, twtab, fs, stream);
+        SSM_FUSED_CASE(4) SSM_FUSED_CASE(5) SSM_FUSED_CASE(6) SSM_FUSED_CASE(7) SSM_FUSED_CASE(8)
+        SSM_FUSED_CASE(9) SSM_FUSED_CASE(10)
+#undef SSM_FUSED_CASE
         default: return hipErrorInvalidValue;
     }
 }

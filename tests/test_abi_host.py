@@ -40,6 +40,18 @@ def test_transform_lengths_rejects_nonpositive():
         ssm.transform_lengths(0)
 
 
+def test_forward_fused_query():
+    # small transforms with few row pairs per channel take the fused launch
+    assert ssm.forward_fused(8, 1024) and ssm.forward_fused(1, 16)
+    assert not ssm.forward_fused(9, 1024)      # five row pairs per channel
+    assert not ssm.forward_fused(2, 1025)      # M = 2048
+    assert not ssm.forward_fused(2, 8)         # M = 8
+    assert not ssm.forward_fused(2, 65536)     # multi-pass transforms
+    for args in [(0, 16), (1, 0)]:
+        with pytest.raises(ssm.SSMError):
+            ssm.forward_fused(*args)
+
+
 def test_status_strings():
     assert ssm.status_string(ssm.ST_RESONANT_DIAGONAL) == O.RESONANT_DIAGONAL
     assert ssm.status_string(ssm.ST_RESONANT_CORRECTION) == O.RESONANT_CORRECTION
