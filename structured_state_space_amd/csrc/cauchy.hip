@@ -22,9 +22,9 @@
 // Every lane reads the same table row, so the sweep moves 64 copies of each row
 // from LDS per wave: with several roots per thread the row is amortised and the
 // table keeps (w x) and w (wide rows: no per-family products beyond the four
-// multiply-adds); with one or two roots per thread the LDS read rate is the
-// limit, so the table keeps w alone (narrow rows, 8 instead of 16 bytes per
-// family) and the loop forms x inv once per (root, state).
+// multiply-adds); with one or two roots per thread the table keeps w alone
+// (narrow rows, 8 instead of 16 bytes per family, which cuts the LDS read
+// rate) and the loop forms x inv once per (root, state).
 // Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
 // with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
 // flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
@@ -214,6 +214,14 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         for (int f = 0; f < F; ++f) acc[i][f] = make_float2(0.f, 0.f);
 
     double m1x = 0.0, m1y = 0.0;
+    // Small grids (one or two roots per thread) are a single round of
+    // workgroups, four per CU.  Issue priority then falls with progress through
+    // the states (3 in the first quarter, 0 in the last), so that the
+    // workgroups sharing a CU advance together instead of oldest-first, which
+    // leaves the last one to finish alone with nothing to hide its latencies.
+    constexpr bool FAIR = RPT <= 2;
+    const int q1 = N / 4, q2 = N / 2, q3 = (3 * N) / 4;
+    if constexpr (FAIR) __builtin_amdgcn_s_setprio(3);
     for (int n0 = 0; n0 < N; n0 += kChunk) {
         const int nch = min(kChunk, N - n0);
         __syncthreads();
@@ -249,18 +257,20 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         }
         __syncthreads();
         for (int n = 0; n < nch; ++n) {
+            if constexpr (FAIR) {
+                if (n0 + n == q1) __builtin_amdgcn_s_setprio(2);
+                if (n0 + n == q2) __builtin_amdgcn_s_setprio(1);
+                if (n0 + n == q3) __builtin_amdgcn_s_setprio(0);
+            }
             const float4 hd = tbl[n * RW];
-            float inv[RPT], p[RPT], q[RPT], pn[RPT];
+            float inv[RPT], p[RPT], q[RPT];
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const float y = st[i] - hd.y;
                 const float den = fmaf(y, y, hd.x);
                 inv[i] = __builtin_amdgcn_rcpf(den);
                 p[i] = y * inv[i];
-                if constexpr (NARROW) {
-                    q[i] = hd.z * inv[i];           // x inv
-                    pn[i] = (hd.y - st[i]) * inv[i];  // -y inv, kept as its own product
-                }
+                if constexpr (NARROW) q[i] = hd.z * inv[i];  // x inv
             }
             if constexpr (NARROW) {
                 const float2* wrow = reinterpret_cast<const float2*>(tbl + n * RW + 1);
@@ -272,7 +282,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
                         acc[i][f].x = fmaf(w.x, q[i], acc[i][f].x);
                         acc[i][f].x = fmaf(w.y, p[i], acc[i][f].x);
                         acc[i][f].y = fmaf(w.y, q[i], acc[i][f].y);
-                        acc[i][f].y = fmaf(w.x, pn[i], acc[i][f].y);
+                        acc[i][f].y = fmaf(-w.x, p[i], acc[i][f].y);  // negation is a free source modifier
                     }
                 }
             } else {
@@ -291,6 +301,7 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         }
     }
 
+    if constexpr (FAIR) __builtin_amdgcn_s_setprio(0);
     // reduce the z = -1 partial sums when this tile holds k = M/2 (uniform test)
     const int k_lo = tile * (kCauchyThreads * RPT);
     const bool has_m1 = M >= 2 && k_lo <= M / 2 && M / 2 < k_lo + kCauchyThreads * RPT;
