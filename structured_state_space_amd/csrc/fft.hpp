@@ -152,24 +152,30 @@ __device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2
 #pragma unroll
                 for (int q = 0; q < R; ++q) v[s][i + q * NB] = x[q];
             } else {
-                const int base = ((b >> LS) << (LS + LR)) + (b & (NS - 1));
+                // lds_pad(base + q NS) = lds_pad(base) + q NS + (q NS >> 4) for these
+                // power-of-two strides, so one address register serves the R
+                // stores (compile-time offsets)
+                float2* const pb = lds[s] + lds_pad(((b >> LS) << (LS + LR)) + (b & (NS - 1)));
 #pragma unroll
-                for (int q = 0; q < R; ++q) lds[s][lds_pad(base + q * NS)] = x[q];
+                for (int q = 0; q < R; ++q) pb[q * NS + ((q * NS) >> 4)] = x[q];
             }
         }
         if constexpr (!LAST && SHARED) {  // one buffer for all vectors: exchange them in turn
             __syncthreads();
+            const float2* const pr = lds[s] + lds_pad(t);  // lds_pad(t + T e) = lds_pad(t) + T e + (T e >> 4)
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[s][e] = lds[s][lds_pad(t + T * e)];
+            for (int e = 0; e < E; ++e) v[s][e] = pr[T * e + ((T * e) >> 4)];
             __syncthreads();
         }
     }
     if constexpr (!LAST && !SHARED) {
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < NV; ++s)
+        for (int s = 0; s < NV; ++s) {
+            const float2* const pr = lds[s] + lds_pad(t);  // lds_pad(t + T e) = lds_pad(t) + T e + (T e >> 4)
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[s][e] = lds[s][lds_pad(t + T * e)];
+            for (int e = 0; e < E; ++e) v[s][e] = pr[T * e + ((T * e) >> 4)];
+        }
         __syncthreads();
     }
 }

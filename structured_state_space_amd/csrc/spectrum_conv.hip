@@ -162,19 +162,25 @@ struct FusedSpec {
 
 // One group of T threads per pair of batch rows (b, b+1) of one channel:
 // z = u_b + i u_{b+1};  y = IFFT(FFT(z) khat0) + conj(tw) IFFT(FFT(tw z) khat1).
-// FUSED: each group first computes its channel's khat0/khat1 from the root values
-// (inverse transform, truncation to L taps, D at tap 0, two forward transforms)
-// while its input rows load; the group of the channel's first row pair also
-// writes K_out and the channel status.  This repeats the kernel transform once
-// per row pair, which pays only where the grid is small and latency-bound.
+// FUSED: each group computes its channel's khat0/khat1 from the root values
+// itself (inverse transform, truncation to L taps, D at tap 0, two forward
+// transforms), the inverse transform alongside the input's forward transforms;
+// the group of the channel's first row pair also writes K_out and the channel
+// status.  This repeats the kernel transform once per row pair, which pays only
+// where the grid is small and latency-bound.
 template <int LOGM, bool FUSED>
 __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
     float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab, FusedSpec fs) {
     using Gm = Geo<LOGM>;
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE, G = Gm::G;
-    __shared__ float2 lds[G * Gm::NBUF * Gm::LDS];
-    const int grp = threadIdx.x / T;
+    // fused: three transforms at once (one buffer each, or one shared buffer)
+    constexpr int FNBUF = Gm::NBUF == 1 ? 1 : 3;
+    constexpr int NB = FUSED ? FNBUF : Gm::NBUF;
+    __shared__ float2 lds[G * NB * Gm::LDS];
+    // one group per workgroup: the row pair is uniform (scalar registers and
+    // scalar-based addressing)
+    const int grp = G == 1 ? 0 : threadIdx.x / T;
     const int t = threadIdx.x - grp * T;
 
     int64_t wg = blockIdx.x;
@@ -184,12 +190,16 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
     }
     const int64_t pair = wg * G + grp;
     const bool active = pair < npairs;
-    const int h = active ? (int)(pair / npb) : 0;
-    const int b1 = active ? 2 * (int)(pair - (int64_t)h * npb) : 0;
+    int h = active ? (int)(pair / npb) : 0;
+    int b1 = active ? 2 * (int)(pair - (int64_t)h * npb) : 0;
+    if constexpr (G == 1) {  // uniform: keep in scalar registers
+        h = __builtin_amdgcn_readfirstlane(h);
+        b1 = __builtin_amdgcn_readfirstlane(b1);
+    }
     const bool has2 = active && (b1 + 1 < Bsz);
     const size_t row1 = ((size_t)b1 * H + h) * (size_t)L;
     const size_t row2 = row1 + (size_t)H * L;
-    float2* my = lds + grp * Gm::NBUF * Gm::LDS;
+    float2* my = lds + grp * NB * Gm::LDS;
     const float2* kh0 = khat + (size_t)h * 2 * M;
     const float2* kh1 = kh0 + M;
     const TwiddleRegs<LOGM, LOGE, Gm::LRMAX> tw(twtab, LOGM, t);
@@ -208,41 +218,45 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
         float2 v[2][E], tws[PRE ? E : 1], k0[PRE ? E : 1], k1[PRE ? E : 1];
         float2* const bufs[2] = {my, my + (Gm::NBUF - 1) * Gm::LDS};
         if constexpr (FUSED) {
-            float2 rv[1][E];
+            // The root values' inverse transform is run as a forward transform of
+            // their conjugates, together with the input's two forward transforms
+            // (they are independent): three vectors in one pass sequence.
+            float2 x3[3][E];
 #pragma unroll
-            for (int e = 0; e < E; ++e) rv[0][e] = fs.roots[(size_t)h * M + t + T * e];
+            for (int e = 0; e < E; ++e) x3[0][e] = c_conj(fs.roots[(size_t)h * M + t + T * e]);
 #pragma unroll
             for (int e = 0; e < E; ++e) tws[e] = twtab[t + T * e];
 #pragma unroll
-            for (int e = 0; e < E; ++e) v[0][e] = load(e);
+            for (int e = 0; e < E; ++e) {
+                const float2 z = load(e);
+                x3[1][e] = z;
+                x3[2][e] = c_mul(z, tws[e]);
+            }
             for (int i = 0; i < fs.tiles; ++i) chst = max(chst, fs.tile_status[(size_t)h * fs.tiles + i]);
             const bool lead = active && b1 == 0;
             if (lead && t == 0 && fs.status) fs.status[h] = chst;
-            float2* const one[1] = {my};
-            fft_multi<1, LOGM, LOGE, true, false, Gm::LRMAX>(rv, one, t, tw);
+            constexpr int STEP = FNBUF == 1 ? 0 : Gm::LDS;  // FNBUF == 1: one shared buffer
+            float2* const three[3] = {my, my + STEP, my + 2 * STEP};
+            fft_multi<3, LOGM, LOGE, false, FNBUF == 1, Gm::LRMAX>(x3, three, t, tw);
             const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int j = t + T * e;
-                const float2 kv = c_scale(rv[0][e], invM);
-                if (lead && fs.K_out && j < L) fs.K_out[(size_t)h * L + j] = chst ? c_nan() : kv;
-                float kr = j < L ? kv.x : 0.0f;
-                if (j == 0 && fs.D) kr += fs.D[h];
-                k0[e] = make_float2(kr * sc, 0.0f);
-                k1[e] = c_scale(tws[e], kr * sc);
-            }
             float2 w[2][E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                w[0][e] = k0[e];
-                w[1][e] = k1[e];
+                const int j = t + T * e;
+                const float2 kv = c_scale(c_conj(x3[0][e]), invM);
+                if (lead && fs.K_out && j < L) fs.K_out[(size_t)h * L + j] = chst ? c_nan() : kv;
+                float kr = j < L ? kv.x : 0.0f;
+                if (j == 0 && fs.D) kr += fs.D[h];
+                w[0][e] = make_float2(kr * sc, 0.0f);
+                w[1][e] = c_scale(tws[e], kr * sc);
+                v[0][e] = x3[1][e];
+                v[1][e] = x3[2][e];
             }
             fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(w, bufs, t, tw);
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 k0[e] = w[0][e];
                 k1[e] = w[1][e];
-                v[1][e] = c_mul(v[0][e], tws[e]);
             }
         } else {
             if constexpr (PRE) {
@@ -259,8 +273,8 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
                 v[0][e] = z;
                 v[1][e] = c_mul(z, PRE ? tws[PRE ? e : 0] : twtab[t + T * e]);
             }
+            fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
         }
-        fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             v[0][e] = c_mul(v[0][e], PRE ? k0[PRE ? e : 0] : kh0[t + T * e]);
