@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import re
 import sys
@@ -33,7 +34,8 @@ PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed issue)
 DEFAULT_WORKLOAD = "s4-h256-l1k"
 
 KERNEL_SOURCES = {
-    "cauchy": ["cauchy.hip", "common.hpp"],
+    "filter": ["single_launch.hip", "roots.hpp", "fft.hpp", "common.hpp"],
+    "cauchy": ["cauchy.hip", "roots.hpp", "common.hpp"],
     "spectrum": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
     "conv": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
 }
@@ -143,7 +145,8 @@ def main():
 
     w, p, u = I.workload(args.workload)
     M, n_fft = ssm.transform_lengths(w.L)
-    fused = ssm.forward_fused(w.Bsz, w.L)
+    form = ssm.forward_form(w.Bsz, w.H, w.L)
+    fused = form == 2
     d = ssm.to_device(p, dev)
     ut = torch.from_numpy(u).to(dev)
 
@@ -198,13 +201,21 @@ def main():
         for j, k in enumerate(stages):
             acc[k] += evs[i][j].elapsed_time(evs[i][j + 1]) / reps
     phase_ms = {k: acc[k] / args.steps for k in stages}
-    # fused: stage 2 launches nothing and the convolution kernel includes it
-    names = ("cauchy", "conv") if fused else stages
+    # form 2: stage 2 launches nothing and the convolution kernel includes it;
+    # form 1: one kernel does everything (timed as stage 1)
+    names = ("filter",) if form == 1 else ("cauchy", "conv") if fused else stages
+    if form == 1:
+        phase_ms["filter"] = phase_ms["cauchy"]
     if M > 16384:
         # the repeated multi-pass kernel transform regenerates the root values each time
         phase_ms["spectrum"] -= phase_ms["cauchy"] * (reps - 1) / reps
 
     alg = algorithmic(w, M, fused)
+    if form == 1:
+        # the single launch is VALU-bound: rated on the root values' flops plus
+        # the convolution's transform flops, Bsz*H*(5 n log2 n + 6 (n/2 + 1)), n = n_fft
+        conv_flops = w.Bsz * w.H * (5 * n_fft * int(math.log2(n_fft)) + 6 * (n_fft // 2 + 1))
+        alg["filter"] = dict(alg["cauchy"], work=alg["cauchy"]["work"] + conv_flops)
     phases = {}
     for k in names:
         a = alg[k]
@@ -223,7 +234,7 @@ def main():
         "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "f32", "data": "synthetic",
         "config": {"workload": w.name, "H": w.H, "N": w.N, "r": w.r, "L": w.L, "M": M, "n_fft": n_fft,
-                   "batch": w.Bsz, "spectrum_fused_into_conv": fused},
+                   "batch": w.Bsz, "launch_form": form},
         "roofline": roofline,
         "phases": phases,
         "composite_roofline_frac": troof_ms / ms_per_step,

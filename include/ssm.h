@@ -87,12 +87,17 @@ int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, in
  * Pure integer host computation; SSM_ERR_INVALID_ARGUMENT for L < 1. */
 int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft);
 
-/* Whether ssm_forward forms the kernel spectra inside its convolution kernel
- * (*fused = 1: two launches, no spectra in the workspace) or in a separate
- * kernel-transform launch (*fused = 0) for a batch of Bsz rows and kernel
- * length L.  Informational only: the results are the same either way.  Pure
- * host computation; SSM_ERR_INVALID_ARGUMENT for Bsz < 1, L < 1 or null. */
-int ssm_forward_fused(int64_t Bsz, int64_t L, int32_t* fused);
+/* Launch form ssm_forward takes for Bsz rows, H channels and kernel length L:
+ *   *form = 1: one launch (one workgroup per channel computes root values,
+ *              kernel, spectra and all its rows' convolutions; M = 1024, at
+ *              most 8 rows, H >= 256);
+ *   *form = 2: root values, then a convolution kernel that forms the spectra
+ *              itself (M <= 1024, at most 8 rows);
+ *   *form = 3: root values, kernel transform + spectra, convolution (multi-pass
+ *              transforms above M = 16384).
+ * Informational only: the results are the same in every form.  Pure host
+ * computation; SSM_ERR_INVALID_ARGUMENT for Bsz, H or L < 1 or null. */
+int ssm_forward_form(int64_t Bsz, int64_t H, int64_t L, int32_t* form);
 
 /* Static description of a return code or status code (never NULL). */
 const char* ssm_status_string(int code);
@@ -170,9 +175,10 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
  * idempotent), and four caller-created hipEvent_t (passed as void*) are
  * recorded on `stream`: events[0] before the first stage, events[i] after
  * stage i.  (events[i] - events[i-1]) / repeat is then a stage's duration per
- * launch with the dispatch gaps amortised.  Where ssm_forward_fused reports 1,
- * stage 2 launches nothing and stage 3 includes the kernel transform.  events
- * must not be NULL.
+ * launch with the dispatch gaps amortised.  In form 2 (ssm_forward_form) stage
+ * 2 launches nothing and stage 3 includes the kernel transform; in form 1 stage
+ * 1 is the single launch and stages 2 and 3 are empty.  events must not be
+ * NULL.
  */
 int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
                          const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,

@@ -16,6 +16,11 @@ hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                        const float2* twtab, hipStream_t stream);
 bool conv_fuses_spectrum(int64_t Bsz, int64_t M);
+bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M);
+hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
+                         const float2* P, const float2* Q, const float2* Bv, const float2* Ct, const float* dt,
+                         const float* D, const float* u, float* y, float2* K_out, int32_t* status,
+                         hipStream_t stream);
 hipError_t launch_conv_fused(int64_t Bsz, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                              const int32_t* tstat, const float* D, float2* K_out, int32_t* status, const float* u,
                              float* y, const float2* twtab, hipStream_t stream);
@@ -109,10 +114,17 @@ int ssm_transform_lengths(int64_t L, int64_t* M, int64_t* n_fft) {
     return SSM_OK;
 }
 
-int ssm_forward_fused(int64_t Bsz, int64_t L, int32_t* fused) {
-    if (Bsz < 1 || L < 1 || L > ((int64_t)1 << 61) || !fused) return SSM_ERR_INVALID_ARGUMENT;
-    const int64_t M = pow2_at_least(L);
-    *fused = (M <= ((int64_t)1 << kMaxLdsLogM) && conv_fuses_spectrum(Bsz, M)) ? 1 : 0;
+namespace {
+int forward_form(int64_t Bsz, int64_t H, int64_t M) {
+    if (M > ((int64_t)1 << kMaxLdsLogM)) return 3;
+    if (single_launch_fits(Bsz, H, M)) return 1;
+    return conv_fuses_spectrum(Bsz, M) ? 2 : 3;
+}
+}  // namespace
+
+int ssm_forward_form(int64_t Bsz, int64_t H, int64_t L, int32_t* form) {
+    if (Bsz < 1 || H < 1 || L < 1 || L > ((int64_t)1 << 61) || !form) return SSM_ERR_INVALID_ARGUMENT;
+    *form = forward_form(Bsz, H, pow2_at_least(L));
     return SSM_OK;
 }
 
@@ -253,12 +265,21 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     auto mark = [&](int i) { return ev ? hipEventRecord((hipEvent_t)ev[i], s) : hipSuccess; };
     if (mark(0) != hipSuccess) return SSM_ERR_DEVICE;
     hipError_t e = hipSuccess;
+    const int form = forward_form(Bsz, H, M);
+    if (form == 1) {  // one launch: stages 2 and 3 are empty
+        for (int i = 0; i < repeat && e == hipSuccess; ++i)
+            e = launch_single(Bsz, H, N, r, L, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                              (const float2*)B, (const float2*)Ctilde, dt, D, u, y, (float2*)K_out, status, s);
+        if (e != hipSuccess || mark(1) != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess)
+            return SSM_ERR_DEVICE;
+        return SSM_OK;
+    }
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
                           (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
-    const bool fused = !large && conv_fuses_spectrum(Bsz, M);
+    const bool fused = form == 2;
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
     for (int i = 0; i < repeat && e == hipSuccess && !fused; ++i) {

@@ -32,105 +32,11 @@
 #include <float.h>
 
 #include "common.hpp"
+#include "roots.hpp"
 
 namespace ssm {
 
 namespace {
-
-template <int RK>
-struct Fam {
-    static constexpr int F = (RK + 1) * (RK + 1);
-    static constexpr int ROW = 1 + F;  // float4 per state, wide rows: header + one per family
-    static constexpr int ROWN = 1 + (F + 1) / 2;  // narrow rows: header + a float2 per family
-    // states staged in LDS at a time (<= 26 KB): the whole state vector for N up to this
-    static constexpr int CHUNK = RK == 1 ? 256 : RK == 2 ? 128 : 64;
-};
-
-__device__ __forceinline__ float2 cdivf(float2 a, float2 b) {
-    const float den = fmaf(b.x, b.x, b.y * b.y);
-    const float inv = 1.0f / den;
-    return make_float2(fmaf(a.x, b.x, a.y * b.y) * inv, fmaf(a.y, b.x, -a.x * b.y) * inv);
-}
-
-__device__ __forceinline__ float cabs1(float2 a) { return fabsf(a.x) + fabsf(a.y); }
-
-// Solve W x = rhs in place (x returned in rhs), W r x r complex.  Gaussian
-// elimination with partial pivoting; false when a pivot is exactly zero.
-template <int RK>
-__device__ __forceinline__ bool small_solve(float2 (&W)[RK][RK], float2 (&rhs)[RK]) {
-#pragma unroll
-    for (int c = 0; c < RK; ++c) {
-#pragma unroll
-        for (int r = c + 1; r < RK; ++r) {
-            const bool sw = cabs1(W[r][c]) > cabs1(W[c][c]);
-#pragma unroll
-            for (int j = 0; j < RK; ++j) {
-                const float2 a = W[c][j], b = W[r][j];
-                W[c][j] = sw ? b : a;
-                W[r][j] = sw ? a : b;
-            }
-            const float2 a = rhs[c], b = rhs[r];
-            rhs[c] = sw ? b : a;
-            rhs[r] = sw ? a : b;
-        }
-        if (W[c][c].x == 0.0f && W[c][c].y == 0.0f) return false;
-#pragma unroll
-        for (int r = c + 1; r < RK; ++r) {
-            const float2 f = cdivf(W[r][c], W[c][c]);
-#pragma unroll
-            for (int j = c + 1; j < RK; ++j) W[r][j] = c_sub(W[r][j], c_mul(f, W[c][j]));
-            rhs[r] = c_sub(rhs[r], c_mul(f, rhs[c]));
-        }
-    }
-#pragma unroll
-    for (int c = RK - 1; c >= 0; --c) {
-        float2 s = rhs[c];
-#pragma unroll
-        for (int j = c + 1; j < RK; ++j) s = c_sub(s, c_mul(W[c][j], rhs[j]));
-        rhs[c] = cdivf(s, W[c][c]);
-    }
-    return true;
-}
-
-// u vector of family row iu (0: C~, 1+a: Q_a), v vector of column iv (0: B, 1+b: P_b)
-template <int RK>
-__device__ __forceinline__ float2 fam_u(const float2* Ct, const float2* Q, size_t hn, int iu) {
-    return iu == 0 ? Ct[hn] : Q[hn * RK + (iu - 1)];
-}
-template <int RK>
-__device__ __forceinline__ float2 fam_v(const float2* Bv, const float2* P, size_t hn, int iv) {
-    return iv == 0 ? Bv[hn] : P[hn * RK + (iv - 1)];
-}
-
-// Slow path for one root whose fast sums are not finite: exact resonance test,
-// else the sums again with a scaled complex reciprocal.
-template <int RK>
-__device__ __forceinline__ bool root_recheck(int N, size_t hbase, float st, const float2* Lambda, const float2* P,
-                                          const float2* Q, const float2* Bv, const float2* Ct,
-                                          float2 (&acc)[Fam<RK>::F]) {
-    for (int n = 0; n < N; ++n) {
-        const float2 lam = Lambda[hbase + n];
-        const float x = -lam.x, y = st - lam.y;
-        if (x == 0.0f && y == 0.0f) return false;
-    }
-#pragma unroll
-    for (int f = 0; f < Fam<RK>::F; ++f) acc[f] = make_float2(0.f, 0.f);
-    for (int n = 0; n < N; ++n) {
-        const float2 lam = Lambda[hbase + n];
-        const float2 g = cdivf(make_float2(1.f, 0.f), make_float2(-lam.x, st - lam.y));
-        const float2 gs = (isfinite(g.x) && isfinite(g.y))
-                              ? g
-                              : c_from(z_inv(make_double2(-(double)lam.x, (double)st - (double)lam.y)));
-#pragma unroll
-        for (int iu = 0; iu <= RK; ++iu)
-#pragma unroll
-            for (int iv = 0; iv <= RK; ++iv) {
-                const float2 w = c_mul(c_conj(fam_u<RK>(Ct, Q, hbase + n, iu)), fam_v<RK>(Bv, P, hbase + n, iv));
-                acc[iu * (RK + 1) + iv] = c_add(acc[iu * (RK + 1) + iv], c_mul(w, gs));
-            }
-    }
-    return true;
-}
 
 // Per-root tables, once per call: tan(pi k/M) in float64 (0 at k = M/2, which
 // takes the finite z = -1 formula) and exp(-i pi k/M) for the later transforms.
@@ -241,64 +147,10 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
                 uu[1 + j] = Q[hn * RK + j];
                 vv[1 + j] = P[hn * RK + j];
             }
-#pragma unroll
-            for (int iu = 0; iu <= RK; ++iu)
-#pragma unroll
-                for (int iv = 0; iv <= RK; ++iv) {
-                    const float2 w = c_mul(c_conj(uu[iu]), vv[iv]);
-                    const int f = iu * (RK + 1) + iv;
-                    if constexpr (NARROW)
-                        reinterpret_cast<float2*>(tbl + nn * RW + 1)[f] = w;
-                    else
-                        tbl[nn * RW + 1 + f] = make_float4(w.x * x, w.y * x, w.y, -w.x);
-                }
-            if constexpr (NARROW && (F & 1))  // pad the last float4 of the row
-                reinterpret_cast<float2*>(tbl + nn * RW + 1)[F] = make_float2(0.f, 0.f);
+            stage_row<RK, NARROW>(tbl + nn * RW, lam, uu, vv);
         }
         __syncthreads();
-        for (int n = 0; n < nch; ++n) {
-            if constexpr (FAIR) {
-                if (n0 + n == q1) __builtin_amdgcn_s_setprio(2);
-                if (n0 + n == q2) __builtin_amdgcn_s_setprio(1);
-                if (n0 + n == q3) __builtin_amdgcn_s_setprio(0);
-            }
-            const float4 hd = tbl[n * RW];
-            float inv[RPT], p[RPT], q[RPT];
-#pragma unroll
-            for (int i = 0; i < RPT; ++i) {
-                const float y = st[i] - hd.y;
-                const float den = fmaf(y, y, hd.x);
-                inv[i] = __builtin_amdgcn_rcpf(den);
-                p[i] = y * inv[i];
-                if constexpr (NARROW) q[i] = hd.z * inv[i];  // x inv
-            }
-            if constexpr (NARROW) {
-                const float2* wrow = reinterpret_cast<const float2*>(tbl + n * RW + 1);
-#pragma unroll
-                for (int f = 0; f < F; ++f) {
-                    const float2 w = wrow[f];
-#pragma unroll
-                    for (int i = 0; i < RPT; ++i) {
-                        acc[i][f].x = fmaf(w.x, q[i], acc[i][f].x);
-                        acc[i][f].x = fmaf(w.y, p[i], acc[i][f].x);
-                        acc[i][f].y = fmaf(w.y, q[i], acc[i][f].y);
-                        acc[i][f].y = fmaf(-w.x, p[i], acc[i][f].y);  // negation is a free source modifier
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int f = 0; f < F; ++f) {
-                    const float4 w = tbl[n * RW + 1 + f];
-#pragma unroll
-                    for (int i = 0; i < RPT; ++i) {
-                        acc[i][f].x = fmaf(w.x, inv[i], acc[i][f].x);
-                        acc[i][f].x = fmaf(w.z, p[i], acc[i][f].x);
-                        acc[i][f].y = fmaf(w.y, inv[i], acc[i][f].y);
-                        acc[i][f].y = fmaf(w.w, p[i], acc[i][f].y);
-                    }
-                }
-            }
-        }
+        sweep_chunk<RK, RPT, NARROW, FAIR>(tbl, nch, n0, q1, q2, q3, st, acc);
     }
 
     if constexpr (FAIR) __builtin_amdgcn_s_setprio(0);
@@ -326,41 +178,8 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     for (int i = 0; i < RPT; ++i) {
         const int k = kk[i];
         if (k >= M) continue;
-        float2 H;
-        if (2 * k == M) {
-            // z = -1: (dt/2) C~^* B
-            H = make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y));
-        } else {
-            bool finite = true;
-#pragma unroll
-            for (int f = 0; f < F; ++f) finite = finite && isfinite(acc[i][f].x) && isfinite(acc[i][f].y);
-            bool resonant = false;
-            if (!finite) resonant = !root_recheck<RK>(N, hbase, st[i], Lambda, P, Q, Bv, Ct, acc[i]);
-            if (resonant) {
-                my_status = max(my_status, SSM_ST_RESONANT_DIAGONAL);
-                H = c_nan();
-            } else {
-                float2 W[RK][RK], rhs[RK];
-#pragma unroll
-                for (int r1 = 0; r1 < RK; ++r1) {
-                    rhs[r1] = acc[i][(1 + r1) * (RK + 1)];
-#pragma unroll
-                    for (int c1 = 0; c1 < RK; ++c1) {
-                        W[r1][c1] = acc[i][(1 + r1) * (RK + 1) + 1 + c1];
-                        if (r1 == c1) W[r1][c1].x += 1.0f;
-                    }
-                }
-                if (!small_solve<RK>(W, rhs)) {
-                    my_status = max(my_status, SSM_ST_RESONANT_CORRECTION);
-                    H = c_nan();
-                } else {
-                    float2 s = acc[i][0];
-#pragma unroll
-                    for (int b1 = 0; b1 < RK; ++b1) s = c_sub(s, c_mul(acc[i][1 + b1], rhs[b1]));
-                    H = c_mul(make_float2(1.0f, tf[i]), s);
-                }
-            }
-        }
+        const float2 H = 2 * k == M ? make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y))
+                                    : finish_root<RK>(acc[i], st[i], tf[i], N, hbase, Lambda, P, Q, Bv, Ct, my_status);
         roots[(size_t)h * M + k] = H;
     }
     if (my_status) atomicMax(&blk_status, my_status);

@@ -1,0 +1,273 @@
+// The whole filter path in one launch for 1024-point transforms: one
+// 1024-thread workgroup per channel computes the channel's root values, its
+// kernel and spectra, and the convolution of all its batch rows.
+//
+// Sources: "Recurrent, LSTM, and structured state-space models" -- S4
+// Algorithm 1 / App. C (root values of the truncated generating function at
+// the M-th roots of unity, the kernel as the first L coefficients of their
+// inverse transform), DPLR block (y = K * u + D u) and radix-two DFT block
+// (exact linear product by zero padding).
+//
+// Used where every channel's rows fit one workgroup (at most four row pairs)
+// and there are enough channels to give every CU a workgroup.  Against the
+// two-launch form it keeps the root values in LDS, loads the input rows while
+// the root values are being computed, and has no second launch.
+//
+// Phase A (all 1024 threads, one root each): as the root-value kernel with one
+// root per thread and narrow table rows (roots.hpp); the twiddles
+// exp(-i pi j/M) go to LDS; the root values to LDS.
+// Phase B (eight groups of 128 threads, 8 points per thread): z-half i = 2p + c
+// is row pair p's input z = u_{2p} + i u_{2p+1}, twisted by exp(-i pi j/M)
+// when c = 1 (the two halves of the zero-padded product, as in the convolution
+// kernel).  Three transform stages, in which every group runs the same code
+// (so every wave meets the same workgroup barriers) on data chosen by its
+// group index:
+//   B1: group 0 transforms the conjugated root values (inverse transform of
+//       the root values); group g > 0 transforms z-half g.
+//   B2: groups 0 and 1 transform the kernel's cyclic and twisted sequences
+//       (spectra); group 2 transforms z-half 0 for group 0; the others run the
+//       stage on zeros.
+//   B3: group g multiplies its z-half spectrum by the spectrum of its half and
+//       inverse-transforms; the twisted halves are untwisted and added to the
+//       cyclic ones through LDS; rows are stored.
+#include <float.h>
+
+#include "common.hpp"
+#include "fft.hpp"
+#include "roots.hpp"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kLogM1 = 10, kM1 = 1 << kLogM1;
+constexpr int kThreads1 = 1024;
+constexpr int kLogE1 = 3, kE1 = 1 << kLogE1, kT1 = kM1 >> kLogE1;  // 8 points, 128 threads per transform
+constexpr int kGroups1 = kThreads1 / kT1;                           // 8 = 4 row pairs x 2 halves
+constexpr int kLdsV1 = lds_padded_size(kM1);
+
+template <int RK>
+__global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
+    int Bsz, int H, int N, int L, const float2* __restrict__ Lambda, const float2* __restrict__ P,
+    const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
+    const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ u, float* __restrict__ y,
+    float2* __restrict__ K_out, int32_t* __restrict__ status) {
+    constexpr int M = kM1, E = kE1, T = kT1;
+    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK, RW = Fam<RK>::ROWN;
+    __shared__ float4 tbl[kChunk * RW];
+    __shared__ float2 twl[M];       // exp(-i pi j/M)
+    __shared__ float2 rootl[M];     // root values
+    __shared__ float kl[M];         // real kernel taps (+D), scaled 1/(2M)
+    __shared__ float2 khl[2][M];    // cyclic and twisted spectra
+    __shared__ float2 xfer[M];      // z-half 0 and its spectrum, handed between groups 0 and 2
+    __shared__ float2 fbuf[kGroups1][kLdsV1];
+    __shared__ int blk_status;
+    __shared__ double2 red[kThreads1 / 64];
+
+    const int h = blockIdx.x;
+    const int tid = threadIdx.x;
+    const size_t hbase = (size_t)h * N;
+    // group index, uniform per wave: scalar branches only
+    const int g = __builtin_amdgcn_readfirstlane(tid / T);
+    const int t = tid - g * T;
+    const int pr = g >> 1, half = g & 1;
+    const int npb = (Bsz + 1) / 2;
+    const bool pact = pr < npb;
+    const int b1 = 2 * pr;
+    const bool has2 = pact && b1 + 1 < Bsz;
+    const size_t row1 = pact ? ((size_t)b1 * H + h) * (size_t)L : 0;
+    const size_t row2 = has2 ? row1 + (size_t)H * L : row1;
+
+    float2 z[E];
+
+    // ---- phase A: root values, one per thread (k = tid) ----
+    if (tid == 0) blk_status = 0;
+    const float dtv = dt[h];
+    const bool bad_dt = !(dtv > 0.0f) || !(dtv <= FLT_MAX);  // uniform
+    const int k = tid;
+    double sn, cs;
+    sincospi((double)k / (double)M, &sn, &cs);
+    twl[k] = make_float2((float)cs, (float)-sn);
+    const double tk = (2 * k == M) ? 0.0 : sn / cs;
+    const double a = bad_dt ? 0.0 : 2.0 / (double)dtv;
+    const float st[1] = {(float)(a * tk)};
+    float2 acc[1][F];
+#pragma unroll
+    for (int f = 0; f < F; ++f) acc[0][f] = make_float2(0.f, 0.f);
+    // issue priority falls with progress through the states so that the
+    // block's waves advance together (the phase ends at a barrier)
+    const int q1 = N / 4, q2 = N / 2, q3 = (3 * N) / 4;
+    __builtin_amdgcn_s_setprio(3);
+    double m1x = 0.0, m1y = 0.0;
+    for (int n0 = 0; n0 < N; n0 += kChunk) {
+        const int nch = min(kChunk, N - n0);
+        __syncthreads();
+        if (tid < nch) {
+            const size_t hn = hbase + n0 + tid;
+            const float2 lam = Lambda[hn];
+            float2 uu[RK + 1], vv[RK + 1];
+            uu[0] = Ct[hn];
+            vv[0] = Bv[hn];
+            // z = -1 takes (dt/2) C~^* B: partial sums in float64
+            m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
+            m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                uu[1 + j] = Q[hn * RK + j];
+                vv[1 + j] = P[hn * RK + j];
+            }
+            stage_row<RK, true>(tbl + tid * RW, lam, uu, vv);
+        }
+        __syncthreads();
+        if (n0 == 0) {
+            // this group's input rows, fetched once the state inputs are in (a
+            // wait for those would otherwise also wait for these) so that the
+            // loads overlap the sweep
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int j = t + T * e;
+                const bool in = pact && j < L;
+                z[e] = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+            }
+        }
+        sweep_chunk<RK, 1, true, true>(tbl, nch, n0, q1, q2, q3, st, acc);
+    }
+    __builtin_amdgcn_s_setprio(0);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+        m1x += __shfl_xor(m1x, o, 64);
+        m1y += __shfl_xor(m1y, o, 64);
+    }
+    if ((tid & 63) == 0) red[tid >> 6] = make_double2(m1x, m1y);
+    __syncthreads();
+    int my_status = 0;
+    float2 Hk;
+    if (2 * k == M) {  // z = -1: (dt/2) C~^* B
+        double2 m1 = make_double2(0.0, 0.0);
+#pragma unroll
+        for (int wv = 0; wv < kThreads1 / 64; ++wv) {
+            m1.x += red[wv].x;
+            m1.y += red[wv].y;
+        }
+        Hk = make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y));
+    } else {
+        Hk = finish_root<RK>(acc[0], st[0], (float)tk, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+    }
+    if (bad_dt) {
+        my_status = SSM_ST_INVALID_STEP;
+        Hk = c_nan();
+    }
+    rootl[k] = Hk;
+    if (my_status) atomicMax(&blk_status, my_status);
+    if (g == 0) {  // group 0 owns z-half 0 but transforms the root values in B1: hand z to group 2
+#pragma unroll
+        for (int e = 0; e < E; ++e) xfer[t + T * e] = z[e];
+    }
+    __syncthreads();
+    const int chst = blk_status;
+    if (tid == 0 && status) status[h] = chst;
+
+    // ---- phase B ----
+    const TwiddleRegs<kLogM1, kLogE1> tw(twl, kLogM1, t);
+    float2* const mine[1] = {fbuf[g]};
+    float2 x[1][E];
+
+    // B1
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        x[0][e] = g == 0 ? c_conj(rootl[j]) : (half ? c_mul(z[e], twl[j]) : z[e]);
+    }
+    fft_multi<1, kLogM1, kLogE1, false>(x, mine, t, tw);
+    float2 zs[E];  // this group's z-half spectrum (groups > 0)
+#pragma unroll
+    for (int e = 0; e < E; ++e) zs[e] = make_float2(0.0f, 0.0f);
+    const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
+    if (g == 0) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            const float2 kv = c_scale(c_conj(x[0][e]), invM);
+            if (K_out && j < L) K_out[(size_t)h * L + j] = chst ? c_nan() : kv;
+            float kr = j < L ? kv.x : 0.0f;
+            if (j == 0 && D) kr += D[h];
+            kl[j] = kr * sc;
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < E; ++e) zs[e] = x[0][e];
+    }
+    __syncthreads();
+
+    // B2
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        x[0][e] = g == 0   ? make_float2(kl[j], 0.0f)
+                  : g == 1 ? c_scale(twl[j], kl[j])
+                  : g == 2 ? xfer[j]
+                           : make_float2(0.0f, 0.0f);
+    }
+    fft_multi<1, kLogM1, kLogE1, false>(x, mine, t, tw);
+    if (g <= 1) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) khl[g][t + T * e] = x[0][e];
+    } else if (g == 2) {  // its own reads of xfer all came before the transform's barriers
+#pragma unroll
+        for (int e = 0; e < E; ++e) xfer[t + T * e] = x[0][e];
+    }
+    __syncthreads();
+
+    // B3
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        const float2 s = g == 0 ? xfer[j] : zs[e];
+        x[0][e] = c_mul(s, khl[half][j]);
+    }
+    fft_multi<1, kLogM1, kLogE1, true>(x, mine, t, tw);
+    // the transform's last exchange ended at a barrier: fbuf is free again
+    if (half) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            fbuf[g][j] = c_mul(x[0][e], c_conj(twl[j]));
+        }
+    }
+    __syncthreads();
+    if (!half && pact) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            if (j < L) {
+                float2 o = c_add(x[0][e], fbuf[g + 1][j]);
+                if (chst) o = c_nan();
+                y[row1 + j] = o.x;
+                if (has2) y[row2 + j] = o.y;
+            }
+        }
+    }
+}
+
+}  // namespace
+
+bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M) {
+    return M == kM1 && (Bsz + 1) / 2 <= kGroups1 / 2 && H >= 256;
+}
+
+hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
+                         const float2* P, const float2* Q, const float2* Bv, const float2* Ct, const float* dt,
+                         const float* D, const float* u, float* y, float2* K_out, int32_t* status,
+                         hipStream_t stream) {
+#define SSM_SINGLE(RK)                                                                                        \
+    if (r == RK) {                                                                                            \
+        hipLaunchKernelGGL((filter_m1024_kernel<RK>), dim3((unsigned)H), dim3(kThreads1), 0, stream, (int)Bsz, \
+                           (int)H, (int)N, (int)L, Lambda, P, Q, Bv, Ct, dt, D, u, y, K_out, status);         \
+        return hipGetLastError();                                                                             \
+    }
+    SSM_SINGLE(1) SSM_SINGLE(2) SSM_SINGLE(3) SSM_SINGLE(4)
+#undef SSM_SINGLE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

@@ -31,7 +31,7 @@ ST_SINGULAR_BILINEAR = 18
 ST_INVALID_STEP = 19
 OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD = 0, 1, 2, 3
 
-EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_fused", "ssm_status_string",
+EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
            "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled")
 
 
@@ -51,8 +51,8 @@ def _load():
     lib.ssm_workspace_bytes.restype = i32
     lib.ssm_transform_lengths.argtypes = [i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     lib.ssm_transform_lengths.restype = i32
-    lib.ssm_forward_fused.argtypes = [i64, i64, ctypes.POINTER(ctypes.c_int32)]
-    lib.ssm_forward_fused.restype = i32
+    lib.ssm_forward_form.argtypes = [i64, i64, i64, ctypes.POINTER(ctypes.c_int32)]
+    lib.ssm_forward_form.restype = i32
     lib.ssm_status_string.argtypes = [i32]
     lib.ssm_status_string.restype = ctypes.c_char_p
     lib.ssm_discretize.argtypes = [i64, i64, i64, i64] + [vp] * 10 + [vp, sz, vp]
@@ -83,13 +83,14 @@ def transform_lengths(L: int):
     return M.value, n.value
 
 
-def forward_fused(Bsz: int, L: int) -> bool:
-    """ssm_forward_fused: True when ssm_forward forms the spectra inside its convolution."""
+def forward_form(Bsz: int, H: int, L: int) -> int:
+    """ssm_forward_form: 1 (single launch), 2 (root values + convolution with
+    spectra) or 3 (root values, spectra, convolution)."""
     out = ctypes.c_int32()
-    rc = lib.ssm_forward_fused(int(Bsz), int(L), ctypes.byref(out))
+    rc = lib.ssm_forward_form(int(Bsz), int(H), int(L), ctypes.byref(out))
     if rc != OK:
-        raise SSMError("ssm_forward_fused", rc)
-    return bool(out.value)
+        raise SSMError("ssm_forward_form", rc)
+    return out.value
 
 
 def workspace_bytes(op: int, Bsz: int, H: int, N: int, r: int, L: int) -> int:

@@ -40,16 +40,19 @@ def test_transform_lengths_rejects_nonpositive():
         ssm.transform_lengths(0)
 
 
-def test_forward_fused_query():
-    # small transforms with few row pairs per channel take the fused launch
-    assert ssm.forward_fused(8, 1024) and ssm.forward_fused(1, 16)
-    assert not ssm.forward_fused(9, 1024)      # five row pairs per channel
-    assert not ssm.forward_fused(2, 1025)      # M = 2048
-    assert not ssm.forward_fused(2, 8)         # M = 8
-    assert not ssm.forward_fused(2, 65536)     # multi-pass transforms
-    for args in [(0, 16), (1, 0)]:
+def test_forward_form_query():
+    assert ssm.forward_form(8, 256, 1024) == 1     # one workgroup per channel
+    assert ssm.forward_form(8, 256, 600) == 1      # M = 1024
+    assert ssm.forward_form(8, 128, 1024) == 2     # too few channels for one launch
+    assert ssm.forward_form(8, 256, 512) == 2      # M = 512
+    assert ssm.forward_form(1, 1, 16) == 2
+    assert ssm.forward_form(9, 256, 1024) == 3     # five row pairs per channel
+    assert ssm.forward_form(2, 256, 1025) == 3     # M = 2048
+    assert ssm.forward_form(2, 256, 8) == 3        # M = 8
+    assert ssm.forward_form(2, 256, 65536) == 3    # multi-pass transforms
+    for args in [(0, 1, 16), (1, 0, 16), (1, 1, 0)]:
         with pytest.raises(ssm.SSMError):
-            ssm.forward_fused(*args)
+            ssm.forward_form(*args)
 
 
 def test_status_strings():

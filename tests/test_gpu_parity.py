@@ -250,6 +250,50 @@ def test_invalid_step_status():
 
 
 # ---------------------------------------------------------------------------
+# launch forms: the single launch (one workgroup per channel) against the
+# separate root-value / transform / convolution kernels and the oracle,
+# including a channel with an invalid step and one with an exact pole
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r,L,Bsz", [(1, 1024, 8), (2, 600, 3), (1, 777, 1), (3, 1000, 6)])
+def test_single_launch_form(r, L, Bsz):
+    ssm = _ssm()
+    H, N = 256, 48
+    assert ssm.forward_form(Bsz, H, L) == 1
+    p = I.random_params(7000 + 10 * r + Bsz, H, N, r, L)
+    p.dt[5] = 0.0                       # invalid step
+    p.dt[7] = 0.5                       # a = 2/dt = 4 exactly; tan(pi/4) = 1 exactly
+    p.Lambda[7, 0] = 4.0j               # so s(z_{M/4}) = lambda_0: an exact pole
+    u = I.random_input(L + Bsz, Bsz, H, L)
+    d = _dev(p)
+    ut = torch.from_numpy(u).to(DEV)
+    Ct = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_bbar=False)["Ctilde"]
+    fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut, want_kernel=True)
+    kg = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], L)
+    y_sep = ssm.fftconv(kg["K"], ut, D=d["D"])
+    torch.cuda.synchronize()
+    st, st_sep = _np(fw["status"]), _np(kg["status"])
+    expect = np.zeros(H, np.int32)
+    expect[5], expect[7] = ssm.ST_INVALID_STEP, ssm.ST_RESONANT_DIAGONAL
+    assert list(st) == list(expect) and list(st_sep) == list(expect)
+    K, y, Ks, ys = _np(fw["K"]), _np(fw["y"]), _np(kg["K"]), _np(y_sep)
+    for h in (5, 7):
+        assert np.isnan(K[h]).all() and np.isnan(y[:, h, :]).all()
+    ok = np.array([h for h in range(H) if h not in (5, 7)])
+    assert np.isfinite(K[ok]).all() and np.isfinite(y[:, ok, :]).all()
+    for h in ok:
+        assert_rows_close(K[h][None], Ks[h][None], what=f"K h{h} vs separate kernels")
+        assert_rows_close(y[:, h, :], ys[:, h, :], what=f"y h{h} vs separate kernels")
+    for h in sample_channels(H, 3, seed=r + L):
+        h = int(h)
+        if h in (5, 7):
+            continue
+        c = p.channel(h)
+        ref = O.channel_reference(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], c["D"], u[:, h, :], L)
+        assert_rows_close(K[h][None], ref["K"][None], what=f"K h{h} vs oracle")
+        assert_rows_close(y[:, h, :], ref["y"], what=f"y h{h} vs oracle")
+
+
+# ---------------------------------------------------------------------------
 # edge cases: ragged and tiny lengths, odd batch, any N and r, unordered poles
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
