@@ -29,6 +29,20 @@
 namespace ssm {
 
 __host__ __device__ constexpr int lds_pad(int i) { return i + (i >> 4); }
+
+// Synchronisation of an LDS exchange: the workgroup barrier, or (WAVE: the
+// transform is held by a single wavefront) a wave-level barrier with release /
+// acquire fences, which orders the wave's own LDS writes and reads.
+template <bool WAVE>
+__device__ __forceinline__ void lds_sync() {
+    if constexpr (WAVE) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    } else {
+        __syncthreads();
+    }
+}
 __host__ __device__ constexpr int lds_padded_size(int n) { return n + (n >> 4) + 1; }
 
 // a * exp(-+ 2 pi i K/R) for a compile-time K < R/2, R <= 16
@@ -121,7 +135,7 @@ struct TwiddleRegs {
     __device__ __forceinline__ float2 get(int i, int) const { return w[P][i]; }
 };
 
-template <int NV, int LOGN, int LOGE, bool INV, int P, int LR, int LS, bool LAST, bool SHARED, class TW>
+template <int NV, int LOGN, int LOGE, bool INV, int P, int LR, int LS, bool LAST, bool SHARED, bool WAVE, class TW>
 __device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
                                               const TW& tw) {
     constexpr int E = 1 << LOGE, N = 1 << LOGN, T = N >> LOGE, R = 1 << LR, NB = E / R, NS = 1 << LS;
@@ -161,27 +175,28 @@ __device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2
             }
         }
         if constexpr (!LAST && SHARED) {  // one buffer for all vectors: exchange them in turn
-            __syncthreads();
+            lds_sync<WAVE>();
             const float2* const pr = lds[s] + lds_pad(t);  // lds_pad(t + T e) = lds_pad(t) + T e + (T e >> 4)
 #pragma unroll
             for (int e = 0; e < E; ++e) v[s][e] = pr[T * e + ((T * e) >> 4)];
-            __syncthreads();
+            lds_sync<WAVE>();
         }
     }
     if constexpr (!LAST && !SHARED) {
-        __syncthreads();
+        lds_sync<WAVE>();
 #pragma unroll
         for (int s = 0; s < NV; ++s) {
             const float2* const pr = lds[s] + lds_pad(t);  // lds_pad(t + T e) = lds_pad(t) + T e + (T e >> 4)
 #pragma unroll
             for (int e = 0; e < E; ++e) v[s][e] = pr[T * e + ((T * e) >> 4)];
         }
-        __syncthreads();
+        lds_sync<WAVE>();
     }
 }
 
 // passes of radix 2^LRMAX, the remainder radix first
-template <int NV, int LOGN, int LOGE, int LRMAX, bool INV, bool SHARED, class TW, int P = 0, int LS = 0>
+template <int NV, int LOGN, int LOGE, int LRMAX, bool INV, bool SHARED, bool WAVE, class TW, int P = 0,
+          int LS = 0>
 __device__ __forceinline__ void fft_passes(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
                                            const TW& tw) {
     if constexpr (LOGN > 0) {
@@ -189,25 +204,29 @@ __device__ __forceinline__ void fft_passes(float2 (&v)[NV][1 << LOGE], float2* c
         constexpr int NP = LOGN / LRMAX + (REM ? 1 : 0);
         if constexpr (P < NP) {
             constexpr int LR = (P == 0 && REM) ? REM : LRMAX;
-            stockham_pass<NV, LOGN, LOGE, INV, P, LR, LS, P == NP - 1, SHARED>(v, lds, t, tw);
-            fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, TW, P + 1, LS + LR>(v, lds, t, tw);
+            stockham_pass<NV, LOGN, LOGE, INV, P, LR, LS, P == NP - 1, SHARED, WAVE>(v, lds, t, tw);
+            fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, WAVE, TW, P + 1, LS + LR>(v, lds, t, tw);
         }
     }
 }
 
 // Unscaled forward (INV=false) or inverse (INV=true) transforms of NV vectors of
 // N = 2^LOGN points, each held as v[s][e] = x_s[t + T e]; every thread of the
-// workgroup must call it (it contains workgroup barriers).  lds[s]:
+// workgroup must call it (it contains workgroup barriers), unless WAVE: then
+// the T = N/E threads are exactly one wavefront, only that wave calls it, and
+// the exchanges synchronise the wave alone.  lds[s]:
 // lds_padded_size(N) complex per vector; SHARED: all lds[s] are one buffer and
 // the vectors are exchanged in turn.  Requires LOGE <= LOGN (or LOGN == 0).
 // Butterflies are at most radix 16; a thread with E > 16 points runs E/16
 // butterflies per pass.
-template <int NV, int LOGN, int LOGE, bool INV, bool SHARED = false, int LRMAX = (LOGE < 4 ? LOGE : 4), class TW>
+template <int NV, int LOGN, int LOGE, bool INV, bool SHARED = false, int LRMAX = (LOGE < 4 ? LOGE : 4),
+          bool WAVE = false, class TW>
 __device__ __forceinline__ void fft_multi(float2 (&v)[NV][1 << LOGE], float2* const (&lds)[NV], int t,
                                           const TW& tw) {
+    static_assert(!WAVE || (LOGN - LOGE) == 6, "a wave-level transform takes exactly 64 threads");
     static_assert(LOGN == 0 || (LOGE >= 1 && LOGE <= LOGN), "bad FFT split");
     static_assert(LOGN == 0 || (LRMAX >= 1 && LRMAX <= LOGE && LRMAX <= 4), "bad radix");
-    fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, TW>(v, lds, t, tw);
+    fft_passes<NV, LOGN, LOGE, LRMAX, INV, SHARED, WAVE, TW>(v, lds, t, tw);
 }
 
 // single vector, sin/cos twiddles

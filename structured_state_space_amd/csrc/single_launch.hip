@@ -16,20 +16,19 @@
 // Phase A (all 1024 threads, one root each): as the root-value kernel with one
 // root per thread and narrow table rows (roots.hpp); the twiddles
 // exp(-i pi j/M) go to LDS; the root values to LDS.
-// Phase B (eight groups of 128 threads, 8 points per thread): z-half i = 2p + c
-// is row pair p's input z = u_{2p} + i u_{2p+1}, twisted by exp(-i pi j/M)
-// when c = 1 (the two halves of the zero-padded product, as in the convolution
-// kernel).  Three transform stages, in which every group runs the same code
-// (so every wave meets the same workgroup barriers) on data chosen by its
-// group index:
-//   B1: group 0 transforms the conjugated root values (inverse transform of
-//       the root values); group g > 0 transforms z-half g.
-//   B2: groups 0 and 1 transform the kernel's cyclic and twisted sequences
-//       (spectra); group 2 transforms z-half 0 for group 0; the others run the
-//       stage on zeros.
-//   B3: group g multiplies its z-half spectrum by the spectrum of its half and
-//       inverse-transforms; the twisted halves are untwisted and added to the
-//       cyclic ones through LDS; rows are stored.
+// Phase B: each transform is held by one 64-lane wave (16 points per lane,
+// radix-16 passes), so its LDS exchanges synchronise that wave alone; the
+// workgroup barrier is met only between stages, by every wave.  z-half
+// i = 2p + c is row pair p's input z = u_{2p} + i u_{2p+1}, twisted by
+// exp(-i pi j/M) when c = 1 (the two halves of the zero-padded product, as in
+// the convolution kernel).  Waves 1-8 own z-halves 0-7.
+//   B1: wave 0 transforms the conjugated root values (the inverse transform of
+//       the root values: the kernel); waves 1-8 their z-halves.
+//   B2: waves 9 and 10 transform the kernel's cyclic and twisted sequences
+//       (the spectra).
+//   B3: waves 1-8 multiply by the spectrum of their half and inverse-
+//       transform; the twisted halves are untwisted and added to the cyclic
+//       ones through LDS; rows are stored.
 #include <float.h>
 
 #include "common.hpp"
@@ -42,8 +41,10 @@ namespace {
 
 constexpr int kLogM1 = 10, kM1 = 1 << kLogM1;
 constexpr int kThreads1 = 1024;
-constexpr int kLogE1 = 3, kE1 = 1 << kLogE1, kT1 = kM1 >> kLogE1;  // 8 points, 128 threads per transform
-constexpr int kGroups1 = kThreads1 / kT1;                           // 8 = 4 row pairs x 2 halves
+constexpr int kLogE1 = 4, kE1 = 1 << kLogE1, kT1 = kM1 >> kLogE1;  // 16 points per lane, one wave per transform
+static_assert(kT1 == 64, "phase B transforms are one wave each");
+constexpr int kPairs1 = 4;                                          // row pairs per channel
+constexpr int kBufs1 = 2 * kPairs1 + 2;                             // exchange buffers (see the roles)
 constexpr int kLdsV1 = lds_padded_size(kM1);
 
 template <int RK>
@@ -59,20 +60,23 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     __shared__ float2 rootl[M];     // root values
     __shared__ float kl[M];         // real kernel taps (+D), scaled 1/(2M)
     __shared__ float2 khl[2][M];    // cyclic and twisted spectra
-    __shared__ float2 xfer[M];      // z-half 0 and its spectrum, handed between groups 0 and 2
-    __shared__ float2 fbuf[kGroups1][kLdsV1];
+    // exchange buffers: wave 0 and later wave 10 use 0, wave w in 1..9 uses w
+    __shared__ float2 fbuf[kBufs1][kLdsV1];
     __shared__ int blk_status;
     __shared__ double2 red[kThreads1 / 64];
 
     const int h = blockIdx.x;
     const int tid = threadIdx.x;
     const size_t hbase = (size_t)h * N;
-    // group index, uniform per wave: scalar branches only
-    const int g = __builtin_amdgcn_readfirstlane(tid / T);
-    const int t = tid - g * T;
-    const int pr = g >> 1, half = g & 1;
+    // wave index (uniform: roles are scalar branches) and lane; waves 1-8 own
+    // z-half zi = wave - 1 of row pair pr
+    const int wv = __builtin_amdgcn_readfirstlane(tid / T);
+    const int t = tid - wv * T;
+    const bool zwave = wv >= 1 && wv <= 2 * kPairs1;
+    const int zi = zwave ? wv - 1 : 0;
+    const int pr = zi >> 1, half = zi & 1;
     const int npb = (Bsz + 1) / 2;
-    const bool pact = pr < npb;
+    const bool pact = zwave && pr < npb;
     const int b1 = 2 * pr;
     const bool has2 = pact && b1 + 1 < Bsz;
     const size_t row1 = pact ? ((size_t)b1 * H + h) * (size_t)L : 0;
@@ -120,7 +124,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
         }
         __syncthreads();
         if (n0 == 0) {
-            // this group's input rows, fetched once the state inputs are in (a
+            // the z-half's input rows, fetched once the state inputs are in (a
             // wait for those would otherwise also wait for these) so that the
             // loads overlap the sweep
 #pragma unroll
@@ -159,31 +163,21 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     }
     rootl[k] = Hk;
     if (my_status) atomicMax(&blk_status, my_status);
-    if (g == 0) {  // group 0 owns z-half 0 but transforms the root values in B1: hand z to group 2
-#pragma unroll
-        for (int e = 0; e < E; ++e) xfer[t + T * e] = z[e];
-    }
     __syncthreads();
     const int chst = blk_status;
     if (tid == 0 && status) status[h] = chst;
 
     // ---- phase B ----
     const TwiddleRegs<kLogM1, kLogE1> tw(twl, kLogM1, t);
-    float2* const mine[1] = {fbuf[g]};
+    float2* const mine[1] = {fbuf[wv == 10 ? 0 : min(wv, kBufs1 - 1)]};
     float2 x[1][E];
+    const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
 
     // B1
+    if (wv == 0) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = t + T * e;
-        x[0][e] = g == 0 ? c_conj(rootl[j]) : (half ? c_mul(z[e], twl[j]) : z[e]);
-    }
-    fft_multi<1, kLogM1, kLogE1, false>(x, mine, t, tw);
-    float2 zs[E];  // this group's z-half spectrum (groups > 0)
-#pragma unroll
-    for (int e = 0; e < E; ++e) zs[e] = make_float2(0.0f, 0.0f);
-    const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
-    if (g == 0) {
+        for (int e = 0; e < E; ++e) x[0][e] = c_conj(rootl[t + T * e]);
+        fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(x, mine, t, tw);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
@@ -193,54 +187,48 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
             if (j == 0 && D) kr += D[h];
             kl[j] = kr * sc;
         }
-    } else {
+    } else if (zwave) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) zs[e] = x[0][e];
+        for (int e = 0; e < E; ++e) x[0][e] = half ? c_mul(z[e], twl[t + T * e]) : z[e];
+        fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(x, mine, t, tw);
     }
     __syncthreads();
 
     // B2
+    if (wv == 9 || wv == 10) {
+        const int c = wv - 9;
+        float2 w[1][E];
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = t + T * e;
-        x[0][e] = g == 0   ? make_float2(kl[j], 0.0f)
-                  : g == 1 ? c_scale(twl[j], kl[j])
-                  : g == 2 ? xfer[j]
-                           : make_float2(0.0f, 0.0f);
-    }
-    fft_multi<1, kLogM1, kLogE1, false>(x, mine, t, tw);
-    if (g <= 1) {
+        for (int e = 0; e < E; ++e) {
+            const int j = t + T * e;
+            w[0][e] = c ? c_scale(twl[j], kl[j]) : make_float2(kl[j], 0.0f);
+        }
+        fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(w, mine, t, tw);
 #pragma unroll
-        for (int e = 0; e < E; ++e) khl[g][t + T * e] = x[0][e];
-    } else if (g == 2) {  // its own reads of xfer all came before the transform's barriers
-#pragma unroll
-        for (int e = 0; e < E; ++e) xfer[t + T * e] = x[0][e];
+        for (int e = 0; e < E; ++e) khl[c][t + T * e] = w[0][e];
     }
     __syncthreads();
 
     // B3
+    if (zwave) {
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-        const int j = t + T * e;
-        const float2 s = g == 0 ? xfer[j] : zs[e];
-        x[0][e] = c_mul(s, khl[half][j]);
-    }
-    fft_multi<1, kLogM1, kLogE1, true>(x, mine, t, tw);
-    // the transform's last exchange ended at a barrier: fbuf is free again
-    if (half) {
+        for (int e = 0; e < E; ++e) x[0][e] = c_mul(x[0][e], khl[half][t + T * e]);
+        fft_multi<1, kLogM1, kLogE1, true, false, 4, true>(x, mine, t, tw);
+        if (half) {  // the transform's last exchange is behind it: the buffer is free
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = t + T * e;
-            fbuf[g][j] = c_mul(x[0][e], c_conj(twl[j]));
+            for (int e = 0; e < E; ++e) {
+                const int j = t + T * e;
+                fbuf[wv][j] = c_mul(x[0][e], c_conj(twl[j]));
+            }
         }
     }
     __syncthreads();
-    if (!half && pact) {
+    if (zwave && !half && pact) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int j = t + T * e;
             if (j < L) {
-                float2 o = c_add(x[0][e], fbuf[g + 1][j]);
+                float2 o = c_add(x[0][e], fbuf[wv + 1][j]);
                 if (chst) o = c_nan();
                 y[row1 + j] = o.x;
                 if (has2) y[row2 + j] = o.y;
@@ -252,7 +240,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
 }  // namespace
 
 bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M) {
-    return M == kM1 && (Bsz + 1) / 2 <= kGroups1 / 2 && H >= 256;
+    return M == kM1 && (Bsz + 1) / 2 <= kPairs1 && H >= 256;
 }
 
 hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
