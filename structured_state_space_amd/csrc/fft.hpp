@@ -144,6 +144,10 @@ __device__ __forceinline__ void stockham_pass(float2 (&v)[NV][1 << LOGE], float2
         for (int i = 0; i < NB; ++i) {
             float2 w = tw.template get<P, NS * R>(i, (t + i * T) & (NS - 1));
             if (INV) w.y = -w.y;
+            // the powers of w are formed here, per pass and call: an empty asm
+            // keeps the compiler from hoisting or sharing them across passes and
+            // transforms, where their registers would stay live (and spill)
+            asm volatile("" : "+v"(w.x), "+v"(w.y));
             float2 wq = w;
 #pragma unroll
             for (int q = 1; q < R; ++q) {

@@ -47,6 +47,9 @@ struct Geo {
     static constexpr int SPEC_NBUF = LOGM <= 12 ? 2 : 1;
     static constexpr int WAVES = LOGM >= 14 ? 4 : 2;  // register budget: 128 / 256 VGPRs
     static constexpr bool PREFETCH = LOGM <= 13;
+    // M = 16384 (1024 threads, 128 registers): the cyclic and twisted halves
+    // one after the other, one vector in registers
+    static constexpr bool SEQ = LOGM >= 14;
     static constexpr int LRMAX = LOGE < 4 ? LOGE : 4;  // largest butterfly radix (log2)
 };
 
@@ -212,7 +215,33 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
 
     float2 out[E];
     int chst = 0;
-    {
+    if constexpr (Gm::SEQ && !FUSED) {
+        float2* const one[1] = {my};
+#pragma unroll 1
+        for (int half = 0; half < 2; ++half) {
+            // the thread index passes through an empty asm in each half, so the
+            // inputs, spectra and twist factors are read where they are used
+            // rather than hoisted out of the loop (their registers would spill)
+            int tl = t;
+            asm volatile("" : "+v"(tl));
+            float2 v[1][E];
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                const int j = tl + T * e;
+                const bool in = active && j < L;
+                const float2 z = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+                v[0][e] = half ? c_mul(z, twtab[j]) : z;
+            }
+            fft_multi<1, LOGM, LOGE, false, false, Gm::LRMAX>(v, one, t, tw);
+            const float2* kh = half ? kh1 : kh0;
+#pragma unroll
+            for (int e = 0; e < E; ++e) v[0][e] = c_mul(v[0][e], kh[tl + T * e]);
+            fft_multi<1, LOGM, LOGE, true, false, Gm::LRMAX>(v, one, t, tw);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                out[e] = half ? c_add(out[e], c_mul(v[0][e], c_conj(twtab[tl + T * e]))) : v[0][e];
+        }
+    } else {
         // spectra and twist factors are fetched up front (and held) unless registers are short
         constexpr bool PRE = Gm::PREFETCH || FUSED;
         float2 v[2][E], tws[PRE ? E : 1], k0[PRE ? E : 1], k1[PRE ? E : 1];

@@ -299,7 +299,8 @@ def test_single_launch_form(r, L, Bsz):
 @pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
     (1, 1, 1, 1, 1, "random"), (2, 3, 1, 2, 3, "random"), (3, 5, 2, 3, 1, "random"),
     (5, 100, 1, 100, 3, "s4"), (4, 17, 3, 257, 2, "random"), (3, 9, 4, 64, 2, "random"),
-    (9, 64, 2, 1000, 5, "s4"), (2, 130, 1, 4097, 2, "random"), (2, 16, 1, 20000, 3, "random"),
+    (9, 64, 2, 1000, 5, "s4"), (2, 130, 1, 4097, 2, "random"), (2, 24, 1, 9000, 3, "random"),
+    (2, 16, 1, 20000, 3, "random"),
 ])
 def test_edge_cases_end_to_end(H, N, r, L, Bsz, kind):
     ssm = _ssm()
