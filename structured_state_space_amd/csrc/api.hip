@@ -93,8 +93,10 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
     if (M > ((int64_t)1 << kMaxLdsLogM)) {  // multi-pass transforms
         w.big = off;
         if (op == SSM_OP_KERNEL_GEN) w.big_bytes = (size_t)H * M * sizeof(float2);  // first-pass output
-        if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD)
-            w.big_bytes = (size_t)((Bsz + 1) / 2) * H * 2 * M * sizeof(float2);  // conv intermediate
+        if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {  // conv intermediate: one chunk of row pairs
+            const int64_t npairs = ((Bsz + 1) / 2) * H;
+            w.big_bytes = (size_t)(npairs < kConvChunkPairs ? npairs : kConvChunkPairs) * 2 * M * sizeof(float2);
+        }
         off = align256(off + w.big_bytes);
     }
     w.total = off;

@@ -73,6 +73,9 @@ struct WsLayout {
 };
 
 constexpr int kMaxLdsLogM = 14;           // M <= 16384 runs LDS-resident
+// multi-pass convolution: row pairs per chunk (the intermediate of a chunk,
+// 2 M complex per pair, is the workspace's multi-pass region)
+constexpr int kConvChunkPairs = 64;
 constexpr int kMaxLogM = 16;              // M <= 65536 supported
 constexpr int kCauchyThreads = 256;
 

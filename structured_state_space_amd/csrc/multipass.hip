@@ -207,13 +207,15 @@ __global__ __launch_bounds__(kThreads) void sp3_kernel(float2* __restrict__ khat
 // C1: column transforms (length C) of a row pair and its twisted copy.
 // grid: npairs * (R / CB) blocks, CB = 256 / (C/16) columns per block.
 template <int LOGC>
-__global__ __launch_bounds__(kThreads) void c1_kernel(int Bsz, int H, int L, int npb, const float* __restrict__ u,
-                                                      float2* __restrict__ Z, const float2* __restrict__ twtab) {
+__global__ __launch_bounds__(kThreads) void c1_kernel(int Bsz, int H, int L, int npb, int p0,
+                                                      const float* __restrict__ u, float2* __restrict__ Z,
+                                                      const float2* __restrict__ twtab) {
     constexpr int C = 1 << LOGC, M = kR * C, LOGM = kLogR + LOGC, TC = C / kE, CB = kThreads / TC;
     constexpr int PAD = lds_padded_size(C);
     __shared__ float2 lds[2 * CB * PAD];
     const int nb = kR / CB;
-    const int p = blockIdx.x / nb, c0 = (blockIdx.x % nb) * CB;
+    const int pl = blockIdx.x / nb, c0 = (blockIdx.x % nb) * CB;  // pair pl of the chunk from p0
+    const int p = p0 + pl;
     const int g = threadIdx.x % CB, t = threadIdx.x / CB;
     const int cp = c0 + g;  // column c'
     const int h = p / npb, b1 = 2 * (p % npb);
@@ -231,7 +233,7 @@ __global__ __launch_bounds__(kThreads) void c1_kernel(int Bsz, int H, int L, int
     }
     float2* const b[2] = {lds + g * PAD, lds + (CB + g) * PAD};
     fft_multi<2, LOGC, kLogE, false>(v, b, t, tw);
-    float2* Z0 = Z + (size_t)p * 2 * M;
+    float2* Z0 = Z + (size_t)pl * 2 * M;
     float2* Z1 = Z0 + M;
 #pragma unroll
     for (int e = 0; e < kE; ++e) {
@@ -245,16 +247,17 @@ __global__ __launch_bounds__(kThreads) void c1_kernel(int Bsz, int H, int L, int
 // C2: row transform, times the spectrum, inverse row transform, conj twiddle.
 // grid: npairs * (C / 16) blocks; both halves of 16 rows per block.
 template <int LOGC>
-__global__ __launch_bounds__(kThreads) void c2_kernel(int npb, float2* __restrict__ Z, const float2* __restrict__ khat,
+__global__ __launch_bounds__(kThreads) void c2_kernel(int npb, int p0, float2* __restrict__ Z,
+                                                      const float2* __restrict__ khat,
                                                       const float2* __restrict__ twtab) {
     constexpr int C = 1 << LOGC, M = kR * C, LOGM = kLogR + LOGC, RB = 16;
     __shared__ float2 lds[2 * RB * kPad];
     const int nb = C / RB;
-    const int p = blockIdx.x / nb, row0 = (blockIdx.x % nb) * RB;
+    const int pl = blockIdx.x / nb, row0 = (blockIdx.x % nb) * RB;  // pair pl of the chunk from p0
     const int g = threadIdx.x / 16, t = threadIdx.x % 16;
     const int krp = row0 + g;
-    const int h = p / npb;
-    float2* Z0 = Z + (size_t)p * 2 * M + (size_t)krp * kR;
+    const int h = (p0 + pl) / npb;
+    float2* Z0 = Z + (size_t)pl * 2 * M + (size_t)krp * kR;
     float2* Z1 = Z0 + M;
     const float2* K0 = khat + (size_t)h * 2 * M + (size_t)krp * kR;
     const float2* K1 = K0 + M;
@@ -284,18 +287,19 @@ __global__ __launch_bounds__(kThreads) void c2_kernel(int npb, float2* __restric
 
 // C3: inverse column transforms, untwist, add the halves, store both rows.
 template <int LOGC>
-__global__ __launch_bounds__(kThreads) void c3_kernel(int Bsz, int H, int L, int npb, float* __restrict__ y,
+__global__ __launch_bounds__(kThreads) void c3_kernel(int Bsz, int H, int L, int npb, int p0, float* __restrict__ y,
                                                       const float2* __restrict__ Z, const float2* __restrict__ twtab) {
     constexpr int C = 1 << LOGC, M = kR * C, LOGM = kLogR + LOGC, TC = C / kE, CB = kThreads / TC;
     constexpr int PAD = lds_padded_size(C);
     __shared__ float2 lds[2 * CB * PAD];
     const int nb = kR / CB;
-    const int p = blockIdx.x / nb, c0 = (blockIdx.x % nb) * CB;
+    const int pl = blockIdx.x / nb, c0 = (blockIdx.x % nb) * CB;  // pair pl of the chunk from p0
+    const int p = p0 + pl;
     const int g = threadIdx.x % CB, t = threadIdx.x / CB;
     const int cp = c0 + g;
     const int h = p / npb, b1 = 2 * (p % npb);
     const bool has2 = b1 + 1 < Bsz;
-    const float2* Z0 = Z + (size_t)p * 2 * M;
+    const float2* Z0 = Z + (size_t)pl * 2 * M;
     const float2* Z1 = Z0 + M;
     const TwiddleRegs<LOGC, kLogE> tw(twtab, LOGM, t);
     float2 v[2][kE];
@@ -354,15 +358,21 @@ hipError_t conv_large_t(int64_t Bsz, int64_t H, int64_t L, const float* u, float
                         const float2* twtab, hipStream_t s) {
     constexpr int C = 1 << LOGC, TC = C / kE, CB = kThreads / TC;
     const int64_t npb = (Bsz + 1) / 2, npairs = npb * H;
-    hipLaunchKernelGGL(c1_kernel<LOGC>, dim3((unsigned)(npairs * (kR / CB))), dim3(kThreads), 0, s, (int)Bsz, (int)H,
-                       (int)L, (int)npb, u, Z, twtab);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(c2_kernel<LOGC>, dim3((unsigned)(npairs * (C / 16))), dim3(kThreads), 0, s, (int)npb, Z, khat,
-                       twtab);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(c3_kernel<LOGC>, dim3((unsigned)(npairs * (kR / CB))), dim3(kThreads), 0, s, (int)Bsz, (int)H,
-                       (int)L, (int)npb, y, Z, twtab);
-    return hipGetLastError();
+    // chunks of row pairs, each through the three passes before the next, so
+    // the intermediate of one chunk stays in the caches
+    for (int64_t p0 = 0; p0 < npairs; p0 += kConvChunkPairs) {
+        const int64_t np = npairs - p0 < kConvChunkPairs ? npairs - p0 : kConvChunkPairs;
+        hipLaunchKernelGGL(c1_kernel<LOGC>, dim3((unsigned)(np * (kR / CB))), dim3(kThreads), 0, s, (int)Bsz,
+                           (int)H, (int)L, (int)npb, (int)p0, u, Z, twtab);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(c2_kernel<LOGC>, dim3((unsigned)(np * (C / 16))), dim3(kThreads), 0, s, (int)npb,
+                           (int)p0, Z, khat, twtab);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+        hipLaunchKernelGGL(c3_kernel<LOGC>, dim3((unsigned)(np * (kR / CB))), dim3(kThreads), 0, s, (int)Bsz,
+                           (int)H, (int)L, (int)npb, (int)p0, y, Z, twtab);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
