@@ -254,12 +254,14 @@ def test_invalid_step_status():
 # separate root-value / transform / convolution kernels and the oracle,
 # including a channel with an invalid step and one with an exact pole
 # ---------------------------------------------------------------------------
-@pytest.mark.parametrize("r,L,Bsz", [(1, 1024, 8), (2, 600, 3), (1, 777, 1), (3, 1000, 6)])
-def test_single_launch_form(r, L, Bsz):
+@pytest.mark.parametrize("r,L,Bsz,N", [(1, 1024, 8, 48), (2, 600, 3, 48), (1, 777, 1, 48), (3, 1000, 6, 48),
+                                        (1, 900, 2, 300), (2, 1024, 4, 200)])
+def test_single_launch_form(r, L, Bsz, N):
+    # N = 300 (r = 1) and 200 (r = 2) take more than one staged chunk of states
     ssm = _ssm()
-    H, N = 256, 48
+    H = 256
     assert ssm.forward_form(Bsz, H, L) == 1
-    p = I.random_params(7000 + 10 * r + Bsz, H, N, r, L)
+    p = I.random_params(7000 + 10 * r + Bsz + N, H, N, r, L)
     p.dt[5] = 0.0                       # invalid step
     p.dt[7] = 0.5                       # a = 2/dt = 4 exactly; tan(pi/4) = 1 exactly
     p.Lambda[7, 0] = 4.0j               # so s(z_{M/4}) = lambda_0: an exact pole
