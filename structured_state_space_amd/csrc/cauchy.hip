@@ -205,10 +205,11 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, cons
 
 }  // namespace
 
-// roots per thread: the most this rank allows (more sums share each LDS row)
-// while the grid keeps at least 1024 workgroups (four waves per SIMD)
+// roots per thread: up to 4 for r <= 2 (more sums share each LDS row; 8 roots
+// for r = 1 was measured slower: 140 registers leave 3 workgroups per CU and a
+// partial last round), while the grid keeps at least 1024 workgroups
 int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
-    const int max_rpt = r == 1 ? 8 : r == 2 ? 4 : 1;
+    const int max_rpt = r <= 2 ? 4 : 1;
     int rpt = max_rpt;
     while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
         rpt >>= 1;
@@ -227,7 +228,7 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
     if (r == RK && rpt == RPT)                                                                                \
         return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, stream);
-    SSM_CAUCHY(1, 8) SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 4) SSM_CAUCHY(2, 2)
+    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 4) SSM_CAUCHY(2, 2)
     SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY
