@@ -30,7 +30,7 @@ sys.path.insert(0, ROOT)
 METRIC = "channel-steps/sec (B·H·L) for S4 kernel-gen+FFT conv; % HBM/VALU roofline"
 UNIT = "channel-steps/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
-PEAK_FP32_TFLOPS = 157.3       # MI355X FP32 vector (packed issue)
+PEAK_FP32_TFLOPS = 157.3       # MI355X FP32: dense matrix (MFMA) and vector peaks are both 157.3
 DEFAULT_WORKLOAD = "s4-h256-l1k"
 
 KERNEL_SOURCES = {
@@ -56,7 +56,7 @@ def algorithmic(w, M, fused):
     H, N, r, L, B = w.H, w.N, w.r, w.L, w.Bsz
     roots = M - 1 if M >= 2 else M                      # z = -1 takes its finite formula
     out = {
-        "cauchy": dict(bound="alu", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
+        "cauchy": dict(bound="mfma", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
                        peak=PEAK_FP32_TFLOPS),
         "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * 2 * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
         "conv": dict(bound="hbm", unit="GB/s", work=8 * B * H * L + 4 * H * L + 4 * H, scale=1e-9,
@@ -110,8 +110,8 @@ def cpu_baseline(w, p, u, seconds):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--stage-repeat", type=int, default=10,
@@ -192,15 +192,16 @@ def main():
     stages = ("cauchy", "spectrum", "conv")
     acc = {k: 0.0 for k in stages}
     reps = max(1, args.stage_repeat)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    for i in range(args.steps):
+    nprof = min(args.steps, 20)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nprof)]
+    for i in range(nprof):
         ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut, y=y, status=status,
                     workspace=ws, events=evs[i], repeat=reps)
     torch.cuda.synchronize()
-    for i in range(args.steps):
+    for i in range(nprof):
         for j, k in enumerate(stages):
             acc[k] += evs[i][j].elapsed_time(evs[i][j + 1]) / reps
-    phase_ms = {k: acc[k] / args.steps for k in stages}
+    phase_ms = {k: acc[k] / nprof for k in stages}
     # form 2: stage 2 launches nothing and the convolution kernel includes it;
     # form 1: one kernel does everything (timed as stage 1)
     names = ("filter",) if form == 1 else ("cauchy", "conv") if fused else stages
@@ -212,8 +213,9 @@ def main():
 
     alg = algorithmic(w, M, fused)
     if form == 1:
-        # the single launch is VALU-bound: rated on the root values' flops plus
-        # the convolution's transform flops, Bsz*H*(5 n log2 n + 6 (n/2 + 1)), n = n_fft
+        # the single launch is compute-bound (root-value sums on the matrix cores,
+        # transforms on the vector ALU): rated on the root values' flops plus the
+        # convolution's transform flops, Bsz*H*(5 n log2 n + 6 (n/2 + 1)), n = n_fft
         conv_flops = w.Bsz * w.H * (5 * n_fft * int(math.log2(n_fft)) + 6 * (n_fft // 2 + 1))
         alg["filter"] = dict(alg["cauchy"], work=alg["cauchy"]["work"] + conv_flops)
     phases = {}

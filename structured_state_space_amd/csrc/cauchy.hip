@@ -1,4 +1,4 @@
-// Root values H(z_k) of the S4 filter mode on VALU.
+// Root values H(z_k) of the S4 filter mode (vector ALU + matrix cores).
 //
 // Source: "Recurrent, LSTM, and structured state-space models", block for S4
 // Algorithm 1 / App. C (filter mode).  For z = z_k = exp(-2 pi i k/M), k != M/2,
@@ -14,17 +14,12 @@
 // exactly -Re(lambda_n), which float32 needs when a = 2/dt is large.
 //
 // Work split: one workgroup per (channel, tile of 256*RPT roots).  Per chunk of
-// states the workgroup stages lambda and the weights w = conj(u_n) v_n in LDS;
-// every thread then sweeps the chunk for its RPT roots: one reciprocal and
-// (r+1)^2 complex multiply-adds per (root, state).  With d = x + i y
-// (x = -Re lambda, y = a t_k - Im lambda), 1/d = (x - i y)/|d|^2 and
-//   w/d = (w x) inv + (-i w) (y inv),  inv = 1/|d|^2.
-// Every lane reads the same table row, so the sweep moves 64 copies of each row
-// from LDS per wave: with several roots per thread the row is amortised and the
-// table keeps (w x) and w (wide rows: no per-family products beyond the four
-// multiply-adds); with one or two roots per thread the table keeps w alone
-// (narrow rows, 8 instead of 16 bytes per family, which cuts the LDS read
-// rate) and the loop forms x inv once per (root, state).
+// states the workgroup stages a header (x^2, Im lambda) and the weight block of
+// each state in LDS (roots.hpp); every thread then sweeps the chunk for its RPT
+// roots: per (root, state) one reciprocal and a multiply on the vector ALU
+// (with d = x + i y, x = -Re lambda, y = a t_k - Im lambda: inv = 1/|d|^2 and
+// y inv), and the products with the weights on the matrix cores, four real
+// columns per 4x4x1 instruction.
 // Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
 // with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
 // flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
@@ -51,14 +46,14 @@ __global__ __launch_bounds__(256) void root_tables_kernel(int M, double* __restr
 }
 
 template <int RK, int RPT>
-__global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
+// rank 1: registers capped for four waves per SIMD (fits without spills;
+// measured faster than three waves with more registers)
+__global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(RK == 1 ? 4 : 1))) void cauchy_roots_kernel(
     int M, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
     const double* __restrict__ tant, float2* __restrict__ twtab) {
-    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK;
-    constexpr bool NARROW = RPT <= 2;
-    constexpr int RW = NARROW ? Fam<RK>::ROWN : Fam<RK>::ROW;
+    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK, U = sweep_unroll<RK, RPT>();
     // tan(pi k/M) from the per-call table when each thread has several roots;
     // otherwise computed here, and this grid also writes the twiddle table
     constexpr bool TAB = RPT >= 4;
@@ -68,7 +63,8 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
             sincospi((double)j / (double)M, &sn, &cs);
             twtab[j] = make_float2((float)cs, (float)-sn);
         }
-    __shared__ float4 tbl[kChunk * RW];
+    __shared__ float2 hdr[kChunk];
+    __shared__ float4 wt[kChunk * Fam<RK>::WROW];
     __shared__ int blk_status;
     __shared__ double2 red[kCauchyThreads / 64];
 
@@ -113,11 +109,9 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
         }
     }
 
-    float2 acc[RPT][F];
+    RootAcc<RK> acc[RPT];
 #pragma unroll
-    for (int i = 0; i < RPT; ++i)
-#pragma unroll
-        for (int f = 0; f < F; ++f) acc[i][f] = make_float2(0.f, 0.f);
+    for (int i = 0; i < RPT; ++i) acc_zero<RK>(acc[i]);
 
     double m1x = 0.0, m1y = 0.0;
     // Small grids (one or two roots per thread) are a single round of
@@ -130,12 +124,15 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     if constexpr (FAIR) __builtin_amdgcn_s_setprio(3);
     for (int n0 = 0; n0 < N; n0 += kChunk) {
         const int nch = min(kChunk, N - n0);
+        const int npad = (nch + U - 1) / U * U;
         __syncthreads();
-        for (int nn = tid; nn < nch; nn += kCauchyThreads) {
+        for (int nn = tid; nn < npad; nn += kCauchyThreads) {
+            if (nn >= nch) {
+                stage_pad<RK>(hdr + nn, wt + nn * Fam<RK>::WROW);
+                continue;
+            }
             const size_t hn = hbase + n0 + nn;
             const float2 lam = Lambda[hn];
-            const float x = -lam.x;
-            tbl[nn * RW] = make_float4(x * x, lam.y, x, 0.f);
             float2 uu[RK + 1], vv[RK + 1];
             uu[0] = Ct[hn];
             vv[0] = Bv[hn];
@@ -147,10 +144,10 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
                 uu[1 + j] = Q[hn * RK + j];
                 vv[1 + j] = P[hn * RK + j];
             }
-            stage_row<RK, NARROW>(tbl + nn * RW, lam, uu, vv);
+            stage_state<RK>(hdr + nn, wt + nn * Fam<RK>::WROW, lam, uu, vv);
         }
         __syncthreads();
-        sweep_chunk<RK, RPT, NARROW, FAIR>(tbl, nch, n0, q1, q2, q3, st, acc);
+        sweep_chunk<RK, RPT, U, FAIR>(hdr, wt, npad, n0, q1, q2, q3, st, acc);
     }
 
     if constexpr (FAIR) __builtin_amdgcn_s_setprio(0);
@@ -176,10 +173,12 @@ __global__ __launch_bounds__(kCauchyThreads) void cauchy_roots_kernel(
     int my_status = 0;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
+        float2 sums[F];
+        acc_unpack<RK>(acc[i], sums);  // every lane, before the range test
         const int k = kk[i];
         if (k >= M) continue;
         const float2 H = 2 * k == M ? make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y))
-                                    : finish_root<RK>(acc[i], st[i], tf[i], N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                                    : finish_root<RK>(sums, st[i], tf[i], N, hbase, Lambda, P, Q, Bv, Ct, my_status);
         roots[(size_t)h * M + k] = H;
     }
     if (my_status) atomicMax(&blk_status, my_status);
@@ -205,11 +204,11 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, cons
 
 }  // namespace
 
-// roots per thread: up to 4 for r <= 2 (more sums share each LDS row; 8 roots
-// for r = 1 was measured slower: 140 registers leave 3 workgroups per CU and a
-// partial last round), while the grid keeps at least 1024 workgroups
+// roots per thread: up to 4 for r = 1 and 2 for r = 2 (more sums share each
+// staged weight row; these were measured fastest, the accumulators of more
+// roots crowd out waves), while the grid keeps at least 1024 workgroups
 int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
-    const int max_rpt = r <= 2 ? 4 : 1;
+    const int max_rpt = r == 1 ? 4 : r == 2 ? 2 : 1;
     int rpt = max_rpt;
     while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
         rpt >>= 1;
@@ -228,8 +227,7 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
     if (r == RK && rpt == RPT)                                                                                \
         return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, stream);
-    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 4) SSM_CAUCHY(2, 2)
-    SSM_CAUCHY(2, 1)
+    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY
     return hipErrorInvalidValue;

@@ -11,10 +11,10 @@
 // Used where every channel's rows fit one workgroup (at most four row pairs)
 // and there are enough channels to give every CU a workgroup.  Against the
 // two-launch form it keeps the root values in LDS, loads the input rows while
-// the root values are being computed, and has no second launch.
+// the root values are being finished, and has no second launch.
 //
 // Phase A (all 1024 threads, one root each): as the root-value kernel with one
-// root per thread and narrow table rows (roots.hpp); the twiddles
+// root per thread (roots.hpp: sums on the matrix cores); the twiddles
 // exp(-i pi j/M) go to LDS; the root values to LDS.
 // Phase B: each transform is held by one 64-lane wave (16 points per lane,
 // radix-16 passes), so its LDS exchanges synchronise that wave alone; the
@@ -54,8 +54,9 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ u, float* __restrict__ y,
     float2* __restrict__ K_out, int32_t* __restrict__ status) {
     constexpr int M = kM1, E = kE1, T = kT1;
-    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK, RW = Fam<RK>::ROWN;
-    __shared__ float4 tbl[kChunk * RW];
+    constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK, U = sweep_unroll<RK, 1>();
+    __shared__ float2 hdr[kChunk];
+    __shared__ float4 wt[kChunk * Fam<RK>::WROW];
     __shared__ float2 twl[M];       // exp(-i pi j/M)
     __shared__ float2 rootl[M];     // root values
     __shared__ float kl[M];         // real kernel taps (+D), scaled 1/(2M)
@@ -95,9 +96,8 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     const double tk = (2 * k == M) ? 0.0 : sn / cs;
     const double a = bad_dt ? 0.0 : 2.0 / (double)dtv;
     const float st[1] = {(float)(a * tk)};
-    float2 acc[1][F];
-#pragma unroll
-    for (int f = 0; f < F; ++f) acc[0][f] = make_float2(0.f, 0.f);
+    RootAcc<RK> acc[1];
+    acc_zero<RK>(acc[0]);
     // issue priority falls with progress through the states so that the
     // block's waves advance together (the phase ends at a barrier)
     const int q1 = N / 4, q2 = N / 2, q3 = (3 * N) / 4;
@@ -105,7 +105,9 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     double m1x = 0.0, m1y = 0.0;
     for (int n0 = 0; n0 < N; n0 += kChunk) {
         const int nch = min(kChunk, N - n0);
+        const int npad = (nch + U - 1) / U * U;
         __syncthreads();
+        if (tid >= nch && tid < npad) stage_pad<RK>(hdr + tid, wt + tid * Fam<RK>::WROW);
         if (tid < nch) {
             const size_t hn = hbase + n0 + tid;
             const float2 lam = Lambda[hn];
@@ -120,23 +122,21 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
                 uu[1 + j] = Q[hn * RK + j];
                 vv[1 + j] = P[hn * RK + j];
             }
-            stage_row<RK, true>(tbl + tid * RW, lam, uu, vv);
+            stage_state<RK>(hdr + tid, wt + tid * Fam<RK>::WROW, lam, uu, vv);
         }
         __syncthreads();
-        if (n0 == 0) {
-            // the z-half's input rows, fetched once the state inputs are in (a
-            // wait for those would otherwise also wait for these) so that the
-            // loads overlap the sweep
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int j = t + T * e;
-                const bool in = pact && j < L;
-                z[e] = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
-            }
-        }
-        sweep_chunk<RK, 1, true, true>(tbl, nch, n0, q1, q2, q3, st, acc);
+        sweep_chunk<RK, 1, U, true>(hdr, wt, npad, n0, q1, q2, q3, st, acc);
     }
     __builtin_amdgcn_s_setprio(0);
+    // the z-half's input rows, fetched after the sweep (loads in flight during
+    // it were measured to slow it by more than their latency costs here, where
+    // the barrier wait and the root finish hide it)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+        const int j = t + T * e;
+        const bool in = pact && j < L;
+        z[e] = make_float2(in ? u[row1 + j] : 0.0f, (in && has2) ? u[row2 + j] : 0.0f);
+    }
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
         m1x += __shfl_xor(m1x, o, 64);
@@ -145,6 +145,8 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     if ((tid & 63) == 0) red[tid >> 6] = make_double2(m1x, m1y);
     __syncthreads();
     int my_status = 0;
+    float2 sums[F];
+    acc_unpack<RK>(acc[0], sums);
     float2 Hk;
     if (2 * k == M) {  // z = -1: (dt/2) C~^* B
         double2 m1 = make_double2(0.0, 0.0);
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
         }
         Hk = make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y));
     } else {
-        Hk = finish_root<RK>(acc[0], st[0], (float)tk, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+        Hk = finish_root<RK>(sums, st[0], (float)tk, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
     }
     if (bad_dt) {
         my_status = SSM_ST_INVALID_STEP;
