@@ -232,8 +232,10 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
             if (j < L) {
                 float2 o = c_add(x[0][e], fbuf[wv + 1][j]);
                 if (chst) o = c_nan();
-                y[row1 + j] = o.x;
-                if (has2) y[row2 + j] = o.y;
+                // streaming stores: the rows are not read again here, and
+                // fewer dirty lines are left for the end-of-kernel write-back
+                __builtin_nontemporal_store(o.x, &y[row1 + j]);
+                if (has2) __builtin_nontemporal_store(o.y, &y[row2 + j]);
             }
         }
     }

@@ -321,8 +321,9 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
             const int j = t + T * e;
             if (j < L) {
                 if (FUSED && chst) out[e] = c_nan();
-                y[row1 + j] = out[e].x;
-                if (has2) y[row2 + j] = out[e].y;
+                // streaming stores (not read again; less end-of-kernel write-back)
+                __builtin_nontemporal_store(out[e].x, &y[row1 + j]);
+                if (has2) __builtin_nontemporal_store(out[e].y, &y[row2 + j]);
             }
         }
     }
