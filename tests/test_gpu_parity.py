@@ -99,6 +99,38 @@ def test_root_values_multipass_lengths(L):
     assert_rows_close(K, np.array([r["K"][:L] for r in refs]), what="kernel")
 
 
+@pytest.mark.parametrize("H,N,r,L,nsample", [
+    (256, 301, 1, 4096, 4),   # 4 roots per thread; 256 + 45 states, the last chunk padded to the unroll
+    (256, 203, 2, 4096, 4),   # rank 2, 2 roots per thread; 128 + 75 states (padded)
+    (8, 301, 1, 3000, 2),     # small grid: 1 root per thread, unroll 8; 256 + 45 states (padded)
+    (4, 71, 3, 2048, 2),      # rank 3: 64 + 7 states (padded)
+    (4, 66, 4, 1500, 2),      # rank 4: 64 + 2 states
+])
+def test_root_values_chunks_and_roots_per_thread(H, N, r, L, nsample):
+    """Root values from a supplied C~ (random here: the kernel generator takes it
+    as given) against the oracle's resolvent expression on sampled channels, at
+    shapes whose state vectors span several staged chunks."""
+    ssm = _ssm()
+    p = I.random_params(H + N + r + L, H, N, r, L, lambda_kind="random")
+    d = _dev(p)
+    out = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_kernel=True,
+                         want_roots=True)
+    assert np.all(_np(out["status"]) == 0)
+    roots, K = _np(out["roots"]), _np(out["K"])
+    M = O.transform_length(L)
+    chans = sample_channels(H, nsample, seed=N + r)
+    ref = []
+    for h in chans:
+        c = p.channel(int(h))
+        Hk, st = O.root_values(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], M)
+        assert st == O.OK
+        ref.append(Hk)
+    ref = np.array(ref)
+    assert_rows_close(roots[chans], ref, what="root values")
+    # the kernel: first L taps of the inverse transform of the oracle's root values
+    assert_rows_close(K[chans], np.fft.ifft(ref, axis=1)[:, :L], what="kernel")
+
+
 # ---------------------------------------------------------------------------
 # discretisation
 # ---------------------------------------------------------------------------
@@ -255,7 +287,7 @@ def test_invalid_step_status():
 # including a channel with an invalid step and one with an exact pole
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("r,L,Bsz,N", [(1, 1024, 8, 48), (2, 600, 3, 48), (1, 777, 1, 48), (3, 1000, 6, 48),
-                                        (1, 900, 2, 300), (2, 1024, 4, 200)])
+                                        (1, 900, 2, 300), (2, 1024, 4, 200), (4, 1024, 2, 40)])
 def test_single_launch_form(r, L, Bsz, N):
     # N = 300 (r = 1) and 200 (r = 2) take more than one staged chunk of states
     ssm = _ssm()
