@@ -16,16 +16,18 @@
 // Phase A (all 1024 threads, one root each): as the root-value kernel with one
 // root per thread (roots.hpp: sums on the matrix cores); the twiddles
 // exp(-i pi j/M) go to LDS; the root values to LDS.
-// Phase B: each transform is held by one 64-lane wave (16 points per lane,
-// radix-16 passes), so its LDS exchanges synchronise that wave alone; the
-// workgroup barrier is met only between stages, by every wave.  z-half
-// i = 2p + c is row pair p's input z = u_{2p} + i u_{2p+1}, twisted by
-// exp(-i pi j/M) when c = 1 (the two halves of the zero-padded product, as in
-// the convolution kernel).  Waves 1-8 own z-halves 0-7.
+// Phase B: each transform is held by one 64-lane wave, so its LDS exchanges
+// synchronise that wave alone; the workgroup barrier is met only between
+// stages, by every wave.  z-half i = 2p + c is row pair p's input
+// z = u_{2p} + i u_{2p+1}, twisted by exp(-i pi j/M) when c = 1 (the two halves
+// of the zero-padded product, as in the convolution kernel).  Waves 1-8 own
+// z-halves 0-7.
 //   B1: wave 0 transforms the conjugated root values (the inverse transform of
-//       the root values: the kernel); waves 1-8 their z-halves.
-//   B2: waves 9 and 10 transform the kernel's cyclic and twisted sequences
-//       (the spectra).
+//       the root values: the kernel); waves 1-8 their z-halves (1024 points,
+//       16 per lane, radix-16 passes).
+//   B2: the kernel's cyclic and twisted spectra, each split over four waves
+//       (0 and 9-15) by one radix-4 decimation-in-frequency step: a 256-point
+//       transform per wave.
 //   B3: waves 1-8 multiply by the spectrum of their half and inverse-
 //       transform; the twisted halves are untwisted and added to the cyclic
 //       ones through LDS; rows are stored.
@@ -46,6 +48,16 @@ static_assert(kT1 == 64, "phase B transforms are one wave each");
 constexpr int kPairs1 = 4;                                          // row pairs per channel
 constexpr int kBufs1 = 2 * kPairs1 + 2;                             // exchange buffers (see the roles)
 constexpr int kLdsV1 = lds_padded_size(kM1);
+// spectra stage: four 256-point transforms per spectrum, one wave each
+constexpr int kLogN2 = 8, kN2 = 1 << kLogN2, kLogE2 = 2, kE2 = 1 << kLogE2, kT2 = kN2 >> kLogE2;
+static_assert(kT2 == 64 && 4 * kN2 == kM1, "spectra split: four one-wave transforms of M/4 points");
+static_assert(8 * lds_padded_size(kN2) <= kBufs1 * kLdsV1, "spectra split: exchange buffers");
+
+// a * (-i)^k for a runtime k in 0..3
+__device__ __forceinline__ float2 c_mul_mi_pow(float2 a, int k) {
+    const float2 r = (k & 1) ? make_float2(a.y, -a.x) : a;
+    return (k & 2) ? make_float2(-r.x, -r.y) : r;
+}
 
 template <int RK>
 __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
@@ -196,18 +208,33 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     }
     __syncthreads();
 
-    // B2
-    if (wv == 9 || wv == 10) {
-        const int c = wv - 9;
-        float2 w[1][E];
+    // B2: the cyclic (c = 0) and twisted (c = 1) spectra, each split over four
+    // of the free waves (0 and 9-15) by one radix-4 step of decimation in
+    // frequency: with j = m + 256 p and k = 4 s + q,
+    //   X[4s + q] = sum_m w256^{ms} [w1024^{mq} sum_p x[m + 256 p] (-i)^{pq}],
+    // so wave q forms its 256 inputs from the taps in LDS and runs a 256-point
+    // transform (4 points per lane); the exchange buffers of waves 0-2 are free
+    if (wv == 0 || wv >= 9) {
+        const int idx = wv == 0 ? 0 : wv - 8;
+        const int c = idx >> 2, q = idx & 3;
+        float2 w[1][kE2];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = t + T * e;
-            w[0][e] = c ? c_scale(twl[j], kl[j]) : make_float2(kl[j], 0.0f);
+        for (int e = 0; e < kE2; ++e) {
+            const int m = t + kT2 * e;
+            float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int pp = 0; pp < 4; ++pp) {
+                const int j = m + kN2 * pp;
+                const float2 xv = c ? c_scale(twl[j], kl[j]) : make_float2(kl[j], 0.0f);
+                acc = c_add(acc, c_mul_mi_pow(xv, (pp * q) & 3));
+            }
+            w[0][e] = c_mul(acc, table_root(twl, kLogM1, (m * q) & (M - 1), kLogM1));
         }
-        fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(w, mine, t, tw);
+        const TwiddleRegs<kLogN2, kLogE2> tw2(twl, kLogM1, t);
+        float2* const buf2[1] = {&fbuf[0][0] + idx * lds_padded_size(kN2)};
+        fft_multi<1, kLogN2, kLogE2, false, false, kLogE2, true>(w, buf2, t, tw2);
 #pragma unroll
-        for (int e = 0; e < E; ++e) khl[c][t + T * e] = w[0][e];
+        for (int e = 0; e < kE2; ++e) khl[c][4 * (t + kT2 * e) + q] = w[0][e];
     }
     __syncthreads();
 
