@@ -146,6 +146,23 @@ def recurrence(Abar, Bbar, C, D, u):
     return y.reshape(batch_shape + (L,))
 
 
+def recurrence_from(Abar, Bbar, C, D, u, x0):
+    """The recurrence of one sequence from a given state ([RSS] DPLR block,
+    the discrete recurrence; the step mode carries the state between calls):
+    x_{-1} = x0, x_t = Abar x_{t-1} + Bbar u_t, y_t = C^* x_t + D u_t, t < T.
+
+    u: [T]; x0: [N].  Returns (complex y [T], the state x_{T-1} [N])."""
+    u = np.asarray(u, np.float64)
+    x = np.array(x0, np.complex128)
+    Cc = np.asarray(C, np.complex128).conj()
+    Bb = np.asarray(Bbar, np.complex128)
+    y = np.empty(len(u), np.complex128)
+    for t in range(len(u)):
+        x = Abar @ x + Bb * u[t]
+        y[t] = Cc @ x + D * u[t]
+    return y, x
+
+
 def causal_conv(K, u, D):
     """y_t = sum_{j<=t} K_j u_{t-j} + D u_t.
 

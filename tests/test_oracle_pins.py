@@ -346,6 +346,52 @@ def test_workload_recipe():
 
 
 # --------------------------------------------------------------------------
+# the recurrence from a given state (step mode)
+# --------------------------------------------------------------------------
+def test_recurrence_from_state_cumsum_example():
+    """The scalar example (A = 0, B = C = 1, dt = 1) from x0: Abar = Bbar = 1, so
+    y_t = x0 + sum_{s<=t} u_s exactly, and the final state is x0 + sum(u)."""
+    g = _golden("cumsum_example.json")
+    Abar, Bbar, st = O.bilinear(np.array([[g["A"]]], complex), np.array([g["B"]], complex), g["dt"])
+    assert st == O.OK
+    u = np.array(g["u"], np.float64)
+    x0 = np.array([2.5 - 1.0j])
+    y, xT = O.recurrence_from(Abar, Bbar, np.array([g["C"]], complex), g["D"], u, x0)
+    assert np.array_equal(y, x0[0] + np.cumsum(u))
+    assert xT[0] == x0[0] + u.sum()
+
+
+def test_recurrence_from_state_superposition_and_free_response():
+    """Zero input: y_t = C^* Abar^{t+1} x0 (literal matrix powers); with input,
+    the response is that plus the zero-state recurrence (pinned above), and the
+    final state is Abar^T x0 plus the zero-state final state."""
+    rng = np.random.default_rng(5)
+    N, r, T = 4, 2, 9
+    Lam = -rng.uniform(0.1, 1.0, N) + 1j * rng.normal(0.0, 3.0, N)
+    P = (rng.normal(size=(N, r)) + 1j * rng.normal(size=(N, r))) / 2
+    Q = (rng.normal(size=(N, r)) + 1j * rng.normal(size=(N, r))) / 2
+    B = rng.normal(size=N) + 1j * rng.normal(size=N)
+    C = rng.normal(size=N) + 1j * rng.normal(size=N)
+    Abar, Bbar, st = O.bilinear(O.dplr_matrix(Lam, P, Q), B, 0.2)
+    assert st == O.OK
+    x0 = rng.normal(size=N) + 1j * rng.normal(size=N)
+    y0, xT0 = O.recurrence_from(Abar, Bbar, C, 0.3, np.zeros(T), x0)
+    free = np.array([C.conj() @ np.linalg.matrix_power(Abar, t + 1) @ x0 for t in range(T)])
+    assert np.allclose(y0, free, rtol=1e-12, atol=1e-12)
+    assert np.allclose(xT0, np.linalg.matrix_power(Abar, T) @ x0, rtol=1e-12, atol=1e-12)
+    u = rng.normal(size=T)
+    y, xT = O.recurrence_from(Abar, Bbar, C, 0.3, u, x0)
+    yz = O.recurrence(Abar, Bbar, C, 0.3, u[None])[0]
+    assert np.allclose(y, free + yz, rtol=1e-12, atol=1e-12)
+    _, xTz = O.recurrence_from(Abar, Bbar, C, 0.3, u, np.zeros(N))
+    assert np.allclose(xT, np.linalg.matrix_power(Abar, T) @ x0 + xTz, rtol=1e-12, atol=1e-12)
+    # a stream split into two calls equals one call
+    ya, xa = O.recurrence_from(Abar, Bbar, C, 0.3, u[:4], x0)
+    yb, xb = O.recurrence_from(Abar, Bbar, C, 0.3, u[4:], xa)
+    assert np.allclose(np.concatenate([ya, yb]), y, rtol=1e-13, atol=1e-13) and np.allclose(xb, xT)
+
+
+# --------------------------------------------------------------------------
 # planted mistakes: each must be caught by at least one pin above
 # --------------------------------------------------------------------------
 def _pins_pass():
@@ -362,6 +408,8 @@ def _pins_pass():
         lambda: test_dplr_solve_matches_dense(2),
         test_bordered_branch_matches_dense,
         lambda: test_radix2_matches_numpy_fft(64),
+        test_recurrence_from_state_cumsum_example,
+        test_recurrence_from_state_superposition_and_free_response,
     ]
     for c in checks:
         try:
@@ -406,6 +454,18 @@ def _mut_radix2_sign(a, inverse=False):
     return _orig["radix2_dft"](a, not inverse) * (len(a) if not inverse else 1 / len(a))
 
 
+def _mut_recurrence_from_late_state(Abar, Bbar, C, D, u, x0):
+    # the initial state enters after the first step instead of before it
+    y, x = _orig["recurrence_from"](Abar, Bbar, C, D, u, np.zeros_like(np.asarray(x0, complex)))
+    return y + np.asarray(C, complex).conj() @ np.asarray(x0, complex), x + x0
+
+
+def _mut_recurrence_from_state_before_last(Abar, Bbar, C, D, u, x0):
+    y, x = _orig["recurrence_from"](Abar, Bbar, C, D, u[:-1], x0)
+    y2, _ = _orig["recurrence_from"](Abar, Bbar, C, D, u, x0)
+    return y2, x
+
+
 _orig = {}
 
 
@@ -417,6 +477,8 @@ _orig = {}
     ("kernel_by_iteration", _mut_kernel_no_conj),
     ("recurrence", _mut_recurrence_no_skip),
     ("radix2_dft", _mut_radix2_sign),
+    ("recurrence_from", _mut_recurrence_from_late_state),
+    ("recurrence_from", _mut_recurrence_from_state_before_last),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, name, mutant):
     import oracle.ssm_oracle as mod
