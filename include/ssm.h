@@ -186,6 +186,29 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
                          const float* u, float* y, ssm_c64* K_out, int32_t* status,
                          void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t repeat);
 
+/*
+ * Recurrent (step) mode ([RSS] DPLR block: x_t = Abar x_{t-1} + Bbar u_t,
+ * y_t = C^* x_t + D u_t; recurrent solver of Alg. 1): T steps of the bilinear
+ * recurrence for each of Bsz x H sequences, starting from the state in x and
+ * leaving the state after the last step there, so that successive calls
+ * continue one stream.  Abar is never formed: each step solves with
+ * G = I - (dt/2) A in O(N r) through the Woodbury core, or through the pages'
+ * bordered system when some d_j = 1 - (dt/2) lambda_j is exactly zero
+ * (x_t = 2 G^{-1} x_{t-1} - x_{t-1} + Bbar u_t).  The channel set-up (d, the
+ * core's inverse, Bbar) is float64; the recurrence is float32.
+ *   C    [H,N] complex64: the output vector itself (not C~)
+ *   u, y [Bsz,H,T] float: y_t = Re(C^* x_t) + D u_t
+ *   x    [Bsz,H,N] complex64, in/out (zeros for a fresh stream)
+ *   D    [H] float, nullable (= 0); status [H] int32, nullable
+ * Statuses: invalid-step, singular-bilinear (as ssm_discretize); a failing
+ * channel's y and x are filled with NaN.  Sizes: as above with T in place of
+ * L (T >= 1, any length below 2^31) and N <= 256.  No workspace.
+ */
+int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
+             const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+             const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D,
+             const float* u, float* y, ssm_c64* x, int32_t* status, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,6 +32,9 @@ hipError_t launch_conv_large(int64_t Bsz, int64_t H, int64_t L, int64_t M, const
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                              const float2* Q, const float2* Bv, const float2* C, const float* dt, float2* Bbar,
                              float2* Abar, float2* Ct, int32_t* status, hipStream_t stream);
+hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
+                       const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
+                       const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream);
 }  // namespace ssm
 
 using namespace ssm;
@@ -41,6 +44,7 @@ namespace {
 constexpr int64_t kMaxL = 65536;
 constexpr int64_t kMaxR = 4;
 constexpr int64_t kMaxNDisc = 4096;
+constexpr int64_t kMaxNStep = 256;
 constexpr int64_t kMaxDim = (int64_t)1 << 31;
 
 int64_t pow2_at_least(int64_t v) {
@@ -323,6 +327,24 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
         return SSM_ERR_INVALID_ARGUMENT;
     return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
                         events, repeat);
+}
+
+int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const ssm_c64* Lambda, const ssm_c64* P,
+             const ssm_c64* Q, const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D, const float* u,
+             float* y, ssm_c64* x, int32_t* status, void* stream) {
+    if (Bsz < 1 || H < 1 || N < 1 || r < 1 || T < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (r > kMaxR || N > kMaxNStep || H >= kMaxDim || Bsz >= kMaxDim || T >= kMaxDim || Bsz * H >= kMaxDim ||
+        Bsz * H > ((int64_t)1 << 62) / T)
+        return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !Q || !B || !C || !dt || !u || !y || !x) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, C, x};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(status, 4))
+        return SSM_ERR_INVALID_ARGUMENT;
+    return device_status(launch_step(Bsz, H, N, r, T, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                     (const float2*)B, (const float2*)C, dt, D, u, y, (float2*)x, status,
+                                     (hipStream_t)stream));
 }
 
 }  // extern "C"

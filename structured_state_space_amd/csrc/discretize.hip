@@ -18,61 +18,12 @@
 // and C~ = C - (Abar^*)^M C takes M such adjoint steps.
 #include <float.h>
 
+#include "bilinear.hpp"
 #include "common.hpp"
 
 namespace ssm {
 
 namespace {
-
-constexpr int kWave = 64;
-constexpr int kMaxOrder = 8;  // r + s <= 2 r <= 8
-
-__device__ __forceinline__ double2 wave_sum(double2 v) {
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        v.x += __shfl_xor(v.x, m, kWave);
-        v.y += __shfl_xor(v.y, m, kWave);
-    }
-    return v;
-}
-
-__device__ __forceinline__ double z_abs1(double2 a) { return fabs(a.x) + fabs(a.y); }
-
-// In-place Gauss-Jordan inverse of an n x n complex matrix in LDS (row stride
-// kMaxOrder), run by one lane; false on an exactly zero pivot.
-__device__ bool small_inverse(double2* A, double2* Inv, int n) {
-    for (int i = 0; i < n; ++i)
-        for (int j = 0; j < n; ++j) Inv[i * kMaxOrder + j] = make_double2(i == j ? 1.0 : 0.0, 0.0);
-    for (int c = 0; c < n; ++c) {
-        int piv = c;
-        for (int r = c + 1; r < n; ++r)
-            if (z_abs1(A[r * kMaxOrder + c]) > z_abs1(A[piv * kMaxOrder + c])) piv = r;
-        if (z_is_zero(A[piv * kMaxOrder + c])) return false;
-        if (piv != c)
-            for (int j = 0; j < n; ++j) {
-                double2 t = A[c * kMaxOrder + j];
-                A[c * kMaxOrder + j] = A[piv * kMaxOrder + j];
-                A[piv * kMaxOrder + j] = t;
-                t = Inv[c * kMaxOrder + j];
-                Inv[c * kMaxOrder + j] = Inv[piv * kMaxOrder + j];
-                Inv[piv * kMaxOrder + j] = t;
-            }
-        const double2 pinv = z_inv(A[c * kMaxOrder + c]);
-        for (int j = 0; j < n; ++j) {
-            A[c * kMaxOrder + j] = z_mul(A[c * kMaxOrder + j], pinv);
-            Inv[c * kMaxOrder + j] = z_mul(Inv[c * kMaxOrder + j], pinv);
-        }
-        for (int r = 0; r < n; ++r) {
-            if (r == c) continue;
-            const double2 f = A[r * kMaxOrder + c];
-            for (int j = 0; j < n; ++j) {
-                A[r * kMaxOrder + j] = z_sub(A[r * kMaxOrder + j], z_mul(f, A[c * kMaxOrder + j]));
-                Inv[r * kMaxOrder + j] = z_sub(Inv[r * kMaxOrder + j], z_mul(f, Inv[c * kMaxOrder + j]));
-            }
-        }
-    }
-    return true;
-}
 
 struct SmallMats {
     double2 Mb[kMaxOrder * kMaxOrder];

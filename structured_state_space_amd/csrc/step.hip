@@ -1,0 +1,365 @@
+// Recurrent (step) mode of DPLR channels: the bilinear recurrence run one step
+// at a time, with the state kept between calls (streaming inference).
+//
+// Source: "Recurrent, LSTM, and structured state-space models", DPLR block
+// (x_t = Abar x_{t-1} + Bbar u_t, y_t = C^* x_t + D u_t with
+// Abar = (I - dt A/2)^{-1}(I + dt A/2), Bbar = (I - dt A/2)^{-1} dt B) and the
+// recurrent-solver passage of the Algorithm-1 block (each step solves with
+// G = I - alpha A, alpha = dt/2, in O(N r) through the Woodbury core, or the
+// bordered system when some d_j = 1 - alpha lambda_j is zero).
+//
+// Abar is never formed: Abar = G^{-1}(2I - G) = 2 G^{-1} - I, so
+//   x_t = 2 G^{-1} x_{t-1} - x_{t-1} + Bbar u_t,
+// and with D = diag(d), Z = {j : d_j = 0} (s = |Z| <= r), J its complement,
+//   [z; x_Z] = Mb^{-1} [Q_J^* D_J^{-1} v_J; v_Z],   (G^{-1} v)_J = D_J^{-1} v_J - alpha D_J^{-1} P_J z,
+//   (G^{-1} v)_Z = x_Z
+// where Mb (order r + s) is the matrix of the discretisation kernel.  Per step
+// the wave reduces r + 1 complex sums over the states in one pass (the r sums
+// Q^* D^{-1} x_{t-1} and C^* x_{t-1}, which gives y_{t-1}), reads x_{t-1} at Z,
+// solves with Mb^{-1} and updates its states.
+//
+// Work split: one 64-lane wave per sequence (batch row b, channel h); lane l
+// holds states l + 64 e, e < NPL.  The channel's set-up (d, Z, Mb^{-1}, Bbar)
+// is computed in float64 by the wave itself; the recurrence runs in float32.
+// Inputs and outputs move in blocks of 64 steps (one coalesced load or store
+// per block, the next input block fetched one block ahead).
+#include <float.h>
+
+#include "bilinear.hpp"
+#include "common.hpp"
+
+namespace ssm {
+
+namespace {
+
+constexpr int kMaxRank = 4;
+
+struct StepSetup {
+    double2 Mb[kMaxOrder * kMaxOrder];
+    double2 Mbinv[kMaxOrder * kMaxOrder];
+    float2 Mbf[kMaxOrder * kMaxOrder];
+    int zidx[kMaxRank];
+    int s;
+    int ok;
+};
+
+// The recurrence for one sequence: T steps from the state xs (updated in
+// place).  NZ: room for the bordered form's states in Z (0: Woodbury form).
+template <int NPL, int RK, int NZ>
+__device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const float2* Mbf, const int (&zl)[kMaxRank],
+                                      const int (&ze)[kMaxRank], const float2 (&qd)[NPL][RK],
+                                      const float2 (&pa)[NPL][RK], const float2 (&dv)[NPL], const float2 (&cc)[NPL],
+                                      const float2 (&bb)[NPL], const int (&zs)[NPL], float Dh,
+                                      const float* __restrict__ u, float* __restrict__ y, float2 (&xs)[NPL]) {
+    constexpr int NO = RK + NZ;  // largest order of the small solve
+    float2 Mr[NZ == 0 ? RK : 1][NZ == 0 ? RK : 1];
+    if constexpr (NZ == 0) {
+#pragma unroll
+        for (int i = 0; i < RK; ++i)
+#pragma unroll
+            for (int j = 0; j < RK; ++j) Mr[i][j] = Mbf[i * kMaxOrder + j];
+    }
+    float ucur = (lane < T) ? u[ub + lane] : 0.0f;  // inputs of steps [t0, t0 + 64)
+    float unext = (kWave + lane < T) ? u[ub + kWave + lane] : 0.0f;
+    float yblk = 0.0f;  // outputs of steps [t0, t0 + 64), lane = step - t0
+    float uprev = 0.0f;
+    for (int t = 0; t <= T; ++t) {
+        // sums over x_{t-1}: Q^* D^{-1} x (r of them) and C^* x
+        float2 sq[RK], sc = make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int a = 0; a < RK; ++a) sq[a] = make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) {
+#pragma unroll
+            for (int a = 0; a < RK; ++a) sq[a] = c_add(sq[a], c_mul(qd[e][a], xs[e]));
+            sc = c_add(sc, c_mul(cc[e], xs[e]));
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+            for (int a = 0; a < RK; ++a) {
+                sq[a].x += __shfl_xor(sq[a].x, m, kWave);
+                sq[a].y += __shfl_xor(sq[a].y, m, kWave);
+            }
+            sc.x += __shfl_xor(sc.x, m, kWave);
+            sc.y += __shfl_xor(sc.y, m, kWave);
+        }
+        if (t > 0) {  // y_{t-1} = Re(C^* x_{t-1}) + D u_{t-1}
+            const int k = (t - 1) & (kWave - 1);
+            if (lane == k) yblk = sc.x + Dh * uprev;
+            if (k == kWave - 1 || t == T) {
+                const int t0 = (t - 1) & ~(kWave - 1);
+                if (t0 + lane < T) y[ub + t0 + lane] = yblk;
+            }
+        }
+        if (t == T) break;
+        const int k = t & (kWave - 1);
+        if (k == 0 && t > 0) {  // next block of inputs
+            ucur = unext;
+            unext = (t + kWave + lane < T) ? u[ub + t + kWave + lane] : 0.0f;
+        }
+        const float ut = __shfl(ucur, k, kWave);
+        // [z; x_Z] = Mb^{-1} [Q_J^* D_J^{-1} x; x_Z]
+        float2 sol[NO];
+        if constexpr (NZ == 0) {
+#pragma unroll
+            for (int i = 0; i < RK; ++i) {
+                float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+                for (int j = 0; j < RK; ++j) acc = c_add(acc, c_mul(Mr[i][j], sq[j]));
+                sol[i] = acc;
+            }
+        } else {
+            float2 rhs[NO];
+#pragma unroll
+            for (int a = 0; a < RK; ++a) rhs[a] = sq[a];
+#pragma unroll
+            for (int zz = 0; zz < NZ; ++zz) {
+                rhs[RK + zz] = make_float2(0.0f, 0.0f);
+                if (RK + zz < n) {
+                    float2 v = xs[0];
+#pragma unroll
+                    for (int e = 1; e < NPL; ++e)
+                        if (ze[zz] == e) v = xs[e];
+                    rhs[RK + zz] = make_float2(__shfl(v.x, zl[zz], kWave), __shfl(v.y, zl[zz], kWave));
+                }
+            }
+            // the inverse is read where it is used (an empty asm keeps the
+            // compiler from holding all of it in registers across the loop)
+            int off = 0;
+            asm volatile("" : "+v"(off));
+#pragma unroll
+            for (int i = 0; i < NO; ++i) {
+                float2 acc = make_float2(0.0f, 0.0f);
+                if (i < n) {
+#pragma unroll
+                    for (int j = 0; j < NO; ++j)
+                        if (j < n) acc = c_add(acc, c_mul(Mbf[off + i * kMaxOrder + j], rhs[j]));
+                }
+                sol[i] = acc;
+            }
+        }
+        // x_t = 2 G^{-1} x_{t-1} - x_{t-1} + Bbar u_t
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) {
+            float2 g = c_mul(dv[e], xs[e]);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) g = c_sub(g, c_mul(pa[e][a], sol[a]));
+            if constexpr (NZ > 0) {
+#pragma unroll
+                for (int zz = 0; zz < NZ; ++zz)
+                    if (zs[e] == zz) g = sol[RK + zz];
+            }
+            xs[e] = make_float2(2.0f * g.x - xs[e].x + bb[e].x * ut, 2.0f * g.y - xs[e].y + bb[e].y * ut);
+        }
+        uprev = ut;
+    }
+}
+
+template <int NPL, int RK>
+__global__ __launch_bounds__(kWave) void step_kernel(int Bsz, int H, int N, int T, const float2* __restrict__ Lambda,
+                                                     const float2* __restrict__ P, const float2* __restrict__ Q,
+                                                     const float2* __restrict__ Bv, const float2* __restrict__ C,
+                                                     const float* __restrict__ dt, const float* __restrict__ D,
+                                                     const float* __restrict__ u, float* __restrict__ y,
+                                                     float2* __restrict__ x, int32_t* __restrict__ status) {
+    __shared__ StepSetup sm;
+    const int seq = blockIdx.x;  // = b * H + h, the row order of u, y and x
+    const int h = seq % H;
+    const int b = seq / H;
+    const int lane = threadIdx.x;
+    const size_t hb = (size_t)h * N;
+    const size_t hr = hb * RK;
+    const size_t xb = (size_t)seq * N;
+    const size_t ub = (size_t)seq * T;
+    const float dtf = dt[h];
+    int st = SSM_ST_OK;
+    if (!(dtf > 0.0f) || !(dtf <= FLT_MAX)) st = SSM_ST_INVALID_STEP;
+    const double dtv = (double)dtf, alpha = 0.5 * dtv;
+
+    // ---- set-up in float64: d^{-1}, Z, Mb^{-1} ----
+    double2 dinv[NPL];
+    if (lane == 0) sm.s = 0;
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        bool isz = false;
+        dinv[e] = make_double2(0.0, 0.0);
+        if (j < N && st == SSM_ST_OK) {
+            const double2 lam = z_from(Lambda[hb + j]);
+            const double2 d = make_double2(1.0 - alpha * lam.x, -alpha * lam.y);
+            isz = z_is_zero(d);
+            if (!isz) dinv[e] = z_inv(d);
+        }
+        uint64_t mask = __ballot(isz);
+        if (lane == 0) {
+            while (mask) {
+                const int bit = __ffsll((unsigned long long)mask) - 1;
+                if (sm.s < kMaxRank) sm.zidx[sm.s] = kWave * e + bit;
+                sm.s++;
+                mask &= mask - 1;
+            }
+        }
+    }
+    __syncthreads();
+    const int s = sm.s;
+    if (st == SSM_ST_OK && s > RK) st = SSM_ST_SINGULAR_BILINEAR;
+    if (st == SSM_ST_OK) {
+        for (int a = 0; a < RK; ++a)
+            for (int c = 0; c < RK; ++c) {
+                double2 acc = make_double2(0.0, 0.0);
+#pragma unroll
+                for (int e = 0; e < NPL; ++e) {
+                    const int j = lane + kWave * e;
+                    if (j < N) {
+                        const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
+                        const double2 p = z_from(P[hr + (size_t)j * RK + c]);
+                        acc = z_add(acc, z_mul(z_mul(z_conj(q), dinv[e]), p));
+                    }
+                }
+                acc = wave_sum(acc);
+                if (lane == 0) sm.Mb[a * kMaxOrder + c] = make_double2((a == c ? 1.0 : 0.0) + alpha * acc.x, alpha * acc.y);
+            }
+        if (lane == 0) {
+            for (int zz = 0; zz < s; ++zz) {
+                const size_t jz = (size_t)sm.zidx[zz];
+                for (int a = 0; a < RK; ++a) {
+                    const double2 q = z_from(Q[hr + jz * RK + a]);
+                    const double2 p = z_from(P[hr + jz * RK + a]);
+                    sm.Mb[a * kMaxOrder + RK + zz] = make_double2(-q.x, q.y);  // -conj(Q_za)
+                    sm.Mb[(RK + zz) * kMaxOrder + a] = z_scale(p, alpha);     // alpha P_za
+                }
+                for (int z2 = 0; z2 < s; ++z2) sm.Mb[(RK + zz) * kMaxOrder + RK + z2] = make_double2(0.0, 0.0);
+            }
+            sm.ok = small_inverse(sm.Mb, sm.Mbinv, RK + s);
+            for (int i = 0; i < kMaxOrder * kMaxOrder; ++i) sm.Mbf[i] = c_from(sm.Mbinv[i]);
+        }
+        __syncthreads();
+        if (!sm.ok) st = SSM_ST_SINGULAR_BILINEAR;
+    }
+    if (st != SSM_ST_OK) {
+        const float nanf = __builtin_nanf("");
+        for (int t = lane; t < T; t += kWave) y[ub + t] = nanf;
+        for (int j = lane; j < N; j += kWave) x[xb + j] = c_nan();
+        if (lane == 0 && b == 0 && status) status[h] = st;
+        return;
+    }
+    const int n = RK + s;
+
+    // ---- Bbar = G^{-1} (dt B) (float64), and the per-state constants ----
+    float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL], xs[NPL];
+    int zs[NPL];  // slot in Z of the state, or -1
+    {
+        double2 rhs[kMaxOrder];
+        for (int a = 0; a < RK; ++a) {
+            double2 acc = make_double2(0.0, 0.0);
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) {
+                const int j = lane + kWave * e;
+                if (j < N) {
+                    const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
+                    acc = z_add(acc, z_mul(z_mul(z_conj(q), dinv[e]), z_scale(z_from(Bv[hb + j]), dtv)));
+                }
+            }
+            rhs[a] = wave_sum(acc);
+        }
+        for (int zz = 0; zz < s; ++zz) rhs[RK + zz] = z_scale(z_from(Bv[hb + sm.zidx[zz]]), dtv);
+        double2 sol[kMaxOrder];
+        for (int i = 0; i < n; ++i) {
+            double2 acc = make_double2(0.0, 0.0);
+            for (int j = 0; j < n; ++j) acc = z_add(acc, z_mul(sm.Mbinv[i * kMaxOrder + j], rhs[j]));
+            sol[i] = acc;
+        }
+#pragma unroll
+        for (int e = 0; e < NPL; ++e) {
+            const int j = lane + kWave * e;
+            zs[e] = -1;
+            for (int zz = 0; zz < s; ++zz)
+                if (sm.zidx[zz] == j) zs[e] = zz;
+            double2 bbar = make_double2(0.0, 0.0);
+            dv[e] = c_from(dinv[e]);
+            cc[e] = make_float2(0.0f, 0.0f);
+            xs[e] = make_float2(0.0f, 0.0f);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) {
+                qd[e][a] = make_float2(0.0f, 0.0f);
+                pa[e][a] = make_float2(0.0f, 0.0f);
+            }
+            if (j < N) {
+                cc[e] = c_conj(C[hb + j]);
+                xs[e] = x[xb + j];
+                if (zs[e] < 0) {
+                    double2 tb = z_scale(z_from(Bv[hb + j]), dtv);
+#pragma unroll
+                    for (int a = 0; a < RK; ++a) {
+                        const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
+                        const double2 p = z_from(P[hr + (size_t)j * RK + a]);
+                        qd[e][a] = c_from(z_mul(z_conj(q), dinv[e]));
+                        pa[e][a] = c_from(z_scale(z_mul(dinv[e], p), alpha));
+                        tb = z_sub(tb, z_scale(z_mul(p, sol[a]), alpha));
+                    }
+                    bbar = z_mul(dinv[e], tb);
+                } else {
+                    for (int zz = 0; zz < s; ++zz)
+                        if (zs[e] == zz) bbar = sol[RK + zz];
+                }
+            }
+            bb[e] = c_from(bbar);
+        }
+    }
+    const float Dh = D ? D[h] : 0.0f;
+    // Z's owners: lane and register slot of each state in Z (uniform)
+    int zl[kMaxRank], ze[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) {
+        const int j = zz < s ? sm.zidx[zz] : 0;
+        zl[zz] = j % kWave;
+        ze[zz] = j / kWave;
+    }
+
+    // ---- the recurrence (float32) ----
+    // channels with no zero d_j (the usual case) take the Woodbury form, whose
+    // r x r inverse stays in registers; the bordered form re-reads its order
+    // r + s inverse from LDS every step
+    if (s == 0)
+        recur<NPL, RK, 0>(T, lane, ub, n, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+    else
+        recur<NPL, RK, kMaxRank>(T, lane, ub, n, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        if (j < N) x[xb + j] = xs[e];
+    }
+    if (lane == 0 && b == 0 && status) status[h] = SSM_ST_OK;
+}
+
+template <int NPL>
+hipError_t launch_npl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
+                      const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
+                      const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream) {
+#define SSM_STEP(RK)                                                                                             \
+    if (r == RK) {                                                                                               \
+        hipLaunchKernelGGL((step_kernel<NPL, RK>), dim3((unsigned)(Bsz * H)), dim3(kWave), 0, stream, (int)Bsz,   \
+                           (int)H, (int)N, (int)T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status);                 \
+        return hipGetLastError();                                                                                \
+    }
+    SSM_STEP(1) SSM_STEP(2) SSM_STEP(3) SSM_STEP(4)
+#undef SSM_STEP
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+constexpr int64_t kStepMaxN = 4 * kWave;
+
+hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
+                       const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
+                       const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream) {
+    if (N <= kWave) return launch_npl<1>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+    if (N <= 2 * kWave) return launch_npl<2>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+    if (N <= kStepMaxN) return launch_npl<4>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace ssm

@@ -32,7 +32,7 @@ ST_INVALID_STEP = 19
 OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD = 0, 1, 2, 3
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
-           "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled")
+           "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step")
 
 
 class SSMError(RuntimeError):
@@ -65,6 +65,8 @@ def _load():
     lib.ssm_forward.restype = i32
     lib.ssm_forward_profiled.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp, vp, ctypes.c_int32]
     lib.ssm_forward_profiled.restype = i32
+    lib.ssm_step.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
+    lib.ssm_step.restype = i32
     return lib
 
 
@@ -235,6 +237,32 @@ def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=
     if rc != OK:
         raise SSMError(name, rc)
     return dict(y=y, K=K_out, status=status)
+
+
+def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):
+    """ssm_step: T steps of the recurrence from the state x (zeros when None);
+    returns dict(y [Bsz,H,T] f32, x [Bsz,H,N] c64 (the state after the last
+    step, updated in place when given), status [H] i32)."""
+    H, N, r, dev = _params(Lambda, P, Q, B, C, dt)
+    Bsz, H2, T = u.shape
+    if H2 != H:
+        raise ValueError("u: channel count does not match the parameters")
+    _check(u, "u", torch.float32, (Bsz, H, T), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    if x is None:
+        x = torch.zeros((Bsz, H, N), dtype=torch.complex64, device=dev)
+    _check(x, "x", torch.complex64, (Bsz, H, N), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", torch.float32, (Bsz, H, T), dev)
+    if status is None:
+        status = torch.empty((H,), dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, (H,), dev)
+    rc = lib.ssm_step(Bsz, H, N, r, T, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(C), _ptr(dt), _ptr(D), _ptr(u),
+                      _ptr(y), _ptr(x), _ptr(status), _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_step", rc)
+    return dict(y=y, x=x, status=status)
 
 
 def to_device(params, device="cuda:0"):
