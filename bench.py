@@ -107,6 +107,84 @@ def cpu_baseline(w, p, u, seconds):
                       f"({dt:.1f} s, one thread)"}
 
 
+STEP_METRIC = "channel-steps/sec (B·H·T) for the S4 recurrent step mode; % FP32 roofline"
+
+
+def step_flops(w):
+    """Algorithmic flops of one ssm_step call over T = L steps: per (sequence,
+    step, state) the r sums Q^* D^{-1} x and C^* x (8 flops per complex
+    multiply-add), D^{-1} x (6), the rank-r correction (8 r) and the update
+    2 g - x + Bbar u (8)."""
+    return w.Bsz * w.H * w.L * w.N * (16 * w.r + 22)
+
+
+def cpu_baseline_step(w, p, u, seconds):
+    """The oracle's recurrence from a state, one thread, on a bounded channel sample."""
+    from threadpoolctl import threadpool_limits
+
+    import numpy as np
+    import oracle as O
+    done = 0
+    t0 = time.perf_counter()
+    with threadpool_limits(limits=1):
+        while done < w.H and time.perf_counter() - t0 < seconds:
+            c = p.channel(done)
+            Abar, Bbar, _ = O.bilinear(O.dplr_matrix(c["Lambda"], c["P"], c["Q"]), c["B"], float(c["dt"]))
+            for b in range(w.Bsz):
+                O.recurrence_from(Abar, Bbar, c["C"], float(c["D"]), u[b, done, :], np.zeros(w.N, complex))
+            done += 1
+    dt = time.perf_counter() - t0
+    return {"value": done * w.Bsz * w.L / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
+            "sample": f"{done} of {w.H} channels x {w.Bsz} rows x {w.L} steps of workload {w.name}: complex128 "
+                      f"dense bilinear matrices, time-stepped recurrence ({dt:.1f} s, one thread)"}
+
+
+def bench_step(args, w, p, u, dev):
+    import torch
+
+    from structured_state_space_amd import ssm
+    d = ssm.to_device(p, dev)
+    ut = torch.from_numpy(u).to(dev)
+    x = torch.zeros((w.Bsz, w.H, w.N), dtype=torch.complex64, device=dev)
+    y = torch.empty_like(ut)
+    status = torch.empty(w.H, dtype=torch.int32, device=dev)
+
+    def call():
+        ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], ut, x=x, y=y, status=status)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 100))  # one call covers L steps of every sequence
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        call()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_events = start.elapsed_time(end) / steps
+    ms = max(ms_events, 1e3 * t_wall / steps)
+    if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
+        raise RuntimeError("step mode produced a nonzero status or non-finite output")
+    flops = step_flops(w)
+    achieved = flops * 1e-12 / (ms_events * 1e-3)
+    line = {
+        "metric": STEP_METRIC, "value": w.Bsz * w.H * w.L / (ms * 1e-3), "unit": UNIT, "n_gpus": 1,
+        "steps": steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "op": "step", "H": w.H, "N": w.N, "r": w.r, "T": w.L, "batch": w.Bsz},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None, "kernel": "step"},
+        "ms_per_step_events": ms_events,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_step(w, p, u, args.cpu_seconds)
+    print(json.dumps(line))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +195,9 @@ def main():
     ap.add_argument("--stage-repeat", type=int, default=10,
                     help="launches of each stage per timing bracket in the per-kernel measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--op", choices=("forward", "step"), default="forward",
+                    help="forward: the filter path (the headline); step: the recurrent step mode, "
+                         "T = L steps of every sequence per call, the state carried between calls")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -144,6 +225,8 @@ def main():
     from structured_state_space_amd import ssm
 
     w, p, u = I.workload(args.workload)
+    if args.op == "step":
+        return bench_step(args, w, p, u, dev)
     M, n_fft = ssm.transform_lengths(w.L)
     form = ssm.forward_form(w.Bsz, w.H, w.L)
     fused = form == 2

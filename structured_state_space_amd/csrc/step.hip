@@ -43,6 +43,36 @@ struct StepSetup {
     int ok;
 };
 
+// Sum over the 64 lanes, returned to every lane: DPP exchanges within each
+// row of 16 lanes (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
+// row_mirror: each lane then holds its row's sum), then the four row sums by
+// readlane.  No LDS round trip (the shuffle-based sum takes six).
+template <int CTRL>
+__device__ __forceinline__ float dpp_get(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+// K values at once, stage by stage, so that the exchanges of different values
+// fill each other's wait states
+template <int K>
+__device__ __forceinline__ void wave_allsum(float (&v)[K]) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0xB1>(v[i]);   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x4E>(v[i]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x141>(v[i]);  // row_half_mirror
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x140>(v[i]);  // row_mirror
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+        const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 0));
+        const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 16));
+        const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 32));
+        const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 48));
+        v[i] = (s0 + s1) + (s2 + s3);
+    }
+}
+
 // The recurrence for one sequence: T steps from the state xs (updated in
 // place).  NZ: room for the bordered form's states in Z (0: Woodbury form).
 template <int NPL, int RK, int NZ>
@@ -59,8 +89,11 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
 #pragma unroll
             for (int j = 0; j < RK; ++j) Mr[i][j] = Mbf[i * kMaxOrder + j];
     }
-    float ucur = (lane < T) ? u[ub + lane] : 0.0f;  // inputs of steps [t0, t0 + 64)
-    float unext = (kWave + lane < T) ? u[ub + kWave + lane] : 0.0f;
+    // inputs of steps [t0, t0 + 64) and the next block; lanes past the end
+    // read the last input instead (never used), so the loads carry no branch
+    // and are waited for only where used
+    float ucur = u[ub + min(lane, T - 1)];
+    float unext = u[ub + min(kWave + lane, T - 1)];
     float yblk = 0.0f;  // outputs of steps [t0, t0 + 64), lane = step - t0
     float uprev = 0.0f;
     for (int t = 0; t <= T; ++t) {
@@ -74,15 +107,18 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
             for (int a = 0; a < RK; ++a) sq[a] = c_add(sq[a], c_mul(qd[e][a], xs[e]));
             sc = c_add(sc, c_mul(cc[e], xs[e]));
         }
-#pragma unroll
-        for (int m = 32; m >= 1; m >>= 1) {
+        {  // the r sums and the real part of C^* x (the only part y uses)
+            float v[2 * RK + 1];
 #pragma unroll
             for (int a = 0; a < RK; ++a) {
-                sq[a].x += __shfl_xor(sq[a].x, m, kWave);
-                sq[a].y += __shfl_xor(sq[a].y, m, kWave);
+                v[2 * a] = sq[a].x;
+                v[2 * a + 1] = sq[a].y;
             }
-            sc.x += __shfl_xor(sc.x, m, kWave);
-            sc.y += __shfl_xor(sc.y, m, kWave);
+            v[2 * RK] = sc.x;
+            wave_allsum<2 * RK + 1>(v);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) sq[a] = make_float2(v[2 * a], v[2 * a + 1]);
+            sc.x = v[2 * RK];
         }
         if (t > 0) {  // y_{t-1} = Re(C^* x_{t-1}) + D u_{t-1}
             const int k = (t - 1) & (kWave - 1);
@@ -96,9 +132,9 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
         const int k = t & (kWave - 1);
         if (k == 0 && t > 0) {  // next block of inputs
             ucur = unext;
-            unext = (t + kWave + lane < T) ? u[ub + t + kWave + lane] : 0.0f;
+            unext = u[ub + min(t + kWave + lane, T - 1)];
         }
-        const float ut = __shfl(ucur, k, kWave);
+        const float ut = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ucur), k));  // k is uniform
         // [z; x_Z] = Mb^{-1} [Q_J^* D_J^{-1} x; x_Z]
         float2 sol[NO];
         if constexpr (NZ == 0) {
@@ -121,7 +157,8 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
 #pragma unroll
                     for (int e = 1; e < NPL; ++e)
                         if (ze[zz] == e) v = xs[e];
-                    rhs[RK + zz] = make_float2(__shfl(v.x, zl[zz], kWave), __shfl(v.y, zl[zz], kWave));
+                    rhs[RK + zz] = make_float2(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.x), zl[zz])),
+                                               __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v.y), zl[zz])));
                 }
             }
             // the inverse is read where it is used (an empty asm keeps the
