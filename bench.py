@@ -185,6 +185,53 @@ def bench_step(args, w, p, u, dev):
     return 0
 
 
+def bench_complex(args, w, p, u, dev):
+    """ssm_forward_complex timed like the headline step; its roofline is that of
+    the work it adds to ssm_forward, rated as a whole: the root values' flops
+    at the FP32 peak plus twice the convolution's algorithmic bytes at the HBM
+    peak (the phases are serial), over the measured step."""
+    import torch
+
+    from structured_state_space_amd import ssm
+    d = ssm.to_device(p, dev)
+    ut = torch.from_numpy(u).to(dev)
+    Ct = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], w.L, want_bbar=False)["Ctilde"]
+    nbytes = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, w.Bsz, w.H, w.N, w.r, w.L)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+
+    def call():
+        return ssm.forward_complex(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut, workspace=ws)
+
+    for _ in range(args.warmup):
+        out = call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        out = call()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_events = start.elapsed_time(end) / args.steps
+    ms = max(ms_events, 1e3 * t_wall / args.steps)
+    if int(out["status"].abs().max()) != 0 or not bool(torch.isfinite(out["y_im"]).all()):
+        raise RuntimeError("complex output produced a nonzero status or non-finite values")
+    M = ssm.transform_lengths(w.L)[0]
+    alg = algorithmic(w, M, False)
+    troof_ms = (alg["cauchy"]["work"] / (PEAK_FP32_TFLOPS * 1e12) + 2 * alg["conv"]["work"] / (PEAK_HBM_GBS * 1e9)) * 1e3
+    line = {
+        "metric": "channel-steps/sec (B·H·L) for the S4 filter path with complex output", "unit": UNIT,
+        "value": w.Bsz * w.H * w.L / (ms * 1e-3), "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic", "config": {"workload": w.name, "op": "complex", "H": w.H, "N": w.N, "r": w.r, "L": w.L,
+                                        "batch": w.Bsz},
+        "composite_roofline_frac": troof_ms / ms, "ms_per_step_events": ms_events,
+    }
+    print(json.dumps(line))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -195,9 +242,10 @@ def main():
     ap.add_argument("--stage-repeat", type=int, default=10,
                     help="launches of each stage per timing bracket in the per-kernel measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("forward", "step"), default="forward",
+    ap.add_argument("--op", choices=("forward", "step", "complex"), default="forward",
                     help="forward: the filter path (the headline); step: the recurrent step mode, "
-                         "T = L steps of every sequence per call, the state carried between calls")
+                         "T = L steps of every sequence per call, the state carried between calls; "
+                         "complex: the filter path with the imaginary output as well")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -227,6 +275,8 @@ def main():
     w, p, u = I.workload(args.workload)
     if args.op == "step":
         return bench_step(args, w, p, u, dev)
+    if args.op == "complex":
+        return bench_complex(args, w, p, u, dev)
     M, n_fft = ssm.transform_lengths(w.L)
     form = ssm.forward_form(w.Bsz, w.H, w.L)
     fused = form == 2

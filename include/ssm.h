@@ -72,6 +72,7 @@ typedef struct ssm_c64 {
 #define SSM_OP_KERNEL_GEN 1
 #define SSM_OP_FFTCONV 2
 #define SSM_OP_FORWARD 3
+#define SSM_OP_FORWARD_COMPLEX 4
 
 /*
  * Workspace size in bytes that entry point `op` needs for these sizes (Bsz is
@@ -167,6 +168,24 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
                 const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
                 const float* u, float* y, ssm_c64* K_out, int32_t* status,
                 void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The whole filter path with the complex output ([RSS] DPLR block: y_t = C^* x_t
+ * + D u_t is complex for a complex C; with D real its imaginary part is
+ * Im(C^* x_t) = (Im K) * u):
+ *   y_re = (Re K) * u + D u   (as ssm_forward's y)
+ *   y_im = (Im K) * u
+ * Root values once; then the spectra of Re K (+ D, from the root values, which
+ * also writes K) and its convolution, and the spectra of Im K (read back from
+ * K) and its convolution.  y_re and y_im [Bsz,H,L] float must not overlap u
+ * or each other.  K_out nullable (then K goes to the workspace).  Workspace:
+ * ssm_workspace_bytes(SSM_OP_FORWARD_COMPLEX, ...).
+ */
+int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
+                        const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                        const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                        const float* u, float* y_re, float* y_im, ssm_c64* K_out, int32_t* status,
+                        void* ws, size_t ws_bytes, void* stream);
 
 /*
  * ssm_forward with per-kernel timing marks for benchmarks and profilers.

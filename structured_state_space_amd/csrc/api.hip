@@ -75,7 +75,8 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
     WsLayout w;
     const int64_t M = pow2_at_least(L);
     size_t off = 0;
-    if (op == SSM_OP_KERNEL_GEN || op == SSM_OP_FORWARD) {
+    const bool fwd = op == SSM_OP_FORWARD || op == SSM_OP_FORWARD_COMPLEX;
+    if (op == SSM_OP_KERNEL_GEN || fwd) {
         w.roots = off;
         w.roots_bytes = (size_t)H * M * sizeof(float2);
         off = align256(off + w.roots_bytes);
@@ -86,7 +87,7 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.tant_bytes = (size_t)M * sizeof(double);
         off = align256(off + w.tant_bytes);
     }
-    if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {
+    if (op == SSM_OP_FFTCONV || fwd) {
         w.khat = off;
         w.khat_bytes = (size_t)H * 2 * M * sizeof(float2);
         off = align256(off + w.khat_bytes);
@@ -97,11 +98,16 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
     if (M > ((int64_t)1 << kMaxLdsLogM)) {  // multi-pass transforms
         w.big = off;
         if (op == SSM_OP_KERNEL_GEN) w.big_bytes = (size_t)H * M * sizeof(float2);  // first-pass output
-        if (op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) {  // conv intermediate: one chunk of row pairs
+        if (op == SSM_OP_FFTCONV || fwd) {  // conv intermediate: one chunk of row pairs
             const int64_t npairs = ((Bsz + 1) / 2) * H;
             w.big_bytes = (size_t)(npairs < kConvChunkPairs ? npairs : kConvChunkPairs) * 2 * M * sizeof(float2);
         }
         off = align256(off + w.big_bytes);
+    }
+    if (op == SSM_OP_FORWARD_COMPLEX) {
+        w.kbuf = off;
+        w.kbuf_bytes = (size_t)H * L * sizeof(float2);
+        off = align256(off + w.kbuf_bytes);
     }
     w.total = off;
     return w;
@@ -156,7 +162,8 @@ int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, in
         case SSM_OP_DISCRETIZE: rc = check_sizes(1, H, N, r, L, true, false); break;
         case SSM_OP_KERNEL_GEN: rc = check_sizes(1, H, N, r, L, true, false); break;
         case SSM_OP_FFTCONV: rc = check_sizes(Bsz, H, 1, 1, L, false, true); break;
-        case SSM_OP_FORWARD: rc = check_sizes(Bsz, H, N, r, L, true, true); break;
+        case SSM_OP_FORWARD:
+        case SSM_OP_FORWARD_COMPLEX: rc = check_sizes(Bsz, H, N, r, L, true, true); break;
         default: return SSM_ERR_INVALID_ARGUMENT;
     }
     if (rc != SSM_OK) return rc;
@@ -327,6 +334,55 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
         return SSM_ERR_INVALID_ARGUMENT;
     return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws, ws_bytes, stream,
                         events, repeat);
+}
+
+int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda,
+                        const ssm_c64* P, const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt,
+                        const float* D, const float* u, float* y_re, float* y_im, ssm_c64* K_out, int32_t* status,
+                        void* ws, size_t ws_bytes, void* stream) {
+    int rc = check_sizes(Bsz, H, N, r, L, true, true);
+    if (rc != SSM_OK) return rc;
+    const int64_t M = pow2_at_least(L);
+    if (!Lambda || !P || !Q || !B || !Ctilde || !dt || !u || !y_re || !y_im) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, Ctilde, K_out};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y_re, 4) || !aligned(y_im, 4) ||
+        !aligned(status, 4) || !aligned(ws, 256))
+        return SSM_ERR_INVALID_ARGUMENT;
+    const WsLayout w = layout(SSM_OP_FORWARD_COMPLEX, Bsz, H, N, r, L);
+    if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    char* base = (char*)ws;
+    float2* roots = (float2*)(base + w.roots);
+    int32_t* tstat = (int32_t*)(base + w.tstat);
+    float2* khat = (float2*)(base + w.khat);
+    float2* twtab = (float2*)(base + w.tw);
+    float2* K = K_out ? (float2*)K_out : (float2*)(base + w.kbuf);
+    const bool large = M > ((int64_t)1 << kMaxLdsLogM);
+    const int64_t tiles = cauchy_tiles(H, r, M);
+    hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab,
+                                 (double*)(base + w.tant), s);
+    // real part: the spectra of Re K + D delta_0 from the root values (K written on the way)
+    if (e == hipSuccess)
+        e = large ? launch_spectrum_large(true, H, L, M, tiles, roots, roots, tstat, nullptr, 1, D, K, status, khat,
+                                          twtab, s)
+                  : launch_spectrum(true, H, L, M, tiles, roots, tstat, nullptr, 1, D, K, status, khat, twtab, s);
+    if (e == hipSuccess)
+        e = large ? launch_conv_large(Bsz, H, L, M, u, y_re, khat, (float2*)(base + w.big), twtab, s)
+                  : launch_conv(Bsz, H, L, M, u, y_re, khat, twtab, s);
+    // imaginary part: the spectra of Im K (the odd floats of K; no skip term)
+    const float* Kim = (const float*)K + 1;
+    if (e == hipSuccess)
+        e = large ? launch_spectrum_large(false, H, L, M, 0, nullptr, nullptr, nullptr, Kim, 2, nullptr, nullptr,
+                                          nullptr, khat, twtab, s)
+                  : launch_spectrum(false, H, L, M, 0, nullptr, nullptr, Kim, 2, nullptr, nullptr, nullptr, khat,
+                                    twtab, s);
+    if (e == hipSuccess)
+        e = large ? launch_conv_large(Bsz, H, L, M, u, y_im, khat, (float2*)(base + w.big), twtab, s)
+                  : launch_conv(Bsz, H, L, M, u, y_im, khat, twtab, s);
+    return device_status(e);
 }
 
 int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const ssm_c64* Lambda, const ssm_c64* P,

@@ -69,6 +69,7 @@ struct WsLayout {
     size_t khat = 0, khat_bytes = 0;       // [H, 2, M] complex64: conv spectra (cyclic, twisted)
     size_t tw = 0, tw_bytes = 0;           // [M] complex64: exp(-i pi j/M), the conv's twiddles
     size_t big = 0, big_bytes = 0;         // scratch of the multi-pass transforms (M > 16384)
+    size_t kbuf = 0, kbuf_bytes = 0;       // [H, L] complex64: the kernel (complex output, no K_out given)
     size_t total = 0;
 };
 

@@ -29,10 +29,11 @@ ST_RESONANT_CORRECTION = 16
 ST_RESONANT_DIAGONAL = 17
 ST_SINGULAR_BILINEAR = 18
 ST_INVALID_STEP = 19
-OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD = 0, 1, 2, 3
+OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD, OP_FORWARD_COMPLEX = 0, 1, 2, 3, 4
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
-           "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step")
+           "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step",
+           "ssm_forward_complex")
 
 
 class SSMError(RuntimeError):
@@ -67,6 +68,8 @@ def _load():
     lib.ssm_forward_profiled.restype = i32
     lib.ssm_step.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
     lib.ssm_step.restype = i32
+    lib.ssm_forward_complex.argtypes = [i64, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
+    lib.ssm_forward_complex.restype = i32
     return lib
 
 
@@ -237,6 +240,28 @@ def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=
     if rc != OK:
         raise SSMError(name, rc)
     return dict(y=y, K=K_out, status=status)
+
+
+def forward_complex(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, workspace=None):
+    """ssm_forward_complex: returns dict(y_re, y_im [Bsz,H,L] f32 (the real and
+    imaginary parts of y), K [H,L] c64 or None, status [H] i32)."""
+    H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
+    Bsz, H2, L = u.shape
+    if H2 != H:
+        raise ValueError("u: channel count does not match the parameters")
+    _check(u, "u", torch.float32, (Bsz, H, L), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    y_re, y_im = torch.empty_like(u), torch.empty_like(u)
+    K_out = torch.empty((H, L), dtype=torch.complex64, device=dev) if want_kernel else None
+    status = torch.empty((H,), dtype=torch.int32, device=dev)
+    nbytes = workspace_bytes(OP_FORWARD_COMPLEX, Bsz, H, N, r, L)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.ssm_forward_complex(Bsz, H, N, r, L, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt),
+                                 _ptr(D), _ptr(u), _ptr(y_re), _ptr(y_im), _ptr(K_out), _ptr(status), _ptr(ws),
+                                 nbytes, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_forward_complex", rc)
+    return dict(y_re=y_re, y_im=y_im, K=K_out, status=status)
 
 
 def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):

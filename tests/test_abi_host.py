@@ -130,3 +130,37 @@ def test_fftconv_and_kernel_gen_reject():
                               None) == ssm.ERR_INVALID_ARGUMENT
     assert lib.ssm_discretize(1, 4, 1, 16, FAKE, FAKE, FAKE, FAKE, None, FAKE, None, None, FAKE, None, None, 0,
                               None) == ssm.ERR_INVALID_ARGUMENT
+
+
+def test_forward_complex_workspace_and_rejects():
+    H, L = 256, 1000
+    fwd = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, L)
+    cpx = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, 8, H, 64, 1, L)
+    assert cpx >= fwd + H * L * 8 and cpx % 256 == 0   # plus the complex kernel [H, L]
+
+    def call(r=1, y_re=FAKE, y_im=FAKE, ws_bytes=1 << 30):
+        return ssm.lib.ssm_forward_complex(2, 3, 4, r, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, y_re, y_im,
+                                           None, None, FAKE, ws_bytes, None)
+
+    assert call(y_im=None) == ssm.ERR_INVALID_ARGUMENT
+    assert call(y_re=FAKE + 2) == ssm.ERR_INVALID_ARGUMENT
+    assert call(ws_bytes=64) == ssm.ERR_WORKSPACE
+    assert call(r=5) == ssm.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(Bsz=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(N=257), ssm.ERR_UNSUPPORTED),       # step mode holds at most 4 states per lane
+    (dict(r=5), ssm.ERR_UNSUPPORTED),
+    (dict(C=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(x=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE + 4), ssm.ERR_INVALID_ARGUMENT),    # state not 8-byte aligned
+    (dict(u=FAKE + 2), ssm.ERR_INVALID_ARGUMENT),
+])
+def test_step_rejects_before_launch(kw, code):
+    a = dict(Bsz=2, H=3, N=4, r=1, T=16, Lambda=FAKE, P=FAKE, Q=FAKE, B=FAKE, C=FAKE, dt=FAKE, D=None, u=FAKE,
+             y=FAKE, x=FAKE, status=None)
+    a.update(kw)
+    assert ssm.lib.ssm_step(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["Lambda"], a["P"], a["Q"], a["B"], a["C"],
+                            a["dt"], a["D"], a["u"], a["y"], a["x"], a["status"], None) == code

@@ -381,3 +381,49 @@ def test_deterministic_and_linear_and_causal():
     ref[:, 0] += d["D"]
     err = (out["y"][0] - ref).abs().amax(dim=-1) / ref.abs().amax(dim=-1)
     assert float(err.max()) <= TOL
+
+
+# ---------------------------------------------------------------------------
+# complex output: y_im = Im(C^* x_t) = (Im K) * u, from the recurrence's
+# imaginary part; y_re as ssm_forward's y
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
+    (3, 16, 1, 100, 3, "random"),      # LDS-resident transforms, ragged L
+    (4, 64, 2, 1024, 2, "s4"),
+    (2, 8, 1, 20000, 1, "random"),     # multi-pass transforms (M = 32768)
+])
+def test_forward_complex_matches_recurrence(H, N, r, L, Bsz, kind):
+    ssm = _ssm()
+    p = I.random_params(H * 31 + N + L, H, N, r, L, lambda_kind=kind, dt_range=(1e-2, 1e-1))
+    u = I.random_input(L + 3, Bsz, H, L)
+    d = _dev(p)
+    disc = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_bbar=False)
+    ut = torch.from_numpy(u).to(DEV)
+    out = ssm.forward_complex(d["Lambda"], d["P"], d["Q"], d["B"], disc["Ctilde"], d["dt"], d["D"], ut,
+                              want_kernel=True)
+    fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], disc["Ctilde"], d["dt"], d["D"], ut)
+    torch.cuda.synchronize()
+    assert np.all(_np(out["status"]) == 0)
+    yre, yim, yf = _np(out["y_re"]), _np(out["y_im"]), _np(fw["y"])
+    for h in sample_channels(H, 3, seed=L):
+        h = int(h)
+        c = p.channel(h)
+        ref = O.discretize_channel(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], L)
+        y = O.recurrence(ref["Abar"], ref["Bbar"], c["C"], c["D"], u[:, h, :])
+        assert_rows_close(yre[:, h, :], y.real, what=f"Re y h{h}")
+        assert_rows_close(yim[:, h, :], y.imag, what=f"Im y h{h}")
+        assert_rows_close(yre[:, h, :], yf[:, h, :], what=f"Re y vs ssm_forward h{h}")
+
+
+def test_forward_complex_status_fills_nan():
+    ssm = _ssm()
+    p = I.random_params(9, 3, 6, 1, 50)
+    p.dt[2] = -1.0
+    u = torch.from_numpy(I.random_input(10, 2, 3, 50)).to(DEV)
+    d = _dev(p)
+    out = ssm.forward_complex(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u)
+    torch.cuda.synchronize()
+    assert list(_np(out["status"])) == [0, 0, ssm.ST_INVALID_STEP]
+    for k in ("y_re", "y_im"):
+        y = _np(out[k])
+        assert np.isnan(y[:, 2, :]).all() and np.isfinite(y[:, :2, :]).all()
