@@ -46,7 +46,7 @@ constexpr int kThreads1 = 1024;
 constexpr int kLogE1 = 4, kE1 = 1 << kLogE1, kT1 = kM1 >> kLogE1;  // 16 points per lane, one wave per transform
 static_assert(kT1 == 64, "phase B transforms are one wave each");
 constexpr int kPairs1 = 4;                                          // row pairs per channel
-constexpr int kBufs1 = 2 * kPairs1 + 2;                             // exchange buffers (see the roles)
+constexpr int kBufs1 = 2 * kPairs1 + 1;                             // exchange buffers: waves 0 .. 2 kPairs1
 constexpr int kLdsV1 = lds_padded_size(kM1);
 // spectra stage: four 256-point transforms per spectrum, one wave each
 constexpr int kLogN2 = 8, kN2 = 1 << kLogN2, kLogE2 = 2, kE2 = 1 << kLogE2, kT2 = kN2 >> kLogE2;
@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     __shared__ float2 rootl[M];     // root values
     __shared__ float kl[M];         // real kernel taps (+D), scaled 1/(2M)
     __shared__ float2 khl[2][M];    // cyclic and twisted spectra
-    // exchange buffers: wave 0 and later wave 10 use 0, wave w in 1..9 uses w
+    // exchange buffers: wave w <= 8 uses buffer w for its 1024-point transforms;
+    // the spectra stage (waves 0 and 9-15) uses the start of the array
     __shared__ float2 fbuf[kBufs1][kLdsV1];
     __shared__ int blk_status;
     __shared__ double2 red[kThreads1 / 64];
@@ -195,7 +196,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
 
     // ---- phase B ----
     const TwiddleRegs<kLogM1, kLogE1> tw(twl, kLogM1, t);
-    float2* const mine[1] = {fbuf[wv == 10 ? 0 : min(wv, kBufs1 - 1)]};
+    float2* const mine[1] = {fbuf[min(wv, kBufs1 - 1)]};  // used by waves 0-8 only
     float2 x[1][E];
     const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
 
