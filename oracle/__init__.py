@@ -7,3 +7,4 @@ oracle never imports the library.
 from .ssm_oracle import *  # noqa: F401,F403
 from .ssm_oracle import (OK, SINGULAR_BILINEAR, RESONANT_DIAGONAL, RESONANT_CORRECTION,  # noqa: F401
                          worst_status)
+from . import hippo_oracle  # noqa: F401  (HiPPO generators and their DPLR form)
