@@ -73,6 +73,7 @@ typedef struct ssm_c64 {
 #define SSM_OP_FFTCONV 2
 #define SSM_OP_FORWARD 3
 #define SSM_OP_FORWARD_COMPLEX 4
+#define SSM_OP_HIPPO 5           /* ssm_hippo_dplr: only N is read */
 
 /*
  * Workspace size in bytes that entry point `op` needs for these sizes (Bsz is
@@ -227,6 +228,43 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
              const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
              const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D,
              const float* u, float* y, ssm_c64* x, int32_t* status, void* stream);
+
+/* HiPPO generators for ssm_hippo_dplr. */
+#define SSM_HIPPO_LEGS 0
+#define SSM_HIPPO_LEGT 1
+#define SSM_HIPPO_LAGT 2
+
+/*
+ * DPLR parameters of a HiPPO generator ([RSS] block on the HiPPO generators,
+ * S4 Theorem 1 and App. C.1, HiPPO sec. 2.3 and App. D.1-D.3; [RSS] DPLR
+ * block: NPLR form and the unitary state change).  For the N x N generator G
+ * (LegS, LegT with window theta, or LagT) and the page's similarity S (the
+ * identity, or diag(sqrt(2n+1)) diag((-1)^n) for LegT), S^{-1} G S is split
+ * as (c I + K) - U U^T, K skew-symmetric, with
+ *   LegS: c = -1/2, U [N,1], u_n = sqrt(n + 1/2);
+ *   LagT: c = -1/2, U [N,1], u_n = sqrt(1/2);
+ *   LegT: c = 0, U [N,2], sqrt((2n+1)/theta) in column n mod 2, 0 elsewhere.
+ * With the unitary eigenvectors V of c I + K, the model (G, B, C) becomes
+ * (diag(Lambda) - P P^*, V^* S^{-1} B, V^* S C) under x = S V x~, so the
+ * outputs feed the other entry points with Q = P.
+ *   theta       LegT window (finite, > 0); ignored for LegS and LagT
+ *   B [nb,N], C [nc,N]  input rows (complex64; nb, nc >= 0, may be 0)
+ *   Lambda [N]  eigenvalues c - i mu_j by ascending imaginary part
+ *   P [N,rank]  V^* U, rank 1 (LegS, LagT) or 2 (LegT); column 0 is real and
+ *               non-negative, which fixes each eigenvector's phase
+ *   V [N,N]     eigenvectors as columns, nullable
+ *   Bt [nb,N], Ct [nc,N]  the transformed rows
+ * Arithmetic is float64 on the device (Householder tridiagonalisation of K,
+ * Sturm-count bisection, inverse iteration, back-transformation); outputs
+ * are rounded to complex64.  Sizes: 1 <= N <= 1024 (SSM_ERR_UNSUPPORTED
+ * above).  Workspace: ssm_workspace_bytes(SSM_OP_HIPPO, 0, 0, N, 0, 0, ...),
+ * 32 N^2 bytes plus a little.  No status: for these generators and sizes
+ * adjacent eigenvalues differ by more than 5e-7 of the largest magnitude.
+ */
+int ssm_hippo_dplr(int kind, int64_t N, double theta,
+                   int64_t nb, const ssm_c64* B, int64_t nc, const ssm_c64* C,
+                   ssm_c64* Lambda, ssm_c64* P, ssm_c64* V, ssm_c64* Bt, ssm_c64* Ct,
+                   void* ws, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,6 +1,7 @@
 // C ABI entry points: argument checks, workspace layout, kernel launches.
 // Everything data-dependent happens on the device; the host only validates
 // sizes and pointers and enqueues work on the caller's stream.
+#include <math.h>
 #include <string.h>
 
 #include "common.hpp"
@@ -35,6 +36,10 @@ hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const f
 hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
                        const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
                        const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream);
+int64_t hippo_max_n();
+size_t hippo_workspace_bytes(int64_t N);
+hipError_t launch_hippo(int kind, int64_t N, double theta, int64_t nb, const float2* B, int64_t nc, const float2* C,
+                        float2* Lam, float2* P, float2* V, float2* Bt, float2* Ct, void* ws, hipStream_t stream);
 }  // namespace ssm
 
 using namespace ssm;
@@ -157,6 +162,12 @@ const char* ssm_status_string(int code) {
 
 int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, size_t* bytes) {
     if (!bytes) return SSM_ERR_INVALID_ARGUMENT;
+    if (op == SSM_OP_HIPPO) {
+        if (N < 1) return SSM_ERR_INVALID_ARGUMENT;
+        if (N > hippo_max_n()) return SSM_ERR_UNSUPPORTED;
+        *bytes = hippo_workspace_bytes(N);
+        return SSM_OK;
+    }
     int rc;
     switch (op) {
         case SSM_OP_DISCRETIZE: rc = check_sizes(1, H, N, r, L, true, false); break;
@@ -247,6 +258,23 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
         launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     return device_status(launch_conv(Bsz, H, L, M, u, y, khat, twtab, s));
+}
+
+int ssm_hippo_dplr(int kind, int64_t N, double theta, int64_t nb, const ssm_c64* B, int64_t nc, const ssm_c64* C,
+                   ssm_c64* Lambda, ssm_c64* P, ssm_c64* V, ssm_c64* Bt, ssm_c64* Ct, void* ws, size_t ws_bytes,
+                   void* stream) {
+    if (kind != SSM_HIPPO_LEGS && kind != SSM_HIPPO_LEGT && kind != SSM_HIPPO_LAGT) return SSM_ERR_INVALID_ARGUMENT;
+    if (N < 1 || nb < 0 || nc < 0) return SSM_ERR_INVALID_ARGUMENT;
+    if (kind == SSM_HIPPO_LEGT && !(theta > 0.0 && theta < HUGE_VAL)) return SSM_ERR_INVALID_ARGUMENT;
+    if (N > hippo_max_n() || nb >= kMaxDim || nc >= kMaxDim || nb + nc >= kMaxDim) return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !ws || (nb > 0 && (!B || !Bt)) || (nc > 0 && (!C || !Ct))) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {B, C, Lambda, P, V, Bt, Ct};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(ws, 256)) return SSM_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < hippo_workspace_bytes(N)) return SSM_ERR_WORKSPACE;
+    return device_status(launch_hippo(kind, N, theta, nb, (const float2*)B, nc, (const float2*)C, (float2*)Lambda,
+                                      (float2*)P, (float2*)V, (float2*)Bt, (float2*)Ct, ws, (hipStream_t)stream));
 }
 
 }  // extern "C"

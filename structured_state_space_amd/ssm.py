@@ -29,11 +29,13 @@ ST_RESONANT_CORRECTION = 16
 ST_RESONANT_DIAGONAL = 17
 ST_SINGULAR_BILINEAR = 18
 ST_INVALID_STEP = 19
-OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD, OP_FORWARD_COMPLEX = 0, 1, 2, 3, 4
+OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD, OP_FORWARD_COMPLEX, OP_HIPPO = 0, 1, 2, 3, 4, 5
+HIPPO_LEGS, HIPPO_LEGT, HIPPO_LAGT = 0, 1, 2
+HIPPO_KINDS = {"legs": HIPPO_LEGS, "legt": HIPPO_LEGT, "lagt": HIPPO_LAGT}
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
            "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step",
-           "ssm_forward_complex")
+           "ssm_forward_complex", "ssm_hippo_dplr")
 
 
 class SSMError(RuntimeError):
@@ -70,6 +72,8 @@ def _load():
     lib.ssm_step.restype = i32
     lib.ssm_forward_complex.argtypes = [i64, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     lib.ssm_forward_complex.restype = i32
+    lib.ssm_hippo_dplr.argtypes = [i32, i64, ctypes.c_double, i64, vp, i64, vp] + [vp] * 5 + [vp, sz, vp]
+    lib.ssm_hippo_dplr.restype = i32
     return lib
 
 
@@ -288,6 +292,36 @@ def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):
     if rc != OK:
         raise SSMError("ssm_step", rc)
     return dict(y=y, x=x, status=status)
+
+
+def hippo_dplr(kind, N, theta=1.0, B=None, C=None, want_v=False, device="cuda:0", workspace=None):
+    """ssm_hippo_dplr: DPLR parameters of a HiPPO generator.  kind is "legs",
+    "legt" or "lagt" (or its SSM_HIPPO_* code); B [nb,N] and C [nc,N] are
+    complex64 device tensors or None.  Returns dict(Lambda [N], P [N,rank],
+    V [N,N] or None, Bt [nb,N] or None, Ct [nc,N] or None), all complex64."""
+    code = HIPPO_KINDS[kind] if isinstance(kind, str) else int(kind)
+    dev = torch.device(device)
+    if B is not None:
+        dev = B.device
+        _check(B, "B", torch.complex64, (B.shape[0], N), dev)
+    if C is not None:
+        dev = C.device if B is None else dev
+        _check(C, "C", torch.complex64, (C.shape[0], N), dev)
+    rank = 2 if code == HIPPO_LEGT else 1
+    Lam = torch.empty((N,), dtype=torch.complex64, device=dev)
+    P = torch.empty((N, rank), dtype=torch.complex64, device=dev)
+    V = torch.empty((N, N), dtype=torch.complex64, device=dev) if want_v else None
+    nb = 0 if B is None else B.shape[0]
+    nc = 0 if C is None else C.shape[0]
+    Bt = torch.empty_like(B) if B is not None else None
+    Ct = torch.empty_like(C) if C is not None else None
+    nbytes = workspace_bytes(OP_HIPPO, 0, 0, N, 0, 0)
+    ws = _workspace(nbytes, dev, workspace)
+    rc = lib.ssm_hippo_dplr(code, N, float(theta), nb, _ptr(B), nc, _ptr(C), _ptr(Lam), _ptr(P), _ptr(V), _ptr(Bt),
+                            _ptr(Ct), _ptr(ws), nbytes, _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_hippo_dplr", rc)
+    return dict(Lambda=Lam, P=P, V=V, Bt=Bt, Ct=Ct)
 
 
 def to_device(params, device="cuda:0"):

@@ -164,3 +164,45 @@ def test_step_rejects_before_launch(kw, code):
     a.update(kw)
     assert ssm.lib.ssm_step(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["Lambda"], a["P"], a["Q"], a["B"], a["C"],
                             a["dt"], a["D"], a["u"], a["y"], a["x"], a["status"], None) == code
+
+
+# --------------------------------------------------------------------------
+# ssm_hippo_dplr: sizes and argument checks (host only)
+# --------------------------------------------------------------------------
+def _hippo_ws(N):
+    out = ctypes.c_size_t()
+    rc = ssm.lib.ssm_workspace_bytes(ssm.OP_HIPPO, 0, 0, N, 0, 0, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("N", [1, 2, 64, 256, 1000, 1024])
+def test_hippo_workspace_bytes(N):
+    rc, nbytes = _hippo_ws(N)
+    assert rc == ssm.OK
+    # K and the reflections (float64 N x N each), the phase-fixed eigenvectors
+    # (complex128 N x N), two float64 vectors; each region 256-byte aligned
+    a = lambda v: (v + 255) // 256 * 256
+    assert nbytes == a(8 * N * N) * 2 + a(8 * N) * 2 + a(16 * N * N)
+
+
+def test_hippo_workspace_bytes_rejects():
+    assert _hippo_ws(0)[0] == ssm.ERR_INVALID_ARGUMENT
+    assert _hippo_ws(1025)[0] == ssm.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kind=3), 1), (dict(kind=-1), 1), (dict(N=0), 1), (dict(nb=-1), 1), (dict(nc=-1), 1),
+    (dict(kind=1, theta=0.0), 1), (dict(kind=1, theta=-2.0), 1), (dict(kind=1, theta=float("nan")), 1),
+    (dict(kind=1, theta=float("inf")), 1),
+    (dict(N=1025), 4),
+    (dict(Lambda=None), 1), (dict(P=None), 1), (dict(ws=None), 1),
+    (dict(nb=2, B=None), 1), (dict(nb=2, Bt=None), 1), (dict(nc=3, C=None), 1), (dict(nc=3, Ct=None), 1),
+    (dict(Lambda=FAKE + 4), 1), (dict(ws=FAKE + 64), 1),
+    (dict(ws_bytes=1000), 2),
+])
+def test_hippo_rejects_before_launch(kw, code):
+    a = dict(kind=0, N=8, theta=1.0, nb=0, B=None, nc=0, C=None, Lambda=FAKE, P=FAKE, V=None, Bt=None, Ct=None,
+             ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    assert ssm.lib.ssm_hippo_dplr(a["kind"], a["N"], a["theta"], a["nb"], a["B"], a["nc"], a["C"], a["Lambda"],
+                                  a["P"], a["V"], a["Bt"], a["Ct"], a["ws"], a["ws_bytes"], None) == code

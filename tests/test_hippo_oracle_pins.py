@@ -247,3 +247,15 @@ def test_planted_mistakes_are_caught(monkeypatch, name, mutant):
     _orig[name] = getattr(HO, name)
     monkeypatch.setattr(HO, name, mutant)
     assert not _pins_pass(), f"no pin caught the planted mistake in {name}"
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_eigenvalues_stay_separated_up_to_the_size_cap(kind):
+    # The device solver has no status for close eigenvalues: inverse iteration
+    # keeps the vectors orthogonal to about eps / (relative gap), and for these
+    # generators the relative gap stays above 5e-7 up to N = 1024 (LegS is the
+    # tightest, about 1.07e-6 at 1024), so the vectors are orthogonal to ~1e-9.
+    for N in (256, 512, 1000, 1024):
+        K = HO.normal_part(kind, N, 1.0) - HO.hippo_low_rank(kind, N, 1.0)[0] * np.eye(N)
+        mu = np.sort(np.linalg.eigvalsh(1j * K))
+        assert np.diff(mu).min() > 5e-7 * np.abs(mu).max(), (kind, N)
