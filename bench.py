@@ -31,6 +31,7 @@ METRIC = "channel-steps/sec (B·H·L) for S4 kernel-gen+FFT conv; % HBM/VALU roo
 UNIT = "channel-steps/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3       # MI355X FP32: dense matrix (MFMA) and vector peaks are both 157.3
+PEAK_FP64_TFLOPS = 78.6        # MI355X FP64 vector
 DEFAULT_WORKLOAD = "s4-h256-l1k"
 
 KERNEL_SOURCES = {
@@ -232,6 +233,87 @@ def bench_complex(args, w, p, u, dev):
     return 0
 
 
+HIPPO_METRIC = "HiPPO-to-DPLR constructions/sec (generator, eigenvectors, B and per-channel C)"
+
+
+def hippo_flops(N, rows):
+    """Algorithmic float64 flops of one construction: the tridiagonal reduction
+    of the skew part (4 N^3 / 3, the symmetric count), applying the N - 2
+    reflections to N complex vectors (4 N^3), and projecting `rows` input rows
+    onto the eigenvectors (8 N^2 each); the O(N^2) eigenvalue and
+    inverse-iteration work is left out."""
+    return 4.0 * N ** 3 / 3.0 + 4.0 * N ** 3 + 8.0 * N * N * rows
+
+
+def cpu_baseline_hippo(kind, N, theta, B, C, seconds):
+    """The oracle's construction as it stands, one thread, repeated for about
+    `seconds` (at least once)."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle.hippo_oracle as HO
+    n, t0 = 0, time.perf_counter()
+    with threadpool_limits(limits=1):
+        while True:
+            HO.hippo_dplr(kind, N, theta, B, C)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= seconds:
+                break
+    return {"value": n / el, "unit": "constructions/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} oracle constructions ({kind}, N={N}, {C.shape[0]} C rows, complex128, library "
+                      f"Hermitian eigensolver) in {el:.1f} s, one thread"}
+
+
+def bench_hippo(args, w, dev):
+    """ssm_hippo_dplr for the workload's state size N, with one B row and one C
+    row per channel (H rows)."""
+    import numpy as np
+    import torch
+
+    from structured_state_space_amd import ssm
+    kind, N, H, theta = args.hippo_kind, w.N, w.H, 1.0
+    rng = np.random.default_rng(7)
+    Bn = ((rng.normal(size=(1, N)) + 1j * rng.normal(size=(1, N))) / np.sqrt(2)).astype(np.complex64)
+    Cn = ((rng.normal(size=(H, N)) + 1j * rng.normal(size=(H, N))) / np.sqrt(2)).astype(np.complex64)
+    B, C = torch.from_numpy(Bn).to(dev), torch.from_numpy(Cn).to(dev)
+    ws = torch.empty(ssm.workspace_bytes(ssm.OP_HIPPO, 0, 0, N, 0, 0), dtype=torch.uint8, device=dev)
+
+    def call():
+        return ssm.hippo_dplr(kind, N, theta, B, C, workspace=ws)
+
+    for _ in range(args.warmup):
+        out = call()
+    torch.cuda.synchronize()
+    steps = max(1, min(args.steps, 200))
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        out = call()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_events = start.elapsed_time(end) / steps
+    ms = max(ms_events, 1e3 * t_wall / steps)
+    if not all(bool(torch.isfinite(torch.view_as_real(out[k])).all()) for k in ("Lambda", "P", "Bt", "Ct")):
+        raise RuntimeError("HiPPO construction produced non-finite values")
+    achieved = hippo_flops(N, 1 + H) * 1e-12 / (ms_events * 1e-3)
+    line = {
+        "metric": HIPPO_METRIC, "value": 1e3 / ms, "unit": "constructions/s", "n_gpus": 1, "steps": steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "f64", "data": "synthetic",
+        "config": {"workload": f"hippo-{kind}-n{N}-h{H}", "op": "hippo", "N": N, "C_rows": H, "B_rows": 1},
+        "roofline": {"bound": "alu", "achieved": achieved, "peak": PEAK_FP64_TFLOPS, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_FP64_TFLOPS, "traffic": None, "kernel": "hippo (three launches)"},
+        "ms_per_step_events": ms_events,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_hippo(kind, N, theta, Bn.astype(np.complex128),
+                                                  Cn.astype(np.complex128), min(args.cpu_seconds, 10.0))
+    print(json.dumps(line))
+    return 0
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -242,10 +324,13 @@ def main():
     ap.add_argument("--stage-repeat", type=int, default=10,
                     help="launches of each stage per timing bracket in the per-kernel measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--op", choices=("forward", "step", "complex"), default="forward",
+    ap.add_argument("--hippo-kind", choices=("legs", "legt", "lagt"), default="legs",
+                    help="generator for --op hippo")
+    ap.add_argument("--op", choices=("forward", "step", "complex", "hippo"), default="forward",
                     help="forward: the filter path (the headline); step: the recurrent step mode, "
                          "T = L steps of every sequence per call, the state carried between calls; "
-                         "complex: the filter path with the imaginary output as well")
+                         "complex: the filter path with the imaginary output as well; "
+                         "hippo: DPLR parameters of a HiPPO generator at the workload's N, one C row per channel")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -277,6 +362,8 @@ def main():
         return bench_step(args, w, p, u, dev)
     if args.op == "complex":
         return bench_complex(args, w, p, u, dev)
+    if args.op == "hippo":
+        return bench_hippo(args, w, dev)
     M, n_fft = ssm.transform_lengths(w.L)
     form = ssm.forward_form(w.Bsz, w.H, w.L)
     fused = form == 2
