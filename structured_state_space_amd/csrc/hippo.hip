@@ -13,7 +13,8 @@
 // Only K needs a spectral decomposition:
 //   A  one workgroup reduces K to a skew tridiagonal T = Q^T K Q with
 //      Householder reflections (a skew matrix stays skew, so each trailing
-//      update is the rank-2 step A22 += tau (v p^T - p v^T), p = A22 v);
+//      update is the rank-2 step A22 += tau (v p^T - p v^T), p = A22 v, and
+//      p can be summed down columns: p = -A22^T v);
 //   B  one workgroup per eigenvalue: with the unit diagonal d_{k+1} =
 //      d_k i sign(T_{k+1,k}), D^* (i T) D is the real symmetric tridiagonal
 //      with zero diagonal and off-diagonal |T_{k+1,k}|.  Its eigenvalue mu is
@@ -102,37 +103,53 @@ __device__ double block_max(double v, double* red) {
 // ---- A: skew part and its Householder tridiagonalisation (one workgroup) ----
 // K [N,N] row-major (overwritten), Vh [N,N]: row k holds reflection k on
 // entries k+1 .. N-1 (entry k+1 is 1), e [N]: T_{k+1,k}, tau [N].
+// Step k works on the trailing block of rows and columns k+1 .. N-1 (size m).
+// Each thread owns one column c of it and a residue class of its rows, so
+// every access to K is a coalesced row segment: the product uses skewness,
+// p_c = (A22 v)_c = -sum_i A22[i][c] v_i, from per-class partial sums, and the
+// rank-2 update touches the thread's own column.  The reflector is formed
+// from row k (= -column k).  For N <= kHippoLdsN the matrix stays in LDS.
+constexpr int kHippoLdsN = 64;
+
+template <bool kInLds>
 __global__ __launch_bounds__(1024) void hippo_tridiag_kernel(int kind, int N, double theta, double* __restrict__ K,
                                                              double* __restrict__ Vh, double* __restrict__ e,
                                                              double* __restrict__ tau) {
     __shared__ double v[kHippoMaxN];
     __shared__ double p[kHippoMaxN];
+    __shared__ double part[1024];
     __shared__ double red[16];
+    __shared__ double Kl[kInLds ? kHippoLdsN * kHippoLdsN : 1];
+    double* const A = kInLds ? Kl : K;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, nw = blockDim.x >> 6;
 
     for (int n = wv; n < N; n += nw)
         for (int k = lane; k < N; k += 64)
-            K[(size_t)n * N + k] =
-                0.5 * (transformed_entry(kind, n, k, theta) - transformed_entry(kind, k, n, theta));
+            A[(size_t)n * N + k] = 0.5 * (transformed_entry(kind, n, k, theta) - transformed_entry(kind, k, n, theta));
     __syncthreads();
 
     for (int k = 0; k + 2 < N; ++k) {
-        double part = 0.0;
-        for (int i = k + 2 + tid; i < N; i += blockDim.x) {
-            const double x = K[(size_t)i * N + k];
-            part += x * x;
+        const int c0 = k + 1, m = N - c0;
+        const int wc = (m + 63) & ~63, groups = (int)blockDim.x / wc;
+        const int cl = tid % wc, g = tid / wc, c = c0 + cl;
+        const bool own = g < groups && cl < m;
+        // x_i = A[i][k] = -A[k][i], i >= k + 1
+        double part_sq = 0.0;
+        for (int i = c0 + 1 + tid; i < N; i += blockDim.x) {
+            const double x = A[(size_t)k * N + i];
+            part_sq += x * x;
         }
-        const double sigma = block_sum(part, red);
-        const double alpha = K[(size_t)(k + 1) * N + k];
+        const double sigma = block_sum(part_sq, red);
+        const double alpha = -A[(size_t)k * N + c0];
         double beta = alpha, t = 0.0, scal = 0.0;
         if (sigma != 0.0) {
             const double nrm = sqrt(alpha * alpha + sigma);
             beta = alpha >= 0.0 ? -nrm : nrm;
             t = (beta - alpha) / beta;
-            scal = 1.0 / (alpha - beta);
+            scal = -1.0 / (alpha - beta);
         }
-        for (int i = k + 1 + tid; i < N; i += blockDim.x) {
-            const double vi = i == k + 1 ? 1.0 : K[(size_t)i * N + k] * scal;
+        for (int i = c0 + tid; i < N; i += blockDim.x) {
+            const double vi = i == c0 ? 1.0 : A[(size_t)k * N + i] * scal;
             v[i] = vi;
             Vh[(size_t)k * N + i] = vi;
         }
@@ -142,21 +159,26 @@ __global__ __launch_bounds__(1024) void hippo_tridiag_kernel(int kind, int N, do
         }
         __syncthreads();
         if (t == 0.0) continue;
-        for (int i = k + 1 + wv; i < N; i += nw) {  // p = A22 v, one wave per row
-            double s = 0.0;
-            for (int j = k + 1 + lane; j < N; j += 64) s += K[(size_t)i * N + j] * v[j];
-            s = wave_sum(s);
-            if (lane == 0) p[i] = s;
+        if (own) {  // partial of -(A22^T v)_c over rows i = c0 + g + groups q
+            double sacc = 0.0;
+            for (int i = c0 + g; i < N; i += groups) sacc += A[(size_t)i * N + c] * v[i];
+            part[g * wc + cl] = sacc;
         }
         __syncthreads();
-        for (int i = k + 1 + wv; i < N; i += nw) {  // A22 += t (v p^T - p v^T)
-            const double vi = t * v[i], pi = t * p[i];
-            for (int j = k + 1 + lane; j < N; j += 64) K[(size_t)i * N + j] += vi * p[j] - pi * v[j];
+        if (own && g == 0) {
+            double sacc = 0.0;
+            for (int q = 0; q < groups; ++q) sacc += part[q * wc + cl];
+            p[c] = -sacc;
+        }
+        __syncthreads();
+        if (own) {  // A22 += t (v p^T - p v^T), column c
+            const double tvc = t * v[c], tpc = t * p[c];
+            for (int i = c0 + g; i < N; i += groups) A[(size_t)i * N + c] += v[i] * tpc - p[i] * tvc;
         }
         __syncthreads();
     }
     if (tid == 0 && N >= 2) {
-        e[N - 2] = K[(size_t)(N - 1) * N + (N - 2)];
+        e[N - 2] = A[(size_t)(N - 1) * N + (N - 2)];
         tau[N - 2] = 0.0;
     }
 }
@@ -383,7 +405,10 @@ hipError_t launch_hippo(int kind, int64_t N, double theta, int64_t nb, const flo
     double* tau = (double*)(base + w.tau);
     double2* Vz = (double2*)(base + w.Vz);
     const int n = (int)N, rank = kind == kLegT ? 2 : 1;
-    hipLaunchKernelGGL(hippo_tridiag_kernel, dim3(1), dim3(1024), 0, stream, kind, n, theta, K, Vh, e, tau);
+    if (n <= kHippoLdsN)
+        hipLaunchKernelGGL(hippo_tridiag_kernel<true>, dim3(1), dim3(1024), 0, stream, kind, n, theta, K, Vh, e, tau);
+    else
+        hipLaunchKernelGGL(hippo_tridiag_kernel<false>, dim3(1), dim3(1024), 0, stream, kind, n, theta, K, Vh, e, tau);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     const int threads = (int)((N + 63) / 64 * 64);
