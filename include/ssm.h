@@ -177,9 +177,10 @@ int ssm_forward(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
  *   y_re = (Re K) * u + D u   (as ssm_forward's y)
  *   y_im = (Im K) * u
  * Root values once; then the spectra of Re K (+ D, from the root values, which
- * also writes K) and its convolution, and the spectra of Im K (read back from
- * K) and its convolution.  y_re and y_im [Bsz,H,L] float must not overlap u
- * or each other.  K_out nullable (then K goes to the workspace).  Workspace:
+ * also writes K) and the spectra of Im K (read back from K).  For M <= 1024
+ * and M = 4096 one convolution shares the input's forward transforms between
+ * both spectra sets; other lengths run a convolution for each.  y_re and y_im
+ * [Bsz,H,L] float must not overlap u or each other.  K_out nullable (then K goes to the workspace).  Workspace:
  * ssm_workspace_bytes(SSM_OP_FORWARD_COMPLEX, ...).
  */
 int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,

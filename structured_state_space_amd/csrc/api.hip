@@ -17,6 +17,10 @@ hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int
 hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                        const float2* twtab, hipStream_t stream);
 bool conv_fuses_spectrum(int64_t Bsz, int64_t M);
+bool conv_complex_fits(int64_t M);
+hipError_t launch_conv_complex(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y_re,
+                               float* y_im, const float2* khat_re, const float2* khat_im, const float2* twtab,
+                               hipStream_t stream);
 bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M);
 hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
                          const float2* P, const float2* Q, const float2* Bv, const float2* Ct, const float* dt,
@@ -113,6 +117,11 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.kbuf = off;
         w.kbuf_bytes = (size_t)H * L * sizeof(float2);
         off = align256(off + w.kbuf_bytes);
+        if (conv_complex_fits(M)) {  // both spectra sets live at once for the shared-transform convolution
+            w.khat2 = off;
+            w.khat2_bytes = (size_t)H * 2 * M * sizeof(float2);
+            off = align256(off + w.khat2_bytes);
+        }
     }
     w.total = off;
     return w;
@@ -397,11 +406,21 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
         e = large ? launch_spectrum_large(true, H, L, M, tiles, roots, roots, tstat, nullptr, 1, D, K, status, khat,
                                           twtab, s)
                   : launch_spectrum(true, H, L, M, tiles, roots, tstat, nullptr, 1, D, K, status, khat, twtab, s);
+    const float* Kim = (const float*)K + 1;
+    if (conv_complex_fits(M)) {
+        // the spectra of Im K (the odd floats of K; no skip term) beside those of
+        // Re K + D delta_0, then one convolution sharing the input's transforms
+        float2* khat_im = (float2*)(base + w.khat2);
+        if (e == hipSuccess)
+            e = launch_spectrum(false, H, L, M, 0, nullptr, nullptr, Kim, 2, nullptr, nullptr, nullptr, khat_im,
+                                twtab, s);
+        if (e == hipSuccess) e = launch_conv_complex(Bsz, H, L, M, u, y_re, y_im, khat, khat_im, twtab, s);
+        return device_status(e);
+    }
     if (e == hipSuccess)
         e = large ? launch_conv_large(Bsz, H, L, M, u, y_re, khat, (float2*)(base + w.big), twtab, s)
                   : launch_conv(Bsz, H, L, M, u, y_re, khat, twtab, s);
     // imaginary part: the spectra of Im K (the odd floats of K; no skip term)
-    const float* Kim = (const float*)K + 1;
     if (e == hipSuccess)
         e = large ? launch_spectrum_large(false, H, L, M, 0, nullptr, nullptr, nullptr, Kim, 2, nullptr, nullptr,
                                           nullptr, khat, twtab, s)

@@ -171,11 +171,17 @@ struct FusedSpec {
 // the group of the channel's first row pair also writes K_out and the channel
 // status.  This repeats the kernel transform once per row pair, which pays only
 // where the grid is small and latency-bound.
-template <int LOGM, bool FUSED>
+// CPLX: a complex kernel K = K_r + i K_i given by two spectra sets (khat for
+// K_r + D delta_0, khat_im for K_i).  The input's forward transforms are shared:
+// Z.khat gives (K_r * u_b, K_r * u_{b+1}) into y, Z.khat_im gives
+// (K_i * u_b, K_i * u_{b+1}) into y_im.
+template <int LOGM, bool FUSED, bool CPLX = false>
 __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per_eu(Geo<LOGM>::WAVES))) void conv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
-    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab, FusedSpec fs) {
+    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab, FusedSpec fs,
+    const float2* __restrict__ khat_im = nullptr, float* __restrict__ y_im = nullptr) {
     using Gm = Geo<LOGM>;
+    static_assert(!(CPLX && (FUSED || Gm::SEQ)), "complex kernels take the form with both halves in registers (M <= 8192)");
     constexpr int M = Gm::M, E = Gm::E, T = Gm::T, LOGE = Gm::LOGE, G = Gm::G;
     // fused: three transforms at once (one buffer each, or one shared buffer)
     constexpr int FNBUF = Gm::NBUF == 1 ? 1 : 3;
@@ -214,6 +220,7 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
     };
 
     float2 out[E];
+    float2 outi[CPLX ? E : 1];
     int chst = 0;
     if constexpr (Gm::SEQ && !FUSED) {
         float2* const one[1] = {my};
@@ -304,6 +311,16 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
             }
             fft_multi<2, LOGM, LOGE, false, Gm::NBUF == 1, Gm::LRMAX>(v, bufs, t, tw);
         }
+        float2 wi[CPLX ? 2 : 1][E];
+        if constexpr (CPLX) {  // products with the imaginary part's spectra (read on use)
+            const float2* ki0 = khat_im + (size_t)h * 2 * M;
+            const float2* ki1 = ki0 + M;
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+                wi[0][e] = c_mul(v[0][e], ki0[t + T * e]);
+                wi[1][e] = c_mul(v[1][e], ki1[t + T * e]);
+            }
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             v[0][e] = c_mul(v[0][e], PRE ? k0[PRE ? e : 0] : kh0[t + T * e]);
@@ -313,6 +330,12 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
 #pragma unroll
         for (int e = 0; e < E; ++e)
             out[e] = c_add(v[0][e], c_mul(v[1][e], c_conj(PRE ? tws[PRE ? e : 0] : twtab[t + T * e])));
+        if constexpr (CPLX) {
+            fft_multi<2, LOGM, LOGE, true, Gm::NBUF == 1, Gm::LRMAX>(wi, bufs, t, tw);
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+                outi[e] = c_add(wi[0][e], c_mul(wi[1][e], c_conj(PRE ? tws[PRE ? e : 0] : twtab[t + T * e])));
+        }
     }
 
     if (active) {
@@ -324,6 +347,10 @@ __global__ __launch_bounds__(Geo<LOGM>::THREADS) __attribute__((amdgpu_waves_per
                 // streaming stores (not read again; less end-of-kernel write-back)
                 __builtin_nontemporal_store(out[e].x, &y[row1 + j]);
                 if (has2) __builtin_nontemporal_store(out[e].y, &y[row2 + j]);
+                if constexpr (CPLX) {
+                    __builtin_nontemporal_store(outi[e].x, &y_im[row1 + j]);
+                    if (has2) __builtin_nontemporal_store(outi[e].y, &y_im[row2 + j]);
+                }
             }
         }
     }
@@ -354,6 +381,22 @@ hipError_t conv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float*
     if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
     hipLaunchKernelGGL((conv_kernel<LOGM, false>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream, (int)Bsz,
                        (int)H, (int)L, (int)npb, npairs, remap, u, y, khat, twtab, FusedSpec{});
+    return hipGetLastError();
+}
+
+template <int LOGM>
+hipError_t conv_complex_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y_re, float* y_im,
+                               const float2* khat_re, const float2* khat_im, const float2* twtab,
+                               hipStream_t stream) {
+    using Gm = Geo<LOGM>;
+    const int64_t npb = (Bsz + 1) / 2;
+    const int64_t npairs = npb * H;
+    const int64_t blocks = (npairs + Gm::G - 1) / Gm::G;
+    int remap = 0;
+    if (npb % Gm::G == 0 && H % 8 == 0) remap = (int)(npb / Gm::G);
+    hipLaunchKernelGGL((conv_kernel<LOGM, false, true>), dim3((unsigned)blocks), dim3(Gm::THREADS), 0, stream,
+                       (int)Bsz, (int)H, (int)L, (int)npb, npairs, remap, u, y_re, khat_re, twtab, FusedSpec{},
+                       khat_im, y_im);
     return hipGetLastError();
 }
 
@@ -398,6 +441,27 @@ hipError_t launch_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float
         SSM_CONV_CASE(5) SSM_CONV_CASE(6) SSM_CONV_CASE(7) SSM_CONV_CASE(8) SSM_CONV_CASE(9)
         SSM_CONV_CASE(10) SSM_CONV_CASE(11) SSM_CONV_CASE(12) SSM_CONV_CASE(13) SSM_CONV_CASE(14)
 #undef SSM_CONV_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+// Both parts of a complex kernel in one convolution (shared input transforms),
+// where that measured faster than two convolutions: up to M = 1024 (no spill)
+// and at M = 4096 (a small spill; 10% less added time than a second spectrum
+// and convolution).  At M = 2048 the larger spill made it slower, and from
+// M = 8192 on the two halves do not fit the registers at all.
+bool conv_complex_fits(int64_t M) { return M <= 1024 || M == 4096; }
+
+hipError_t launch_conv_complex(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y_re,
+                               float* y_im, const float2* khat_re, const float2* khat_im, const float2* twtab,
+                               hipStream_t stream) {
+    switch (ilog2_exact(M)) {
+#define SSM_CPLX_CASE(LG) \
+    case LG: return conv_complex_launch<LG>(Bsz, H, L, u, y_re, y_im, khat_re, khat_im, twtab, stream);
+        SSM_CPLX_CASE(0) SSM_CPLX_CASE(1) SSM_CPLX_CASE(2) SSM_CPLX_CASE(3) SSM_CPLX_CASE(4)
+        SSM_CPLX_CASE(5) SSM_CPLX_CASE(6) SSM_CPLX_CASE(7) SSM_CPLX_CASE(8) SSM_CPLX_CASE(9)
+        SSM_CPLX_CASE(10) SSM_CPLX_CASE(11) SSM_CPLX_CASE(12) SSM_CPLX_CASE(13)
+#undef SSM_CPLX_CASE
         default: return hipErrorInvalidValue;
     }
 }

@@ -137,6 +137,11 @@ def test_forward_complex_workspace_and_rejects():
     fwd = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, L)
     cpx = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, 8, H, 64, 1, L)
     assert cpx >= fwd + H * L * 8 and cpx % 256 == 0   # plus the complex kernel [H, L]
+    # where the input's transforms are shared (here M = 1024) the imaginary
+    # part's spectra [H, 2, M] live beside the real part's
+    assert cpx >= fwd + H * L * 8 + H * 2 * 1024 * 8
+    big = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, 8, H, 64, 1, 5000)
+    assert big - ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 5000) < H * 2 * 8192 * 8
 
     def call(r=1, y_re=FAKE, y_im=FAKE, ws_bytes=1 << 30):
         return ssm.lib.ssm_forward_complex(2, 3, 4, r, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, y_re, y_im,

@@ -388,8 +388,13 @@ def test_deterministic_and_linear_and_causal():
 # imaginary part; y_re as ssm_forward's y
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
-    (3, 16, 1, 100, 3, "random"),      # LDS-resident transforms, ragged L
+    (2, 8, 1, 1, 2, "random"),         # L = 1
+    (3, 8, 1, 7, 5, "random"),         # several row pairs per wave, odd batch
+    (3, 16, 1, 100, 3, "random"),      # shared input transforms, ragged L
     (4, 64, 2, 1024, 2, "s4"),
+    (2, 16, 1, 1500, 2, "random"),     # M = 2048: two convolutions
+    (2, 16, 2, 3000, 3, "random"),     # M = 4096: shared transforms, odd batch
+    (2, 8, 1, 5000, 2, "random"),      # M = 8192: two convolutions
     (2, 8, 1, 20000, 1, "random"),     # multi-pass transforms (M = 32768)
 ])
 def test_forward_complex_matches_recurrence(H, N, r, L, Bsz, kind):
