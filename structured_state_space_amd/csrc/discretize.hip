@@ -36,6 +36,134 @@ struct SmallMats {
     int ok;
 };
 
+// C~ = C - (Abar^*)^M C for N <= 64 NPL, with the iteration state in
+// registers: lane l holds states l + 64 e.  Each adjoint step is one DPP
+// reduction of the r sums P^* D^{-*} c, the order r + s solve (the values at
+// Z read by readlane), and the update c <- 2 G^{-*} c - c; no barrier.
+template <int NPL, int RK>
+__device__ void ctilde_in_registers(int N, int s, int M, double alpha, const double2* dinv, const float2* P,
+                                    const float2* Q, size_t hb, const SmallMats& sm, const float2* C, float2* Ct,
+                                    int lane) {
+    const size_t hr = hb * RK;
+    const int n = RK + s;
+    double2 c[NPL], dc[NPL], pc[NPL][RK], qc[NPL][RK];
+    int zs[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        const bool live = j < N;
+        c[e] = live ? z_from(C[hb + j]) : make_double2(0.0, 0.0);
+        const double2 di = live ? dinv[j] : make_double2(0.0, 0.0);
+        dc[e] = z_conj(di);
+        zs[e] = -1;
+        for (int z = 0; z < s; ++z)
+            if (sm.zidx[z] == j) zs[e] = z;
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            const double2 p = live ? z_from(P[hr + (size_t)j * RK + a]) : make_double2(0.0, 0.0);
+            const double2 q = live ? z_from(Q[hr + (size_t)j * RK + a]) : make_double2(0.0, 0.0);
+            pc[e][a] = z_conj(z_mul(p, di));
+            qc[e][a] = z_scale(q, alpha);
+        }
+    }
+    int zl[4], ze[4];  // owner lane and slot of each state in Z (uniform)
+#pragma unroll
+    for (int z = 0; z < 4; ++z) {
+        const int j = z < s ? sm.zidx[z] : 0;
+        zl[z] = j % kWave;
+        ze[z] = j / kWave;
+    }
+    // one adjoint step: the r sums P^* D^{-*} c over the states, then
+    // c <- 2 x - c with x_J = conj(D_J^{-1}) (c_J - alpha Q_J sol), x_Z = sol_Z
+    auto sums = [&](double2 (&rhs)[RK]) {
+        double v[2 * RK];
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            double2 acc = make_double2(0.0, 0.0);
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) acc = z_add(acc, z_mul(pc[e][a], c[e]));
+            v[2 * a] = acc.x;
+            v[2 * a + 1] = acc.y;
+        }
+        wave_allsum_d<2 * RK>(v);
+#pragma unroll
+        for (int a = 0; a < RK; ++a) rhs[a] = make_double2(v[2 * a], v[2 * a + 1]);
+    };
+    if (s == 0) {  // Woodbury form: the r x r inverse in registers
+        double2 mi[RK][RK];
+#pragma unroll
+        for (int a = 0; a < RK; ++a)
+#pragma unroll
+            for (int b = 0; b < RK; ++b) mi[a][b] = sm.Mainv[a * kMaxOrder + b];
+        for (int step = 0; step < M; ++step) {
+            double2 rhs[RK], sol[RK];
+            sums(rhs);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) {
+                double2 acc = make_double2(0.0, 0.0);
+#pragma unroll
+                for (int b = 0; b < RK; ++b) acc = z_add(acc, z_mul(mi[a][b], rhs[b]));
+                sol[a] = acc;
+            }
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) {
+                double2 t = c[e];
+#pragma unroll
+                for (int a = 0; a < RK; ++a) t = z_sub(t, z_mul(qc[e][a], sol[a]));
+                const double2 x = z_mul(dc[e], t);
+                c[e] = make_double2(2.0 * x.x - c[e].x, 2.0 * x.y - c[e].y);
+            }
+        }
+    } else {  // bordered form: order r + s, the inverse read from LDS
+        for (int step = 0; step < M; ++step) {
+            double2 r0[RK];
+            sums(r0);
+            double2 rhs[kMaxOrder], sol[kMaxOrder];
+#pragma unroll
+            for (int a = 0; a < RK; ++a) rhs[a] = r0[a];
+            for (int z = 0; z < s; ++z) {
+                double2 cz = c[0];
+#pragma unroll
+                for (int e = 1; e < NPL; ++e)
+                    if (ze[z] == e) cz = c[e];
+                rhs[RK + z] = make_double2(readlane_d(cz.x, zl[z]), readlane_d(cz.y, zl[z]));
+            }
+            for (int a = 0; a < n; ++a) {
+                double2 acc = make_double2(0.0, 0.0);
+                for (int b = 0; b < n; ++b) acc = z_add(acc, z_mul(sm.Mainv[a * kMaxOrder + b], rhs[b]));
+                sol[a] = acc;
+            }
+#pragma unroll
+            for (int e = 0; e < NPL; ++e) {
+                double2 t = c[e];
+#pragma unroll
+                for (int a = 0; a < RK; ++a) t = z_sub(t, z_mul(qc[e][a], sol[a]));
+                double2 x = z_mul(dc[e], t);
+                for (int z = 0; z < s; ++z)
+                    if (zs[e] == z) x = sol[RK + z];
+                c[e] = make_double2(2.0 * x.x - c[e].x, 2.0 * x.y - c[e].y);
+            }
+        }
+    }
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        if (j < N) Ct[hb + j] = c_from(z_sub(z_from(C[hb + j]), c[e]));
+    }
+}
+
+template <int NPL>
+__device__ void ctilde_dispatch(int N, int r, int s, int M, double alpha, const double2* dinv, const float2* P,
+                                const float2* Q, size_t hb, const SmallMats& sm, const float2* C, float2* Ct,
+                                int lane) {
+    switch (r) {
+        case 1: ctilde_in_registers<NPL, 1>(N, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane); break;
+        case 2: ctilde_in_registers<NPL, 2>(N, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane); break;
+        case 3: ctilde_in_registers<NPL, 3>(N, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane); break;
+        default: ctilde_in_registers<NPL, 4>(N, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane); break;
+    }
+}
+
 __global__ __launch_bounds__(kWave) void discretize_kernel(int N, int r, int M, const float2* __restrict__ Lambda,
                                                            const float2* __restrict__ P, const float2* __restrict__ Q,
                                                            const float2* __restrict__ Bv, const float2* __restrict__ C,
@@ -204,7 +332,15 @@ __global__ __launch_bounds__(kWave) void discretize_kernel(int N, int r, int M, 
     }
 
     // ---- C~ = C - (Abar^*)^M C by M adjoint steps ----
-    if (Ct) {
+    if (Ct && N <= 4 * kWave) {
+        const int s = sm.s;
+        if (N <= kWave)
+            ctilde_dispatch<1>(N, r, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane);
+        else if (N <= 2 * kWave)
+            ctilde_dispatch<2>(N, r, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane);
+        else
+            ctilde_dispatch<4>(N, r, s, M, alpha, dinv, P, Q, hb, sm, C, Ct, lane);
+    } else if (Ct) {
         for (int j = lane; j < N; j += kWave) cst[j] = z_from(C[hb + j]);
         __syncthreads();
         for (int step = 0; step < M; ++step) {
