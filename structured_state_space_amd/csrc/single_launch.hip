@@ -52,6 +52,7 @@ constexpr int kLdsV1 = lds_padded_size(kM1);
 constexpr int kLogN2 = 8, kN2 = 1 << kLogN2, kLogE2 = 2, kE2 = 1 << kLogE2, kT2 = kN2 >> kLogE2;
 static_assert(kT2 == 64 && 4 * kN2 == kM1, "spectra split: four one-wave transforms of M/4 points");
 static_assert(8 * lds_padded_size(kN2) <= kBufs1 * kLdsV1, "spectra split: exchange buffers");
+static_assert(4 * lds_padded_size(kN2) <= 2 * kM1, "kernel transform split: exchange buffers in the spectra array");
 
 // a * (-i)^k for a runtime k in 0..3
 __device__ __forceinline__ float2 c_mul_mi_pow(float2 a, int k) {
@@ -200,15 +201,29 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     float2 x[1][E];
     const float invM = 1.0f / (float)M, sc = 1.0f / (float)(2 * M);
 
-    // B1
-    if (wv == 0) {
+    // B1: the kernel's inverse transform, as the forward transform of the
+    // conjugated root values, split over waves 0, 9, 10 and 11 (one per SIMD
+    // beside the z-waves' two each) by one radix-4 step of decimation in
+    // frequency, as in B2; their exchange buffers are the spectra array,
+    // which B2 fills only after the barrier
+    if (wv == 0 || (wv >= 9 && wv <= 11)) {
+        const int q = wv == 0 ? 0 : wv - 8;
+        float2 w[1][kE2];
 #pragma unroll
-        for (int e = 0; e < E; ++e) x[0][e] = c_conj(rootl[t + T * e]);
-        fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(x, mine, t, tw);
+        for (int e = 0; e < kE2; ++e) {
+            const int m = t + kT2 * e;
+            float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-            const int j = t + T * e;
-            const float2 kv = c_scale(c_conj(x[0][e]), invM);
+            for (int pp = 0; pp < 4; ++pp) acc = c_add(acc, c_mul_mi_pow(c_conj(rootl[m + kN2 * pp]), (pp * q) & 3));
+            w[0][e] = c_mul(acc, table_root(twl, kLogM1, (m * q) & (M - 1), kLogM1));
+        }
+        const TwiddleRegs<kLogN2, kLogE2> tw2(twl, kLogM1, t);
+        float2* const buf2[1] = {&khl[0][0] + q * lds_padded_size(kN2)};
+        fft_multi<1, kLogN2, kLogE2, false, false, kLogE2, true>(w, buf2, t, tw2);
+#pragma unroll
+        for (int e = 0; e < kE2; ++e) {
+            const int j = 4 * (t + kT2 * e) + q;
+            const float2 kv = c_scale(c_conj(w[0][e]), invM);
             if (K_out && j < L) K_out[(size_t)h * L + j] = chst ? c_nan() : kv;
             float kr = j < L ? kv.x : 0.0f;
             if (j == 0 && D) kr += D[h];
