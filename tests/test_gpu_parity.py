@@ -155,6 +155,37 @@ def test_discretize_matches_dense(idx, nsample):
 # ---------------------------------------------------------------------------
 # the whole path from the conventional C: discretize -> forward
 # ---------------------------------------------------------------------------
+@pytest.mark.parametrize("N,r,L,bordered", [
+    (100, 1, 4, True),       # states in registers, bordered form
+    (200, 2, 300, False),    # states in registers, four per lane
+    (300, 1, 100, False),    # LDS loop (N > 256)
+    (700, 2, 3, True),       # LDS loop, bordered form
+])
+def test_discretize_register_and_lds_paths(N, r, L, bordered):
+    """C~ by the register-resident adjoint steps (N <= 256) and by the LDS loop
+    (larger N), each with and without an exactly zero d_j, against the dense
+    oracle."""
+    ssm = _ssm()
+    H = 2
+    p = I.random_params(N + 7 * r, H, N, r, L, dt_range=(1.0, 1.0) if bordered else (1e-3, 1e-1),
+                        lambda_kind="random")
+    if bordered:
+        # d_j = 1 - (dt/2) lambda_j = 0 exactly for one state of each channel
+        # (dt = 1).  Abar then has an eigenvalue of order -4/delta, delta ~ 1/N
+        # from the low-rank term, so C~ is checked over a few adjoint steps only.
+        p.Lambda[:, N // 3] = np.complex64(2.0)
+    d = _dev(p)
+    out = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L)
+    assert np.all(_np(out["status"]) == 0)
+    Bbar, Ct = _np(out["Bbar"]), _np(out["Ctilde"])
+    for h in range(H):
+        c = p.channel(h)
+        ref = O.discretize_channel(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], float(c["dt"]), L)
+        assert ref["status"] == O.OK
+        assert_rows_close(Bbar[h][None], ref["Bbar"][None], what=f"Bbar h{h}")
+        assert_rows_close(Ct[h][None], ref["Ctilde"][None], what=f"C~ h{h}")
+
+
 @pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 12), (2, 3), (3, 3), (4, 2)])
 def test_forward_end_to_end(idx, nsample):
     ssm = _ssm()
