@@ -27,13 +27,15 @@ __device__ __forceinline__ double2 wave_sum(double2 v) {
 
 // K float64 sums over the 64 lanes at once, returned to every lane: DPP
 // exchanges of both 32-bit halves within each row of 16 lanes (quad_perm
-// [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror), then the four row
-// sums by readlane.  Stage by stage over the K values, so their exchanges
-// fill each other's wait states.
-template <int CTRL>
+// [1,0,3,2] and [2,3,0,1], row_half_mirror, row_mirror), then the rows
+// combined by the row broadcasts (lane 15 of rows 0 and 2 into rows 1 and 3,
+// then lane 31 into rows 2 and 3; rows outside the mask add zero), and the
+// total read from lane 63.  Stage by stage over the K values, so their
+// exchanges fill each other's wait states.
+template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ double dpp_get_d(double v) {
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, 0xF, 0xF, false);
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, 0xF, 0xF, false);
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(v), CTRL, ROWS, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(v), CTRL, ROWS, 0xF, false);
     return __hiloint2double(hi, lo);
 }
 __device__ __forceinline__ double readlane_d(double v, int l) {
@@ -51,8 +53,11 @@ __device__ __forceinline__ void wave_allsum_d(double (&v)[K]) {
 #pragma unroll
     for (int i = 0; i < K; ++i) v[i] += dpp_get_d<0x140>(v[i]);
 #pragma unroll
-    for (int i = 0; i < K; ++i)
-        v[i] = (readlane_d(v[i], 0) + readlane_d(v[i], 16)) + (readlane_d(v[i], 32) + readlane_d(v[i], 48));
+    for (int i = 0; i < K; ++i) v[i] += dpp_get_d<0x142, 0xA>(v[i]);  // row_bcast:15 into rows 1 and 3
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get_d<0x143, 0xC>(v[i]);  // row_bcast:31 into rows 2 and 3
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = readlane_d(v[i], 63);
 }
 
 __device__ __forceinline__ double z_abs1(double2 a) { return fabs(a.x) + fabs(a.y); }

@@ -45,11 +45,13 @@ struct StepSetup {
 
 // Sum over the 64 lanes, returned to every lane: DPP exchanges within each
 // row of 16 lanes (quad_perm [1,0,3,2] and [2,3,0,1], row_half_mirror,
-// row_mirror: each lane then holds its row's sum), then the four row sums by
-// readlane.  No LDS round trip (the shuffle-based sum takes six).
-template <int CTRL>
+// row_mirror: each lane then holds its row's sum), then the rows combined by
+// the row broadcasts (lane 15 of rows 0 and 2 added into rows 1 and 3, then
+// lane 31 into rows 2 and 3), so lane 63 holds the total, read once.  No LDS
+// round trip (the shuffle-based sum takes six).
+template <int CTRL, int ROWS = 0xF>
 __device__ __forceinline__ float dpp_get(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
 // K values at once, stage by stage, so that the exchanges of different values
 // fill each other's wait states
@@ -64,13 +66,11 @@ __device__ __forceinline__ void wave_allsum(float (&v)[K]) {
 #pragma unroll
     for (int i = 0; i < K; ++i) v[i] += dpp_get<0x140>(v[i]);  // row_mirror
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-        const float s0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 0));
-        const float s1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 16));
-        const float s2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 32));
-        const float s3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 48));
-        v[i] = (s0 + s1) + (s2 + s3);
-    }
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x142, 0xA>(v[i]);  // row_bcast:15 into rows 1 and 3
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x143, 0xC>(v[i]);  // row_bcast:31 into rows 2 and 3
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
 }
 
 // The recurrence for one sequence: T steps from the state xs (updated in
