@@ -27,6 +27,7 @@
 // Eigenvalues come out by ascending imaginary part, Lambda_j = c - i mu_j.
 #include <cfloat>
 
+#include "bilinear.hpp"
 #include "common.hpp"
 
 namespace ssm {
@@ -61,8 +62,9 @@ __device__ __forceinline__ double similarity_entry(int kind, int n) {
 }
 
 __device__ __forceinline__ double wave_sum(double v) {
-    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    double a[1] = {v};
+    wave_allsum_d<1>(a);  // DPP exchanges, no LDS round trip
+    return a[0];
 }
 
 // sum over the workgroup, returned to every thread (two barriers)
@@ -79,8 +81,9 @@ __device__ double block_sum(double v, double* red) {
 
 __device__ double2 block_sum2(double2 v, double2* red) {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
-    v.x = wave_sum(v.x);
-    v.y = wave_sum(v.y);
+    double a[2] = {v.x, v.y};
+    wave_allsum_d<2>(a);
+    v = make_double2(a[0], a[1]);
     if (lane == 0) red[wv] = v;
     __syncthreads();
     double2 s = make_double2(0.0, 0.0);
@@ -271,8 +274,10 @@ __global__ __launch_bounds__(1024) void hippo_eigvec_kernel(int kind, int N, dou
                 }
             }
             u0[N - 1] = dd;
-            for (int i = 0; i < N; ++i)
+            for (int i = 0; i < N; ++i) {  // floored pivots, kept as reciprocals for the solves
                 if (fabs(u0[i]) < floor_piv) u0[i] = u0[i] < 0.0 ? -floor_piv : floor_piv;
+                u0[i] = 1.0 / u0[i];
+            }
             // start vector: a fixed low-discrepancy sequence in (-1, 1)
             for (int i = 0; i < N; ++i) {
                 const double f = (double)(i + 1) * 0.6180339887498949 + (double)j * 0.7548776662466927;
@@ -287,9 +292,9 @@ __global__ __launch_bounds__(1024) void hippo_eigvec_kernel(int kind, int N, dou
                     }
                     y[i + 1] -= lm[i] * y[i];
                 }
-                y[N - 1] /= u0[N - 1];
-                y[N - 2] = (y[N - 2] - u1[N - 2] * y[N - 1]) / u0[N - 2];
-                for (int i = N - 3; i >= 0; --i) y[i] = (y[i] - u1[i] * y[i + 1] - u2[i] * y[i + 2]) / u0[i];
+                y[N - 1] *= u0[N - 1];
+                y[N - 2] = (y[N - 2] - u1[N - 2] * y[N - 1]) * u0[N - 2];
+                for (int i = N - 3; i >= 0; --i) y[i] = (y[i] - u1[i] * y[i + 1] - u2[i] * y[i + 2]) * u0[i];
                 double m = 0.0;
                 for (int i = 0; i < N; ++i) m = fmax(m, fabs(y[i]));
                 const double s = 1.0 / m;
@@ -316,10 +321,14 @@ __global__ __launch_bounds__(1024) void hippo_eigvec_kernel(int kind, int N, dou
             default: z = make_double2(0.0, -yi); break;
         }
     }
+    // each reflection's entries are fetched one step ahead, so the load is in
+    // flight during the previous step's sums
+    double vnext = (N >= 3 && tid > N - 3 && tid < N) ? Vh[(size_t)(N - 3) * N + tid] : 0.0;
     for (int k = N - 3; k >= 0; --k) {
         const double t = tau[k];
+        const double vi = vnext;
+        vnext = (k > 0 && tid > k - 1 && tid < N) ? Vh[(size_t)(k - 1) * N + tid] : 0.0;
         if (t == 0.0) continue;
-        const double vi = (tid > k && tid < N) ? Vh[(size_t)k * N + tid] : 0.0;
         const double2 s = block_sum2(z_scale(z, vi), red2);
         z = z_sub(z, z_scale(s, t * vi));
     }
