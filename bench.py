@@ -450,6 +450,30 @@ def main():
                 "unit": phases[dom]["unit"], "frac": phases[dom]["frac"], "traffic": traffic, "kernel": dom}
     troof_ms = (alg["cauchy"]["work"] / (PEAK_FP32_TFLOPS * 1e12) + alg["conv"]["work"] / (PEAK_HBM_GBS * 1e9)) * 1e3
 
+    # the other entry points of the path as whole calls: the kernel alone
+    # (root values and its transform) and the convolution with a given kernel
+    def timed(fn, reps=20):
+        for _ in range(3):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ws_kg = torch.empty(ssm.workspace_bytes(ssm.OP_KERNEL_GEN, 1, w.H, w.N, w.r, w.L), dtype=torch.uint8,
+                        device=dev)
+    ws_fc = torch.empty(ssm.workspace_bytes(ssm.OP_FFTCONV, w.Bsz, w.H, w.N, w.r, w.L), dtype=torch.uint8,
+                        device=dev)
+    Kbuf = torch.empty((w.H, w.L), dtype=torch.complex64, device=dev)
+    y2 = torch.empty_like(ut)
+    kg = lambda: ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], w.L, workspace=ws_kg)
+    calls_ms = {"kernel_gen": timed(kg)}
+    Kbuf.copy_(kg()["K"])
+    calls_ms["fftconv"] = timed(lambda: ssm.fftconv(Kbuf, ut, d["D"], y=y2, workspace=ws_fc))
+
     value = w.Bsz * w.H * w.L / (ms_per_step * 1e-3)
     out = {
         "metric": METRIC, "value": value, "unit": UNIT, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -462,6 +486,7 @@ def main():
         "composite_roofline_frac": troof_ms / ms_per_step,
         "ms_per_step_events": ms_events,
         "discretize_ms_off_timer": discretize_ms,
+        "calls_ms_off_timer": calls_ms,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, p, u, args.cpu_seconds)
