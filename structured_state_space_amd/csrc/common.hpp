@@ -76,8 +76,9 @@ struct WsLayout {
 
 constexpr int kMaxLdsLogM = 14;           // M <= 16384 runs LDS-resident
 // multi-pass convolution: row pairs per chunk (the intermediate of a chunk,
-// 2 M complex per pair, is the workspace's multi-pass region)
-constexpr int kConvChunkPairs = 64;
+// 2 M complex per pair, is the workspace's multi-pass region; 128 pairs at
+// M = 65536 is 134 MB, inside the 256 MB Infinity Cache)
+constexpr int kConvChunkPairs = 128;
 constexpr int kMaxLogM = 16;              // M <= 65536 supported
 constexpr int kCauchyThreads = 256;
 
