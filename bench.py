@@ -180,10 +180,66 @@ def bench_step(args, w, p, u, dev):
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None, "kernel": "step"},
         "ms_per_step_events": ms_events,
     }
+    # the two-call form: the set-up once, then only the recurrence per call
+    prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+
+    def call_prepared():
+        ssm.step_prepared(prep, d["D"], ut, x=x, y=y, status=status)
+
+    for _ in range(args.warmup):
+        call_prepared()
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        call_prepared()
+    end.record()
+    torch.cuda.synchronize()
+    if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
+        raise RuntimeError("prepared step mode produced a nonzero status or non-finite output")
+    line["prepared"] = {"ms_per_call_events": start.elapsed_time(end) / steps,
+                        "decode_us_per_call_graph": decode_us(ssm, d, prep, u, w, dev)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_step(w, p, u, args.cpu_seconds)
     print(json.dumps(line))
     return 0
+
+
+def decode_us(ssm, d, prep, u, w, dev, calls=50):
+    """Streaming decode: microseconds per call of T = 1, 8 and 64 steps, for
+    ssm_step and ssm_step_prepared, each captured `calls` times in one HIP
+    graph and the graph replayed (launch overhead of the graph included)."""
+    import torch
+    x = torch.zeros((w.Bsz, w.H, w.N), dtype=torch.complex64, device=dev)
+    st = torch.empty(w.H, dtype=torch.int32, device=dev)
+    out = {}
+    for T in (1, 8, 64):
+        ut = torch.from_numpy(u[:, :, :T].copy()).to(dev)
+        y = torch.empty_like(ut)
+        fns = {"step": lambda: ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], ut, x=x, y=y,
+                                        status=st),
+               "prepared": lambda: ssm.step_prepared(prep, d["D"], ut, x=x, y=y, status=st)}
+        for name, f in fns.items():
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                f()
+            torch.cuda.current_stream().wait_stream(s)
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for _ in range(calls):
+                    f()
+            g.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            out[f"{name}_T{T}"] = e0.elapsed_time(e1) / calls * 1e3
+            if int(st.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
+                raise RuntimeError(f"decode timing: {name} at T = {T} gave a nonzero status or non-finite output")
+    return out
 
 
 def bench_complex(args, w, p, u, dev):

@@ -66,6 +66,8 @@ typedef struct ssm_c64 {
 #define SSM_ST_RESONANT_DIAGONAL 17   /* s(z_k) - lambda_j exactly zero, [RSS] Alg. 1 */
 #define SSM_ST_SINGULAR_BILINEAR 18   /* G = I - dt A/2 singular, [RSS] recurrent solver */
 #define SSM_ST_INVALID_STEP 19        /* dt not finite and positive ([RSS] requires dt > 0) */
+#define SSM_ST_UNPREPARED 20          /* ssm_step_prepared: the channel's block was not written by
+                                         ssm_step_prepare for these N and r */
 
 /* Operation ids for ssm_workspace_bytes. */
 #define SSM_OP_DISCRETIZE 0
@@ -74,6 +76,7 @@ typedef struct ssm_c64 {
 #define SSM_OP_FORWARD 3
 #define SSM_OP_FORWARD_COMPLEX 4
 #define SSM_OP_HIPPO 5           /* ssm_hippo_dplr: only N is read */
+#define SSM_OP_STEP_PREPARED 6   /* the constants ssm_step_prepare writes: H, N, r read */
 
 /*
  * Workspace size in bytes that entry point `op` needs for these sizes (Bsz is
@@ -229,6 +232,34 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
              const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
              const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D,
              const float* u, float* y, ssm_c64* x, int32_t* status, void* stream);
+
+/*
+ * The recurrent mode in two calls, for streaming decode: the channel set-up
+ * of ssm_step (d, the Woodbury or bordered core's inverse, Bbar; float64,
+ * rounded to float32) runs once per parameter set in ssm_step_prepare, which
+ * writes the float32 constants of the recurrence to a caller-owned buffer of
+ * ssm_workspace_bytes(SSM_OP_STEP_PREPARED, 0, H, N, r, 0) bytes.  Each
+ * ssm_step_prepared call then runs only the recurrence ([RSS] DPLR block and
+ * recurrent solver of Alg. 1, as ssm_step) from those constants: its y and x
+ * equal ssm_step's on the same parameters, bit for bit.
+ *   ssm_step_prepare:  parameters as ssm_step; prep [prep_bytes] device,
+ *                      written; status [H] int32, nullable (as ssm_step's
+ *                      set-up statuses).  A failing channel's block records
+ *                      its status.
+ *   ssm_step_prepared: prep as written by ssm_step_prepare for the same H, N
+ *                      and r (read only; one buffer may serve any number of
+ *                      calls and streams); D, u, y, x, status as ssm_step.
+ *                      A channel whose block holds a failure status gets it
+ *                      again with NaN y and x; a block not written for these
+ *                      N and r gives SSM_ST_UNPREPARED, NaN y and x.
+ * Sizes as ssm_step.  SSM_ERR_WORKSPACE when prep_bytes is below the size.
+ */
+int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, const ssm_c64* P,
+                     const ssm_c64* Q, const ssm_c64* B, const ssm_c64* C, const float* dt,
+                     void* prep, size_t prep_bytes, int32_t* status, void* stream);
+int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
+                      const void* prep, size_t prep_bytes, const float* D, const float* u,
+                      float* y, ssm_c64* x, int32_t* status, void* stream);
 
 /* HiPPO generators for ssm_hippo_dplr. */
 #define SSM_HIPPO_LEGS 0

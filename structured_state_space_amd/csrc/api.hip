@@ -40,6 +40,13 @@ hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const f
 hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
                        const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
                        const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream);
+size_t step_prepared_channel_bytes(int64_t N, int64_t r);
+hipError_t launch_step_prepare(int64_t H, int64_t N, int64_t r, const float2* Lambda, const float2* P,
+                               const float2* Q, const float2* Bv, const float2* C, const float* dt, uint8_t* prep,
+                               int32_t* status, hipStream_t stream);
+hipError_t launch_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
+                                const float* D, const float* u, float* y, float2* x, int32_t* status,
+                                hipStream_t stream);
 int64_t hippo_max_n();
 size_t hippo_workspace_bytes(int64_t N);
 hipError_t launch_hippo(int kind, int64_t N, double theta, int64_t nb, const float2* B, int64_t nc, const float2* C,
@@ -165,6 +172,7 @@ const char* ssm_status_string(int code) {
         case SSM_ST_RESONANT_DIAGONAL: return "resonant-diagonal";
         case SSM_ST_SINGULAR_BILINEAR: return "singular-bilinear-matrix";
         case SSM_ST_INVALID_STEP: return "invalid-step";
+        case SSM_ST_UNPREPARED: return "unprepared";
         default: return "unknown code";
     }
 }
@@ -175,6 +183,12 @@ int ssm_workspace_bytes(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, in
         if (N < 1) return SSM_ERR_INVALID_ARGUMENT;
         if (N > hippo_max_n()) return SSM_ERR_UNSUPPORTED;
         *bytes = hippo_workspace_bytes(N);
+        return SSM_OK;
+    }
+    if (op == SSM_OP_STEP_PREPARED) {
+        if (H < 1 || N < 1 || r < 1) return SSM_ERR_INVALID_ARGUMENT;
+        if (r > kMaxR || N > kMaxNStep || H >= kMaxDim) return SSM_ERR_UNSUPPORTED;
+        *bytes = (size_t)H * step_prepared_channel_bytes(N, r);
         return SSM_OK;
     }
     int rc;
@@ -448,6 +462,37 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const ssm_
     return device_status(launch_step(Bsz, H, N, r, T, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                      (const float2*)B, (const float2*)C, dt, D, u, y, (float2*)x, status,
                                      (hipStream_t)stream));
+}
+
+int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                     const ssm_c64* B, const ssm_c64* C, const float* dt, void* prep, size_t prep_bytes,
+                     int32_t* status, void* stream) {
+    if (H < 1 || N < 1 || r < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (r > kMaxR || N > kMaxNStep || H >= kMaxDim) return SSM_ERR_UNSUPPORTED;
+    if (!Lambda || !P || !Q || !B || !C || !dt || !prep) return SSM_ERR_INVALID_ARGUMENT;
+    const void* c64s[] = {Lambda, P, Q, B, C};
+    for (const void* p : c64s)
+        if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(dt, 4) || !aligned(status, 4) || !aligned(prep, 256)) return SSM_ERR_INVALID_ARGUMENT;
+    if (prep_bytes < (size_t)H * step_prepared_channel_bytes(N, r)) return SSM_ERR_WORKSPACE;
+    return device_status(launch_step_prepare(H, N, r, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
+                                             (const float2*)B, (const float2*)C, dt, (uint8_t*)prep, status,
+                                             (hipStream_t)stream));
+}
+
+int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const void* prep, size_t prep_bytes,
+                      const float* D, const float* u, float* y, ssm_c64* x, int32_t* status, void* stream) {
+    if (Bsz < 1 || H < 1 || N < 1 || r < 1 || T < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (r > kMaxR || N > kMaxNStep || H >= kMaxDim || Bsz >= kMaxDim || T >= kMaxDim || Bsz * H >= kMaxDim ||
+        Bsz * H > ((int64_t)1 << 62) / T)
+        return SSM_ERR_UNSUPPORTED;
+    if (!prep || !u || !y || !x) return SSM_ERR_INVALID_ARGUMENT;
+    if (!aligned(prep, 256) || !aligned(x, 8) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) ||
+        !aligned(status, 4))
+        return SSM_ERR_INVALID_ARGUMENT;
+    if (prep_bytes < (size_t)H * step_prepared_channel_bytes(N, r)) return SSM_ERR_WORKSPACE;
+    return device_status(launch_step_prepared(Bsz, H, N, r, T, (const uint8_t*)prep, D, u, y, (float2*)x, status,
+                                              (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -193,28 +193,25 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
     }
 }
 
+// The channel set-up in float64: d^{-1}, the zero set Z, Mb^{-1} (into sm, as
+// float32 in sm.Mbf) and Bbar = G^{-1} (dt B), then the float32 per-state
+// constants of the recurrence in the lane's registers.  Returns the channel's
+// status (uniform over the wave); on a failure the constants are not formed.
+// States past N get zero constants.
 template <int NPL, int RK>
-__global__ __launch_bounds__(kWave) void step_kernel(int Bsz, int H, int N, int T, const float2* __restrict__ Lambda,
-                                                     const float2* __restrict__ P, const float2* __restrict__ Q,
-                                                     const float2* __restrict__ Bv, const float2* __restrict__ C,
-                                                     const float* __restrict__ dt, const float* __restrict__ D,
-                                                     const float* __restrict__ u, float* __restrict__ y,
-                                                     float2* __restrict__ x, int32_t* __restrict__ status) {
-    __shared__ StepSetup sm;
-    const int seq = blockIdx.x;  // = b * H + h, the row order of u, y and x
-    const int h = seq % H;
-    const int b = seq / H;
-    const int lane = threadIdx.x;
+__device__ __forceinline__ int channel_setup(int h, int N, int lane, const float2* __restrict__ Lambda,
+                                             const float2* __restrict__ P, const float2* __restrict__ Q,
+                                             const float2* __restrict__ Bv, const float2* __restrict__ C,
+                                             const float* __restrict__ dt, StepSetup& sm, float2 (&qd)[NPL][RK],
+                                             float2 (&pa)[NPL][RK], float2 (&dv)[NPL], float2 (&cc)[NPL],
+                                             float2 (&bb)[NPL]) {
     const size_t hb = (size_t)h * N;
     const size_t hr = hb * RK;
-    const size_t xb = (size_t)seq * N;
-    const size_t ub = (size_t)seq * T;
     const float dtf = dt[h];
     int st = SSM_ST_OK;
     if (!(dtf > 0.0f) || !(dtf <= FLT_MAX)) st = SSM_ST_INVALID_STEP;
     const double dtv = (double)dtf, alpha = 0.5 * dtv;
 
-    // ---- set-up in float64: d^{-1}, Z, Mb^{-1} ----
     double2 dinv[NPL];
     if (lane == 0) sm.s = 0;
     __syncthreads();
@@ -275,94 +272,254 @@ __global__ __launch_bounds__(kWave) void step_kernel(int Bsz, int H, int N, int 
         __syncthreads();
         if (!sm.ok) st = SSM_ST_SINGULAR_BILINEAR;
     }
-    if (st != SSM_ST_OK) {
-        const float nanf = __builtin_nanf("");
-        for (int t = lane; t < T; t += kWave) y[ub + t] = nanf;
-        for (int j = lane; j < N; j += kWave) x[xb + j] = c_nan();
-        if (lane == 0 && b == 0 && status) status[h] = st;
-        return;
-    }
+    if (st != SSM_ST_OK) return st;
     const int n = RK + s;
 
-    // ---- Bbar = G^{-1} (dt B) (float64), and the per-state constants ----
-    float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL], xs[NPL];
-    int zs[NPL];  // slot in Z of the state, or -1
-    {
-        double2 rhs[kMaxOrder];
-        for (int a = 0; a < RK; ++a) {
-            double2 acc = make_double2(0.0, 0.0);
-#pragma unroll
-            for (int e = 0; e < NPL; ++e) {
-                const int j = lane + kWave * e;
-                if (j < N) {
-                    const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
-                    acc = z_add(acc, z_mul(z_mul(z_conj(q), dinv[e]), z_scale(z_from(Bv[hb + j]), dtv)));
-                }
-            }
-            rhs[a] = wave_sum(acc);
-        }
-        for (int zz = 0; zz < s; ++zz) rhs[RK + zz] = z_scale(z_from(Bv[hb + sm.zidx[zz]]), dtv);
-        double2 sol[kMaxOrder];
-        for (int i = 0; i < n; ++i) {
-            double2 acc = make_double2(0.0, 0.0);
-            for (int j = 0; j < n; ++j) acc = z_add(acc, z_mul(sm.Mbinv[i * kMaxOrder + j], rhs[j]));
-            sol[i] = acc;
-        }
+    // Bbar = G^{-1} (dt B) (float64), and the per-state constants
+    double2 rhs[kMaxOrder];
+    for (int a = 0; a < RK; ++a) {
+        double2 acc = make_double2(0.0, 0.0);
 #pragma unroll
         for (int e = 0; e < NPL; ++e) {
             const int j = lane + kWave * e;
-            zs[e] = -1;
-            for (int zz = 0; zz < s; ++zz)
-                if (sm.zidx[zz] == j) zs[e] = zz;
-            double2 bbar = make_double2(0.0, 0.0);
-            dv[e] = c_from(dinv[e]);
-            cc[e] = make_float2(0.0f, 0.0f);
-            xs[e] = make_float2(0.0f, 0.0f);
-#pragma unroll
-            for (int a = 0; a < RK; ++a) {
-                qd[e][a] = make_float2(0.0f, 0.0f);
-                pa[e][a] = make_float2(0.0f, 0.0f);
-            }
             if (j < N) {
-                cc[e] = c_conj(C[hb + j]);
-                xs[e] = x[xb + j];
-                if (zs[e] < 0) {
-                    double2 tb = z_scale(z_from(Bv[hb + j]), dtv);
-#pragma unroll
-                    for (int a = 0; a < RK; ++a) {
-                        const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
-                        const double2 p = z_from(P[hr + (size_t)j * RK + a]);
-                        qd[e][a] = c_from(z_mul(z_conj(q), dinv[e]));
-                        pa[e][a] = c_from(z_scale(z_mul(dinv[e], p), alpha));
-                        tb = z_sub(tb, z_scale(z_mul(p, sol[a]), alpha));
-                    }
-                    bbar = z_mul(dinv[e], tb);
-                } else {
-                    for (int zz = 0; zz < s; ++zz)
-                        if (zs[e] == zz) bbar = sol[RK + zz];
-                }
+                const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
+                acc = z_add(acc, z_mul(z_mul(z_conj(q), dinv[e]), z_scale(z_from(Bv[hb + j]), dtv)));
             }
-            bb[e] = c_from(bbar);
         }
+        rhs[a] = wave_sum(acc);
     }
-    const float Dh = D ? D[h] : 0.0f;
-    // Z's owners: lane and register slot of each state in Z (uniform)
-    int zl[kMaxRank], ze[kMaxRank];
+    for (int zz = 0; zz < s; ++zz) rhs[RK + zz] = z_scale(z_from(Bv[hb + sm.zidx[zz]]), dtv);
+    double2 sol[kMaxOrder];
+    for (int i = 0; i < n; ++i) {
+        double2 acc = make_double2(0.0, 0.0);
+        for (int j = 0; j < n; ++j) acc = z_add(acc, z_mul(sm.Mbinv[i * kMaxOrder + j], rhs[j]));
+        sol[i] = acc;
+    }
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        int zslot = -1;
+        for (int zz = 0; zz < s; ++zz)
+            if (sm.zidx[zz] == j) zslot = zz;
+        double2 bbar = make_double2(0.0, 0.0);
+        dv[e] = c_from(dinv[e]);
+        cc[e] = make_float2(0.0f, 0.0f);
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            qd[e][a] = make_float2(0.0f, 0.0f);
+            pa[e][a] = make_float2(0.0f, 0.0f);
+        }
+        if (j < N) {
+            cc[e] = c_conj(C[hb + j]);
+            if (zslot < 0) {
+                double2 tb = z_scale(z_from(Bv[hb + j]), dtv);
+#pragma unroll
+                for (int a = 0; a < RK; ++a) {
+                    const double2 q = z_from(Q[hr + (size_t)j * RK + a]);
+                    const double2 p = z_from(P[hr + (size_t)j * RK + a]);
+                    qd[e][a] = c_from(z_mul(z_conj(q), dinv[e]));
+                    pa[e][a] = c_from(z_scale(z_mul(dinv[e], p), alpha));
+                    tb = z_sub(tb, z_scale(z_mul(p, sol[a]), alpha));
+                }
+                bbar = z_mul(dinv[e], tb);
+            } else {
+                for (int zz = 0; zz < s; ++zz)
+                    if (zslot == zz) bbar = sol[RK + zz];
+            }
+        }
+        bb[e] = c_from(bbar);
+    }
+    return SSM_ST_OK;
+}
+
+// Z's bookkeeping for the recurrence: the slot in Z of each of the lane's
+// states (or -1), and the owner lane and register slot of each state in Z
+template <int NPL>
+__device__ __forceinline__ void z_slots(int lane, int s, const int* zidx, int (&zs)[NPL], int (&zl)[kMaxRank],
+                                        int (&ze)[kMaxRank]) {
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        zs[e] = -1;
+        for (int zz = 0; zz < s; ++zz)
+            if (zidx[zz] == j) zs[e] = zz;
+    }
 #pragma unroll
     for (int zz = 0; zz < kMaxRank; ++zz) {
-        const int j = zz < s ? sm.zidx[zz] : 0;
+        const int j = zz < s ? zidx[zz] : 0;
         zl[zz] = j % kWave;
         ze[zz] = j / kWave;
     }
+}
+
+// A failing channel: NaN outputs and state for the sequence
+__device__ __forceinline__ void fail_sequence(int lane, int N, int T, size_t ub, size_t xb, float* __restrict__ y,
+                                              float2* __restrict__ x) {
+    const float nanf = __builtin_nanf("");
+    for (int t = lane; t < T; t += kWave) y[ub + t] = nanf;
+    for (int j = lane; j < N; j += kWave) x[xb + j] = c_nan();
+}
+
+template <int NPL, int RK>
+__global__ __launch_bounds__(kWave) void step_kernel(int Bsz, int H, int N, int T, const float2* __restrict__ Lambda,
+                                                     const float2* __restrict__ P, const float2* __restrict__ Q,
+                                                     const float2* __restrict__ Bv, const float2* __restrict__ C,
+                                                     const float* __restrict__ dt, const float* __restrict__ D,
+                                                     const float* __restrict__ u, float* __restrict__ y,
+                                                     float2* __restrict__ x, int32_t* __restrict__ status) {
+    __shared__ StepSetup sm;
+    const int seq = blockIdx.x;  // = b * H + h, the row order of u, y and x
+    const int h = seq % H;
+    const int b = seq / H;
+    const int lane = threadIdx.x;
+    const size_t xb = (size_t)seq * N;
+    const size_t ub = (size_t)seq * T;
+
+    float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL], xs[NPL];
+    const int st = channel_setup<NPL, RK>(h, N, lane, Lambda, P, Q, Bv, C, dt, sm, qd, pa, dv, cc, bb);
+    if (st != SSM_ST_OK) {
+        fail_sequence(lane, N, T, ub, xb, y, x);
+        if (lane == 0 && b == 0 && status) status[h] = st;
+        return;
+    }
+    const int s = sm.s;
+    int zs[NPL], zl[kMaxRank], ze[kMaxRank];
+    z_slots<NPL>(lane, s, sm.zidx, zs, zl, ze);
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        xs[e] = j < N ? x[xb + j] : make_float2(0.0f, 0.0f);
+    }
+    const float Dh = D ? D[h] : 0.0f;
 
     // ---- the recurrence (float32) ----
     // channels with no zero d_j (the usual case) take the Woodbury form, whose
     // r x r inverse stays in registers; the bordered form re-reads its order
     // r + s inverse from LDS every step
     if (s == 0)
-        recur<NPL, RK, 0>(T, lane, ub, n, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, 0>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
     else
-        recur<NPL, RK, kMaxRank>(T, lane, ub, n, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        if (j < N) x[xb + j] = xs[e];
+    }
+    if (lane == 0 && b == 0 && status) status[h] = SSM_ST_OK;
+}
+
+// ---- prepared constants ----
+// One block of step_prepared_channel_bytes(N, r) bytes per channel:
+//   int32[16] header: magic, N, r, status, s, zidx[4], zeros;
+//   float2[kMaxOrder^2] Mb^{-1} (zero outside the order r + s block);
+//   float2 arrays of 64 NPL slots each (state j at slot j, zero past N):
+//   d^{-1}, conj(C), Bbar, then Q^* D^{-1} and alpha D^{-1} P column by column.
+// The set-up writes them once per parameter set; the recurrence then reads
+// the same float32 values its one-call form keeps in registers.
+constexpr int32_t kPrepMagic = 0x50534d53;
+constexpr int kPrepHeaderWords = 16;
+constexpr size_t kPrepConstOffset = kPrepHeaderWords * 4 + kMaxOrder * kMaxOrder * sizeof(float2);
+
+template <int NPL, int RK>
+__global__ __launch_bounds__(kWave) void step_prepare_kernel(int N, const float2* __restrict__ Lambda,
+                                                             const float2* __restrict__ P,
+                                                             const float2* __restrict__ Q,
+                                                             const float2* __restrict__ Bv,
+                                                             const float2* __restrict__ C,
+                                                             const float* __restrict__ dt, uint8_t* __restrict__ prep,
+                                                             size_t chan_bytes, int32_t* __restrict__ status) {
+    __shared__ StepSetup sm;
+    const int h = blockIdx.x;
+    const int lane = threadIdx.x;
+    float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL];
+    const int st = channel_setup<NPL, RK>(h, N, lane, Lambda, P, Q, Bv, C, dt, sm, qd, pa, dv, cc, bb);
+    uint8_t* base = prep + (size_t)h * chan_bytes;
+    const int s = st == SSM_ST_OK ? sm.s : 0;
+    if (lane < kPrepHeaderWords) {
+        int32_t w = 0;
+        if (lane == 0) w = kPrepMagic;
+        if (lane == 1) w = N;
+        if (lane == 2) w = RK;
+        if (lane == 3) w = st;
+        if (lane == 4) w = s;
+        if (lane >= 5 && lane < 5 + kMaxRank && lane - 5 < s) w = sm.zidx[lane - 5];
+        reinterpret_cast<int32_t*>(base)[lane] = w;
+    }
+    if (lane == 0 && status) status[h] = st;
+    if (st != SSM_ST_OK) return;
+    {  // kMaxOrder^2 = 64 entries, one per lane
+        const int i = lane / kMaxOrder, j = lane % kMaxOrder, n = RK + s;
+        reinterpret_cast<float2*>(base + kPrepHeaderWords * 4)[lane] =
+            i < n && j < n ? sm.Mbf[lane] : make_float2(0.0f, 0.0f);
+    }
+    float2* cst = reinterpret_cast<float2*>(base + kPrepConstOffset);
+    constexpr int NS = NPL * kWave;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        cst[j] = dv[e];
+        cst[NS + j] = cc[e];
+        cst[2 * NS + j] = bb[e];
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            cst[(3 + a) * NS + j] = qd[e][a];
+            cst[(3 + RK + a) * NS + j] = pa[e][a];
+        }
+    }
+}
+
+template <int NPL, int RK>
+__global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, int N, int T,
+                                                              const uint8_t* __restrict__ prep, size_t chan_bytes,
+                                                              const float* __restrict__ D,
+                                                              const float* __restrict__ u, float* __restrict__ y,
+                                                              float2* __restrict__ x, int32_t* __restrict__ status) {
+    __shared__ float2 mbf[kMaxOrder * kMaxOrder];
+    const int seq = blockIdx.x;  // = b * H + h
+    const int h = seq % H;
+    const int b = seq / H;
+    const int lane = threadIdx.x;
+    const size_t xb = (size_t)seq * N;
+    const size_t ub = (size_t)seq * T;
+    const uint8_t* base = prep + (size_t)h * chan_bytes;
+    const int32_t* hd = reinterpret_cast<const int32_t*>(base);
+    int st = hd[3];
+    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
+    if (st != SSM_ST_OK) {
+        fail_sequence(lane, N, T, ub, xb, y, x);
+        if (lane == 0 && b == 0 && status) status[h] = st;
+        return;
+    }
+    const int s = min(max(hd[4], 0), RK);
+    int zidx[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(hd[5 + zz], 0), NPL * kWave - 1);
+    mbf[lane] = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4)[lane];
+    const float2* cst = reinterpret_cast<const float2*>(base + kPrepConstOffset);
+    constexpr int NS = NPL * kWave;
+    float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL], xs[NPL];
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+        const int j = lane + kWave * e;
+        dv[e] = cst[j];
+        cc[e] = cst[NS + j];
+        bb[e] = cst[2 * NS + j];
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            qd[e][a] = cst[(3 + a) * NS + j];
+            pa[e][a] = cst[(3 + RK + a) * NS + j];
+        }
+        xs[e] = j < N ? x[xb + j] : make_float2(0.0f, 0.0f);
+    }
+    int zs[NPL], zl[kMaxRank], ze[kMaxRank];
+    z_slots<NPL>(lane, s, zidx, zs, zl, ze);
+    const float Dh = D ? D[h] : 0.0f;
+    __syncthreads();
+    if (s == 0)
+        recur<NPL, RK, 0>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+    else
+        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
         const int j = lane + kWave * e;
@@ -386,6 +543,36 @@ hipError_t launch_npl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, c
     return hipErrorInvalidValue;
 }
 
+template <int NPL>
+hipError_t launch_prepare_npl(int64_t H, int64_t N, int64_t r, const float2* Lambda, const float2* P, const float2* Q,
+                              const float2* Bv, const float2* C, const float* dt, uint8_t* prep, size_t chan_bytes,
+                              int32_t* status, hipStream_t stream) {
+#define SSM_PREP(RK)                                                                                             \
+    if (r == RK) {                                                                                               \
+        hipLaunchKernelGGL((step_prepare_kernel<NPL, RK>), dim3((unsigned)H), dim3(kWave), 0, stream, (int)N,    \
+                           Lambda, P, Q, Bv, C, dt, prep, chan_bytes, status);                                   \
+        return hipGetLastError();                                                                                \
+    }
+    SSM_PREP(1) SSM_PREP(2) SSM_PREP(3) SSM_PREP(4)
+#undef SSM_PREP
+    return hipErrorInvalidValue;
+}
+
+template <int NPL>
+hipError_t launch_prepared_npl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
+                               size_t chan_bytes, const float* D, const float* u, float* y, float2* x,
+                               int32_t* status, hipStream_t stream) {
+#define SSM_PREPD(RK)                                                                                            \
+    if (r == RK) {                                                                                               \
+        hipLaunchKernelGGL((step_prepared_kernel<NPL, RK>), dim3((unsigned)(Bsz * H)), dim3(kWave), 0, stream,   \
+                           (int)Bsz, (int)H, (int)N, (int)T, prep, chan_bytes, D, u, y, x, status);              \
+        return hipGetLastError();                                                                                \
+    }
+    SSM_PREPD(1) SSM_PREPD(2) SSM_PREPD(3) SSM_PREPD(4)
+#undef SSM_PREPD
+    return hipErrorInvalidValue;
+}
+
 }  // namespace
 
 constexpr int64_t kStepMaxN = 4 * kWave;
@@ -396,6 +583,33 @@ hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, 
     if (N <= kWave) return launch_npl<1>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
     if (N <= 2 * kWave) return launch_npl<2>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
     if (N <= kStepMaxN) return launch_npl<4>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+    return hipErrorInvalidValue;
+}
+
+// Bytes of one channel's prepared constants (a multiple of 256)
+size_t step_prepared_channel_bytes(int64_t N, int64_t r) {
+    const int64_t npl = N <= kWave ? 1 : N <= 2 * kWave ? 2 : 4;
+    const size_t raw = kPrepConstOffset + sizeof(float2) * (size_t)(npl * kWave) * (size_t)(3 + 2 * r);
+    return (raw + 255) / 256 * 256;
+}
+
+hipError_t launch_step_prepare(int64_t H, int64_t N, int64_t r, const float2* Lambda, const float2* P,
+                               const float2* Q, const float2* Bv, const float2* C, const float* dt, uint8_t* prep,
+                               int32_t* status, hipStream_t stream) {
+    const size_t cb = step_prepared_channel_bytes(N, r);
+    if (N <= kWave) return launch_prepare_npl<1>(H, N, r, Lambda, P, Q, Bv, C, dt, prep, cb, status, stream);
+    if (N <= 2 * kWave) return launch_prepare_npl<2>(H, N, r, Lambda, P, Q, Bv, C, dt, prep, cb, status, stream);
+    if (N <= kStepMaxN) return launch_prepare_npl<4>(H, N, r, Lambda, P, Q, Bv, C, dt, prep, cb, status, stream);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
+                                const float* D, const float* u, float* y, float2* x, int32_t* status,
+                                hipStream_t stream) {
+    const size_t cb = step_prepared_channel_bytes(N, r);
+    if (N <= kWave) return launch_prepared_npl<1>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
+    if (N <= 2 * kWave) return launch_prepared_npl<2>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
+    if (N <= kStepMaxN) return launch_prepared_npl<4>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
     return hipErrorInvalidValue;
 }
 

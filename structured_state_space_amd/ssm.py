@@ -29,13 +29,15 @@ ST_RESONANT_CORRECTION = 16
 ST_RESONANT_DIAGONAL = 17
 ST_SINGULAR_BILINEAR = 18
 ST_INVALID_STEP = 19
+ST_UNPREPARED = 20
 OP_DISCRETIZE, OP_KERNEL_GEN, OP_FFTCONV, OP_FORWARD, OP_FORWARD_COMPLEX, OP_HIPPO = 0, 1, 2, 3, 4, 5
+OP_STEP_PREPARED = 6
 HIPPO_LEGS, HIPPO_LEGT, HIPPO_LAGT = 0, 1, 2
 HIPPO_KINDS = {"legs": HIPPO_LEGS, "legt": HIPPO_LEGT, "lagt": HIPPO_LAGT}
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
            "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step",
-           "ssm_forward_complex", "ssm_hippo_dplr")
+           "ssm_forward_complex", "ssm_hippo_dplr", "ssm_step_prepare", "ssm_step_prepared")
 
 
 class SSMError(RuntimeError):
@@ -70,6 +72,10 @@ def _load():
     lib.ssm_forward_profiled.restype = i32
     lib.ssm_step.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
     lib.ssm_step.restype = i32
+    lib.ssm_step_prepare.argtypes = [i64, i64, i64] + [vp] * 7 + [sz, vp, vp]
+    lib.ssm_step_prepare.restype = i32
+    lib.ssm_step_prepared.argtypes = [i64, i64, i64, i64, i64, vp, sz] + [vp] * 6
+    lib.ssm_step_prepared.restype = i32
     lib.ssm_forward_complex.argtypes = [i64, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     lib.ssm_forward_complex.restype = i32
     lib.ssm_hippo_dplr.argtypes = [i32, i64, ctypes.c_double, i64, vp, i64, vp] + [vp] * 5 + [vp, sz, vp]
@@ -291,6 +297,54 @@ def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):
                       _ptr(y), _ptr(x), _ptr(status), _stream(dev))
     if rc != OK:
         raise SSMError("ssm_step", rc)
+    return dict(y=y, x=x, status=status)
+
+
+def step_prepare(Lambda, P, Q, B, C, dt, prep=None, status=None):
+    """ssm_step_prepare: the per-channel set-up of the step mode, once per
+    parameter set.  Returns dict(prep (uint8 device buffer of the float32
+    constants), status [H] i32, H, N, r), which step_prepared takes."""
+    H, N, r, dev = _params(Lambda, P, Q, B, C, dt)
+    nbytes = workspace_bytes(OP_STEP_PREPARED, 0, H, N, r, 0)
+    if prep is None:
+        prep = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    elif not (isinstance(prep, torch.Tensor) and prep.dtype == torch.uint8 and prep.is_cuda and prep.device == dev
+              and prep.is_contiguous() and prep.numel() >= nbytes):
+        raise ValueError(f"prep: expected a contiguous uint8 tensor of at least {nbytes} bytes on {dev}")
+    if status is None:
+        status = torch.empty((H,), dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, (H,), dev)
+    rc = lib.ssm_step_prepare(H, N, r, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(C), _ptr(dt), _ptr(prep),
+                              prep.numel(), _ptr(status), _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_step_prepare", rc)
+    return dict(prep=prep, status=status, H=H, N=N, r=r)
+
+
+def step_prepared(prepared, D, u, x=None, y=None, status=None):
+    """ssm_step_prepared: T steps of the recurrence from the state x (zeros
+    when None) with the constants of step_prepare's result `prepared`;
+    returns dict(y, x, status) as step does, with the same values."""
+    prep, H, N, r = prepared["prep"], prepared["H"], prepared["N"], prepared["r"]
+    dev = prep.device
+    Bsz, H2, T = u.shape
+    if H2 != H:
+        raise ValueError("u: channel count does not match the prepared constants")
+    _check(u, "u", torch.float32, (Bsz, H, T), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    if x is None:
+        x = torch.zeros((Bsz, H, N), dtype=torch.complex64, device=dev)
+    _check(x, "x", torch.complex64, (Bsz, H, N), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", torch.float32, (Bsz, H, T), dev)
+    if status is None:
+        status = torch.empty((H,), dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, (H,), dev)
+    rc = lib.ssm_step_prepared(Bsz, H, N, r, T, _ptr(prep), prep.numel(), _ptr(D), _ptr(u), _ptr(y), _ptr(x),
+                               _ptr(status), _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_step_prepared", rc)
     return dict(y=y, x=x, status=status)
 
 

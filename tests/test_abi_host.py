@@ -60,6 +60,7 @@ def test_status_strings():
     assert ssm.status_string(ssm.ST_RESONANT_CORRECTION) == O.RESONANT_CORRECTION
     assert ssm.status_string(ssm.ST_SINGULAR_BILINEAR) == O.SINGULAR_BILINEAR
     assert ssm.status_string(ssm.OK) == "ok"
+    assert ssm.status_string(ssm.ST_UNPREPARED) == "unprepared"
     assert ssm.status_string(12345) == "unknown code"
 
 
@@ -169,6 +170,71 @@ def test_step_rejects_before_launch(kw, code):
     a.update(kw)
     assert ssm.lib.ssm_step(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["Lambda"], a["P"], a["Q"], a["B"], a["C"],
                             a["dt"], a["D"], a["u"], a["y"], a["x"], a["status"], None) == code
+
+
+# --------------------------------------------------------------------------
+# ssm_step_prepare / ssm_step_prepared: the constants' size and argument checks
+
+
+@pytest.mark.parametrize("N,r,npl", [(1, 1, 1), (64, 1, 1), (65, 2, 2), (128, 4, 2), (129, 1, 4), (256, 4, 4)])
+def test_step_prepared_bytes(N, r, npl):
+    """Per channel: a 64-byte header, the order-8 inverse (64 complex64), then
+    3 + 2r arrays of 64 npl complex64, rounded up to 256 bytes."""
+    raw = 64 + 64 * 8 + (3 + 2 * r) * 64 * npl * 8
+    per = -(-raw // 256) * 256
+    for H in (1, 7):
+        assert ssm.workspace_bytes(ssm.OP_STEP_PREPARED, 0, H, N, r, 0) == H * per
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, 4, 1), ssm.ERR_INVALID_ARGUMENT),
+    ((3, 0, 1), ssm.ERR_INVALID_ARGUMENT),
+    ((3, 4, 0), ssm.ERR_INVALID_ARGUMENT),
+    ((3, 257, 1), ssm.ERR_UNSUPPORTED),
+    ((3, 4, 5), ssm.ERR_UNSUPPORTED),
+])
+def test_step_prepared_bytes_rejects(args, code):
+    H, N, r = args
+    with pytest.raises(ssm.SSMError) as e:
+        ssm.workspace_bytes(ssm.OP_STEP_PREPARED, 0, H, N, r, 0)
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(H=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(N=257), ssm.ERR_UNSUPPORTED),
+    (dict(r=5), ssm.ERR_UNSUPPORTED),
+    (dict(Q=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(prep=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(prep=FAKE + 64), ssm.ERR_INVALID_ARGUMENT),   # constants not 256-byte aligned
+    (dict(dt=FAKE + 2), ssm.ERR_INVALID_ARGUMENT),
+    (dict(prep_bytes=3 * 3328 - 1), ssm.ERR_WORKSPACE),  # 3 channels need 3 x 3328 bytes at N = 4, r = 1
+])
+def test_step_prepare_rejects_before_launch(kw, code):
+    a = dict(H=3, N=4, r=1, Lambda=FAKE, P=FAKE, Q=FAKE, B=FAKE, C=FAKE, dt=FAKE, prep=FAKE, prep_bytes=1 << 20,
+             status=None)
+    a.update(kw)
+    assert ssm.lib.ssm_step_prepare(a["H"], a["N"], a["r"], a["Lambda"], a["P"], a["Q"], a["B"], a["C"], a["dt"],
+                                    a["prep"], a["prep_bytes"], a["status"], None) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(Bsz=0), ssm.ERR_INVALID_ARGUMENT),
+    (dict(N=257), ssm.ERR_UNSUPPORTED),
+    (dict(r=5), ssm.ERR_UNSUPPORTED),
+    (dict(prep=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(prep=FAKE + 8), ssm.ERR_INVALID_ARGUMENT),
+    (dict(x=FAKE + 4), ssm.ERR_INVALID_ARGUMENT),
+    (dict(y=None), ssm.ERR_INVALID_ARGUMENT),
+    (dict(prep_bytes=3327), ssm.ERR_WORKSPACE),
+])
+def test_step_prepared_rejects_before_launch(kw, code):
+    a = dict(Bsz=2, H=1, N=4, r=1, T=16, prep=FAKE, prep_bytes=1 << 20, D=None, u=FAKE, y=FAKE, x=FAKE,
+             status=None)
+    a.update(kw)
+    assert ssm.lib.ssm_step_prepared(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["prep"], a["prep_bytes"], a["D"],
+                                     a["u"], a["y"], a["x"], a["status"], None) == code
 
 
 # --------------------------------------------------------------------------

@@ -123,3 +123,33 @@ def test_step_replays_continue_the_stream():
         assert torch.equal(y, ref["y"]), f"replay {k}"
         assert torch.equal(x, xr), f"state after replay {k}"
     assert np.isfinite(y.cpu().numpy()).all()
+
+
+def test_step_prepared_replays():
+    """The prepared form under capture: one ssm_step_prepare outside the
+    graph, a captured ssm_step_prepared of T = 1 (a decode step) replayed as
+    a stream; each replay equals an eager ssm_step call bit for bit."""
+    ssm = _ssm()
+    H, N, r, Bsz = 8, 64, 1, 2
+    p = I.random_params(61, H, N, r, 16)
+    d = ssm.to_device(p, DEV)
+    prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+    steps = [torch.from_numpy(I.random_input(62 + k, Bsz, H, 1)).to(DEV) for k in range(5)]
+    u = steps[0].clone()
+    x = torch.zeros((Bsz, H, N), dtype=torch.complex64, device=DEV)
+    y = torch.empty_like(u)
+    status = torch.empty(H, dtype=torch.int32, device=DEV)
+    call = lambda: ssm.step_prepared(prep, d["D"], u, x=x, y=y, status=status)
+    g, _ = _capture(call)
+    x.zero_()
+    xr = torch.zeros_like(x)
+    for k in range(5):
+        u.copy_(steps[k])
+        _eager_noise()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], steps[k], x=xr)
+        torch.cuda.synchronize()
+        assert torch.equal(y, ref["y"]), f"replay {k}"
+        assert torch.equal(x, xr), f"state after replay {k}"
+    assert int(status.abs().max()) == 0
