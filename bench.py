@@ -145,6 +145,13 @@ def bench_step(args, w, p, u, dev):
 
     from structured_state_space_amd import ssm
     d = ssm.to_device(p, dev)
+    if args.decode == "only":  # short calls alone (a kernel trace of them stays apart from the long calls)
+        prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+        print(json.dumps({"metric": "microseconds per streaming-decode call from a HIP graph", "unit": "us",
+                          "higher_is_better": False, "n_gpus": 1, "data": "synthetic",
+                          "config": {"workload": w.name, "op": "step", "H": w.H, "N": w.N, "r": w.r, "batch": w.Bsz},
+                          "decode_us_per_call_graph": decode_us(ssm, d, prep, u, w, dev)}))
+        return 0
     ut = torch.from_numpy(u).to(dev)
     x = torch.zeros((w.Bsz, w.H, w.N), dtype=torch.complex64, device=dev)
     y = torch.empty_like(ut)
@@ -196,8 +203,9 @@ def bench_step(args, w, p, u, dev):
     torch.cuda.synchronize()
     if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
         raise RuntimeError("prepared step mode produced a nonzero status or non-finite output")
-    line["prepared"] = {"ms_per_call_events": start.elapsed_time(end) / steps,
-                        "decode_us_per_call_graph": decode_us(ssm, d, prep, u, w, dev)}
+    line["prepared"] = {"ms_per_call_events": start.elapsed_time(end) / steps}
+    if args.decode == "graph":
+        line["prepared"]["decode_us_per_call_graph"] = decode_us(ssm, d, prep, u, w, dev)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_step(w, p, u, args.cpu_seconds)
     print(json.dumps(line))
@@ -380,6 +388,9 @@ def main():
     ap.add_argument("--stage-repeat", type=int, default=10,
                     help="launches of each stage per timing bracket in the per-kernel measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", choices=("graph", "none", "only"), default="graph",
+                    help="--op step: also time short decode calls from a HIP graph (graph), skip them (none), "
+                         "or time only them (only)")
     ap.add_argument("--hippo-kind", choices=("legs", "legt", "lagt"), default="legs",
                     help="generator for --op hippo")
     ap.add_argument("--op", choices=("forward", "step", "complex", "hippo"), default="forward",
