@@ -187,23 +187,26 @@ def bench_step(args, w, p, u, dev):
                      "frac": achieved / PEAK_FP32_TFLOPS, "traffic": None, "kernel": "step"},
         "ms_per_step_events": ms_events,
     }
-    # the two-call form: the set-up once, then only the recurrence per call
+    # the two-call form: the set-up once, then only the recurrence per call,
+    # in the layout the library picks (0) and in each fixed one
     prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+    line["prepared"] = {}
+    for lanes in ((0, 16, 64) if w.N <= 64 else (0, 64)):
+        def call_prepared():
+            ssm.step_prepared(prep, d["D"], ut, x=x, y=y, status=status, lanes=lanes)
 
-    def call_prepared():
-        ssm.step_prepared(prep, d["D"], ut, x=x, y=y, status=status)
-
-    for _ in range(args.warmup):
-        call_prepared()
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(steps):
-        call_prepared()
-    end.record()
-    torch.cuda.synchronize()
-    if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
-        raise RuntimeError("prepared step mode produced a nonzero status or non-finite output")
-    line["prepared"] = {"ms_per_call_events": start.elapsed_time(end) / steps}
+        for _ in range(args.warmup):
+            call_prepared()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(steps):
+            call_prepared()
+        end.record()
+        torch.cuda.synchronize()
+        if int(status.abs().max()) != 0 or not bool(torch.isfinite(y).all()):
+            raise RuntimeError("prepared step mode produced a nonzero status or non-finite output")
+        key = "ms_per_call_events" if lanes == 0 else f"ms_per_call_events_lanes{lanes}"
+        line["prepared"][key] = start.elapsed_time(end) / steps
     if args.decode == "graph":
         line["prepared"]["decode_us_per_call_graph"] = decode_us(ssm, d, prep, u, w, dev)
     if not args.no_cpu_baseline:

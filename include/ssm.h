@@ -240,8 +240,7 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
  * writes the float32 constants of the recurrence to a caller-owned buffer of
  * ssm_workspace_bytes(SSM_OP_STEP_PREPARED, 0, H, N, r, 0) bytes.  Each
  * ssm_step_prepared call then runs only the recurrence ([RSS] DPLR block and
- * recurrent solver of Alg. 1, as ssm_step) from those constants: its y and x
- * equal ssm_step's on the same parameters, bit for bit.
+ * recurrent solver of Alg. 1, as ssm_step) from those constants.
  *   ssm_step_prepare:  parameters as ssm_step; prep [prep_bytes] device,
  *                      written; status [H] int32, nullable (as ssm_step's
  *                      set-up statuses).  A failing channel's block records
@@ -252,6 +251,17 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
  *                      A channel whose block holds a failure status gets it
  *                      again with NaN y and x; a block not written for these
  *                      N and r gives SSM_ST_UNPREPARED, NaN y and x.
+ *   lanes              lanes of a wave per sequence: 64 (one sequence per
+ *                      wave: ssm_step's recurrence, so y and x equal its own
+ *                      bit for bit), 16 (N <= 64 only: four sequences per
+ *                      wave, fewer instructions per step, the sums taken in
+ *                      another order, so the float32 results differ from
+ *                      ssm_step's by rounding), or 0 (chosen per call: 16
+ *                      when N <= 64, T >= 8 and Bsz * H is at least three
+ *                      sequences per SIMD of the device, else 64).  A stream
+ *                      split into calls repeats one call's results bit for
+ *                      bit when every call takes the same layout; pass 16 or
+ *                      64 to fix it.  Anything else: SSM_ERR_INVALID_ARGUMENT.
  * Sizes as ssm_step.  SSM_ERR_WORKSPACE when prep_bytes is below the size.
  */
 int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, const ssm_c64* P,
@@ -259,7 +269,7 @@ int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, con
                      void* prep, size_t prep_bytes, int32_t* status, void* stream);
 int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
                       const void* prep, size_t prep_bytes, const float* D, const float* u,
-                      float* y, ssm_c64* x, int32_t* status, void* stream);
+                      float* y, ssm_c64* x, int32_t* status, int32_t lanes, void* stream);
 
 /* HiPPO generators for ssm_hippo_dplr. */
 #define SSM_HIPPO_LEGS 0

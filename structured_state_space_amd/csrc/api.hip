@@ -45,7 +45,7 @@ hipError_t launch_step_prepare(int64_t H, int64_t N, int64_t r, const float2* La
                                const float2* Q, const float2* Bv, const float2* C, const float* dt, uint8_t* prep,
                                int32_t* status, hipStream_t stream);
 hipError_t launch_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
-                                const float* D, const float* u, float* y, float2* x, int32_t* status,
+                                const float* D, const float* u, float* y, float2* x, int32_t* status, int lanes,
                                 hipStream_t stream);
 int64_t hippo_max_n();
 size_t hippo_workspace_bytes(int64_t N);
@@ -481,8 +481,10 @@ int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, con
 }
 
 int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const void* prep, size_t prep_bytes,
-                      const float* D, const float* u, float* y, ssm_c64* x, int32_t* status, void* stream) {
+                      const float* D, const float* u, float* y, ssm_c64* x, int32_t* status, int32_t lanes,
+                      void* stream) {
     if (Bsz < 1 || H < 1 || N < 1 || r < 1 || T < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (!(lanes == 0 || lanes == 64 || (lanes == 16 && N <= 64))) return SSM_ERR_INVALID_ARGUMENT;
     if (r > kMaxR || N > kMaxNStep || H >= kMaxDim || Bsz >= kMaxDim || T >= kMaxDim || Bsz * H >= kMaxDim ||
         Bsz * H > ((int64_t)1 << 62) / T)
         return SSM_ERR_UNSUPPORTED;
@@ -491,8 +493,22 @@ int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, c
         !aligned(status, 4))
         return SSM_ERR_INVALID_ARGUMENT;
     if (prep_bytes < (size_t)H * step_prepared_channel_bytes(N, r)) return SSM_ERR_WORKSPACE;
+    if (lanes == 0) {
+        // 16-lane groups issue fewer instructions per sequence step but put
+        // four sequences in a wave: they pay once at least three sequences
+        // per SIMD keep every SIMD busy and the call is long enough to amortise
+        // their longer first step
+        lanes = 64;
+        if (N <= 64 && T >= 8) {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+                return SSM_ERR_DEVICE;
+            if (Bsz * H >= (int64_t)3 * 4 * cus) lanes = 16;
+        }
+    }
     return device_status(launch_step_prepared(Bsz, H, N, r, T, (const uint8_t*)prep, D, u, y, (float2*)x, status,
-                                              (hipStream_t)stream));
+                                              lanes, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -528,6 +528,251 @@ __global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, in
     if (lane == 0 && b == 0 && status) status[h] = SSM_ST_OK;
 }
 
+// ---- 16-lane groups (N <= 64): four sequences per wave ----
+// Lane g of group q holds states g + 16 e (e < S) of sequence 4 w + q.  The
+// per-step sums then reduce within a row of 16 lanes (four DPP stages, after
+// which every lane of the row holds the sum), with no cross-row combine and
+// no scalar round trip; a wave issues about as many instructions per step as
+// the one-sequence wave but for four sequences.
+constexpr int kGroup = 16;
+
+template <int K>
+__device__ __forceinline__ void row_allsum(float (&v)[K]) {
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0xB1>(v[i]);   // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x4E>(v[i]);   // quad_perm [2,3,0,1]
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x141>(v[i]);  // row_half_mirror
+#pragma unroll
+    for (int i = 0; i < K; ++i) v[i] += dpp_get<0x140>(v[i]);  // row_mirror
+}
+
+// value of lane (own group, index k) for every lane
+__device__ __forceinline__ float group_read(float v, int lane, int k) {
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & ~(kGroup - 1)) | k) << 2, __float_as_int(v)));
+}
+
+// T steps of one group's sequence from xs (updated in place).  NZ: room for
+// the bordered form's states in Z (0: Woodbury form; the whole wave takes
+// the bordered loop when any of its groups needs it).  Mbf: the group's
+// order r + s inverse (row stride kMaxOrder); n = r + s of the group.
+// store: this group writes its outputs.
+template <int S, int RK, int NZ>
+__device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n, const float2* Mbf,
+                                        const int (&zl)[kMaxRank], const int (&ze)[kMaxRank],
+                                        const float2 (&qd)[S][RK], const float2 (&pa)[S][RK], const float2 (&dv)[S],
+                                        const float2 (&cc)[S], const float2 (&bb)[S], const int (&zs)[S], float Dh,
+                                        bool store, const float* __restrict__ u, float* __restrict__ y,
+                                        float2 (&xs)[S]) {
+    constexpr int NO = RK + NZ;
+    float2 Mr[NZ == 0 ? RK : 1][NZ == 0 ? RK : 1];
+    if constexpr (NZ == 0) {
+#pragma unroll
+        for (int i = 0; i < RK; ++i)
+#pragma unroll
+            for (int j = 0; j < RK; ++j) Mr[i][j] = Mbf[i * kMaxOrder + j];
+    }
+    // inputs of steps [t0, t0 + 16) (lane g holds step t0 + g) and the next
+    // block; indexes past the end read the last input (never used)
+    float ucur = u[ub + min(g, T - 1)];
+    float unext = u[ub + min(kGroup + g, T - 1)];
+    float yblk = 0.0f;
+    float uprev = 0.0f;
+    for (int t = 0; t <= T; ++t) {
+        const int k = t & (kGroup - 1);
+        const float ut = group_read(ucur, lane, k);  // needed only at the end of the step
+        // the lane's partial sums, seeded with its first state's terms
+        float2 sq[RK], sc = c_mul(cc[0], xs[0]);
+#pragma unroll
+        for (int a = 0; a < RK; ++a) sq[a] = c_mul(qd[0][a], xs[0]);
+#pragma unroll
+        for (int e = 1; e < S; ++e) {
+#pragma unroll
+            for (int a = 0; a < RK; ++a) sq[a] = c_add(sq[a], c_mul(qd[e][a], xs[e]));
+            sc = c_add(sc, c_mul(cc[e], xs[e]));
+        }
+        {
+            float v[2 * RK + 1];
+#pragma unroll
+            for (int a = 0; a < RK; ++a) {
+                v[2 * a] = sq[a].x;
+                v[2 * a + 1] = sq[a].y;
+            }
+            v[2 * RK] = sc.x;
+            row_allsum<2 * RK + 1>(v);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) sq[a] = make_float2(v[2 * a], v[2 * a + 1]);
+            sc.x = v[2 * RK];
+        }
+        if (t > 0) {  // y_{t-1} = Re(C^* x_{t-1}) + D u_{t-1}
+            const int kp = (t - 1) & (kGroup - 1);
+            if (g == kp) yblk = sc.x + Dh * uprev;
+            if (kp == kGroup - 1 || t == T) {
+                const int t0 = (t - 1) & ~(kGroup - 1);
+                if (store && t0 + g < T) y[ub + t0 + g] = yblk;
+            }
+        }
+        if (t == T) break;
+        if (k == kGroup - 1) {  // next block of inputs, for step t + 1
+            ucur = unext;
+            unext = u[ub + min(t + 1 + kGroup + g, T - 1)];
+        }
+        float2 sol[NO];
+        if constexpr (NZ == 0) {
+#pragma unroll
+            for (int i = 0; i < RK; ++i) {
+                float2 acc = make_float2(0.0f, 0.0f);
+#pragma unroll
+                for (int j = 0; j < RK; ++j) acc = c_add(acc, c_mul(Mr[i][j], sq[j]));
+                sol[i] = acc;
+            }
+        } else {
+            float2 rhs[NO];
+#pragma unroll
+            for (int a = 0; a < RK; ++a) rhs[a] = sq[a];
+#pragma unroll
+            for (int zz = 0; zz < NZ; ++zz) {
+                float2 v = xs[0];
+#pragma unroll
+                for (int e = 1; e < S; ++e)
+                    if (ze[zz] == e) v = xs[e];
+                v = make_float2(group_read(v.x, lane, zl[zz]), group_read(v.y, lane, zl[zz]));
+                rhs[RK + zz] = RK + zz < n ? v : make_float2(0.0f, 0.0f);
+            }
+            int off = 0;
+            asm volatile("" : "+v"(off));
+#pragma unroll
+            for (int i = 0; i < NO; ++i) {
+                float2 acc = make_float2(0.0f, 0.0f);
+                if (i < n) {
+#pragma unroll
+                    for (int j = 0; j < NO; ++j)
+                        if (j < n) acc = c_add(acc, c_mul(Mbf[off + i * kMaxOrder + j], rhs[j]));
+                }
+                sol[i] = acc;
+            }
+        }
+#pragma unroll
+        for (int e = 0; e < S; ++e) {
+            float2 gv = c_mul(dv[e], xs[e]);
+#pragma unroll
+            for (int a = 0; a < RK; ++a) gv = c_sub(gv, c_mul(pa[e][a], sol[a]));
+            if constexpr (NZ > 0) {
+#pragma unroll
+                for (int zz = 0; zz < NZ; ++zz)
+                    if (zs[e] == zz) gv = sol[RK + zz];
+            }
+            xs[e] = make_float2(2.0f * gv.x - xs[e].x + bb[e].x * ut, 2.0f * gv.y - xs[e].y + bb[e].y * ut);
+        }
+        uprev = ut;
+    }
+}
+
+template <int S, int RK>
+__global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H, int N, int T,
+                                                                const uint8_t* __restrict__ prep, size_t chan_bytes,
+                                                                const float* __restrict__ D,
+                                                                const float* __restrict__ u, float* __restrict__ y,
+                                                                float2* __restrict__ x,
+                                                                int32_t* __restrict__ status) {
+    constexpr int kGroups = kWave / kGroup;
+    __shared__ float2 mbf[kGroups][kMaxOrder * kMaxOrder];
+    const int lane = threadIdx.x;
+    const int q = lane / kGroup, g = lane % kGroup;
+    const int seq_raw = blockIdx.x * kGroups + q;
+    const bool live = seq_raw < nseq;
+    const int seq = live ? seq_raw : nseq - 1;  // a group past the end shadows the last sequence, storing nothing
+    const int h = seq % H;
+    const int b = seq / H;
+    const size_t xb = (size_t)seq * N;
+    const size_t ub = (size_t)seq * T;
+    const uint8_t* base = prep + (size_t)h * chan_bytes;
+    const int32_t* hd = reinterpret_cast<const int32_t*>(base);
+    int st = hd[3];
+    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
+    const bool ok = st == SSM_ST_OK;
+    if (live && !ok) {  // NaN outputs now; the loop below stores nothing for this group
+        const float nanf = __builtin_nanf("");
+        for (int t = g; t < T; t += kGroup) y[ub + t] = nanf;
+        for (int j = g; j < N; j += kGroup) x[xb + j] = c_nan();
+    }
+    if (live && g == 0 && b == 0 && status) status[h] = st;
+    const int s = ok ? min(max(hd[4], 0), RK) : 0;
+    int zidx[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(hd[5 + zz], 0), S * kGroup - 1);
+    const float2* mb = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4);
+#pragma unroll
+    for (int i = 0; i < kMaxOrder * kMaxOrder / kGroup; ++i)
+        mbf[q][g + kGroup * i] = ok ? mb[g + kGroup * i] : make_float2(0.0f, 0.0f);
+    // constants of states g + 16 e (slots of the 64-slot arrays; zero past N),
+    // all zero for a failing group so that it runs the loop harmlessly
+    const float2* cst = reinterpret_cast<const float2*>(base + kPrepConstOffset);
+    constexpr int NS = kWave;
+    const float2 zero = make_float2(0.0f, 0.0f);
+    float2 qd[S][RK], pa[S][RK], dv[S], cc[S], bb[S], xs[S];
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+        const int j = g + kGroup * e;
+        dv[e] = ok ? cst[j] : zero;
+        cc[e] = ok ? cst[NS + j] : zero;
+        bb[e] = ok ? cst[2 * NS + j] : zero;
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            qd[e][a] = ok ? cst[(3 + a) * NS + j] : zero;
+            pa[e][a] = ok ? cst[(3 + RK + a) * NS + j] : zero;
+        }
+        xs[e] = ok && j < N ? x[xb + j] : zero;
+    }
+    int zs[S], zl[kMaxRank], ze[kMaxRank];
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+        const int j = g + kGroup * e;
+        zs[e] = -1;
+        for (int zz = 0; zz < s; ++zz)
+            if (zidx[zz] == j) zs[e] = zz;
+    }
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) {
+        const int j = zz < s ? zidx[zz] : 0;
+        zl[zz] = j % kGroup;
+        ze[zz] = j / kGroup;
+    }
+    const float Dh = D ? D[h] : 0.0f;
+    const bool store = live && ok;
+    __syncthreads();
+    if (__ballot(s > 0) == 0)
+        recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbf[q], zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
+    else
+        recur16<S, RK, kMaxRank>(T, g, lane, ub, RK + s, mbf[q], zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y,
+                                 xs);
+    if (store) {
+#pragma unroll
+        for (int e = 0; e < S; ++e) {
+            const int j = g + kGroup * e;
+            if (j < N) x[xb + j] = xs[e];
+        }
+    }
+}
+
+template <int S>
+hipError_t launch_prepared16(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
+                             size_t chan_bytes, const float* D, const float* u, float* y, float2* x, int32_t* status,
+                             hipStream_t stream) {
+    const int64_t nseq = Bsz * H;
+    const unsigned waves = (unsigned)((nseq + kWave / kGroup - 1) / (kWave / kGroup));
+#define SSM_PREPD16(RK)                                                                                          \
+    if (r == RK) {                                                                                               \
+        hipLaunchKernelGGL((step_prepared16_kernel<S, RK>), dim3(waves), dim3(kWave), 0, stream, (int)nseq,      \
+                           (int)H, (int)N, (int)T, prep, chan_bytes, D, u, y, x, status);                        \
+        return hipGetLastError();                                                                                \
+    }
+    SSM_PREPD16(1) SSM_PREPD16(2) SSM_PREPD16(3) SSM_PREPD16(4)
+#undef SSM_PREPD16
+    return hipErrorInvalidValue;
+}
+
 template <int NPL>
 hipError_t launch_npl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
                       const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
@@ -603,10 +848,17 @@ hipError_t launch_step_prepare(int64_t H, int64_t N, int64_t r, const float2* La
     return hipErrorInvalidValue;
 }
 
+// lanes: 16 (N <= 64: four sequences per wave) or 64 (one per wave)
 hipError_t launch_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const uint8_t* prep,
-                                const float* D, const float* u, float* y, float2* x, int32_t* status,
+                                const float* D, const float* u, float* y, float2* x, int32_t* status, int lanes,
                                 hipStream_t stream) {
     const size_t cb = step_prepared_channel_bytes(N, r);
+    if (lanes == kGroup) {
+        if (N <= kGroup) return launch_prepared16<1>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
+        if (N <= 2 * kGroup) return launch_prepared16<2>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
+        if (N <= kWave) return launch_prepared16<4>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
+        return hipErrorInvalidValue;
+    }
     if (N <= kWave) return launch_prepared_npl<1>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
     if (N <= 2 * kWave) return launch_prepared_npl<2>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);
     if (N <= kStepMaxN) return launch_prepared_npl<4>(Bsz, H, N, r, T, prep, cb, D, u, y, x, status, stream);

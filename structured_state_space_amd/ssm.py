@@ -74,7 +74,7 @@ def _load():
     lib.ssm_step.restype = i32
     lib.ssm_step_prepare.argtypes = [i64, i64, i64] + [vp] * 7 + [sz, vp, vp]
     lib.ssm_step_prepare.restype = i32
-    lib.ssm_step_prepared.argtypes = [i64, i64, i64, i64, i64, vp, sz] + [vp] * 6
+    lib.ssm_step_prepared.argtypes = [i64, i64, i64, i64, i64, vp, sz] + [vp] * 5 + [ctypes.c_int32, vp]
     lib.ssm_step_prepared.restype = i32
     lib.ssm_forward_complex.argtypes = [i64, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     lib.ssm_forward_complex.restype = i32
@@ -321,10 +321,12 @@ def step_prepare(Lambda, P, Q, B, C, dt, prep=None, status=None):
     return dict(prep=prep, status=status, H=H, N=N, r=r)
 
 
-def step_prepared(prepared, D, u, x=None, y=None, status=None):
+def step_prepared(prepared, D, u, x=None, y=None, status=None, lanes=0):
     """ssm_step_prepared: T steps of the recurrence from the state x (zeros
     when None) with the constants of step_prepare's result `prepared`;
-    returns dict(y, x, status) as step does, with the same values."""
+    returns dict(y, x, status) as step does.  lanes: 64 (step's recurrence,
+    the same values bit for bit), 16 (N <= 64: four sequences per wave,
+    equal up to float32 rounding) or 0 (chosen by the library per call)."""
     prep, H, N, r = prepared["prep"], prepared["H"], prepared["N"], prepared["r"]
     dev = prep.device
     Bsz, H2, T = u.shape
@@ -342,7 +344,7 @@ def step_prepared(prepared, D, u, x=None, y=None, status=None):
         status = torch.empty((H,), dtype=torch.int32, device=dev)
     _check(status, "status", torch.int32, (H,), dev)
     rc = lib.ssm_step_prepared(Bsz, H, N, r, T, _ptr(prep), prep.numel(), _ptr(D), _ptr(u), _ptr(y), _ptr(x),
-                               _ptr(status), _stream(dev))
+                               _ptr(status), int(lanes), _stream(dev))
     if rc != OK:
         raise SSMError("ssm_step_prepared", rc)
     return dict(y=y, x=x, status=status)

@@ -94,12 +94,14 @@ int main(void) {
     expect(ssm_step_prepare(3, 4, 1, c, c, c, c, c, f, FAKE_OFF(64), 1 << 20, NULL, NULL), SSM_ERR_INVALID_ARGUMENT,
            "prepare align");
     expect(ssm_step_prepare(3, 4, 5, c, c, c, c, c, f, FAKE, 1 << 20, NULL, NULL), SSM_ERR_UNSUPPORTED, "prepare r");
-    expect(ssm_step_prepared(2, 3, 4, 1, 16, FAKE, 64, NULL, f, fo, co, NULL, NULL), SSM_ERR_WORKSPACE,
+    expect(ssm_step_prepared(2, 3, 4, 1, 16, FAKE, 64, NULL, f, fo, co, NULL, 0, NULL), SSM_ERR_WORKSPACE,
            "prepared bytes");
-    expect(ssm_step_prepared(2, 3, 4, 1, 0, FAKE, 1 << 20, NULL, f, fo, co, NULL, NULL), SSM_ERR_INVALID_ARGUMENT,
+    expect(ssm_step_prepared(2, 3, 4, 1, 0, FAKE, 1 << 20, NULL, f, fo, co, NULL, 0, NULL), SSM_ERR_INVALID_ARGUMENT,
            "prepared T");
-    expect(ssm_step_prepared(2, 3, 4, 1, 16, NULL, 1 << 20, NULL, f, fo, co, NULL, NULL), SSM_ERR_INVALID_ARGUMENT,
-           "prepared null");
+    expect(ssm_step_prepared(2, 3, 4, 1, 16, NULL, 1 << 20, NULL, f, fo, co, NULL, 0, NULL),
+           SSM_ERR_INVALID_ARGUMENT, "prepared null");
+    expect(ssm_step_prepared(2, 3, 65, 1, 16, FAKE, 1 << 20, NULL, f, fo, co, NULL, 16, NULL),
+           SSM_ERR_INVALID_ARGUMENT, "prepared lanes");
     expect(ssm_hippo_dplr(3, 8, 1.0, 0, NULL, 0, NULL, co, co, NULL, NULL, NULL, FAKE, 1 << 30, NULL),
            SSM_ERR_INVALID_ARGUMENT, "hippo kind");
     expect(ssm_hippo_dplr(SSM_HIPPO_LEGT, 8, -1.0, 0, NULL, 0, NULL, co, co, NULL, NULL, NULL, FAKE, 1 << 30, NULL),

@@ -228,13 +228,16 @@ def test_step_prepare_rejects_before_launch(kw, code):
     (dict(x=FAKE + 4), ssm.ERR_INVALID_ARGUMENT),
     (dict(y=None), ssm.ERR_INVALID_ARGUMENT),
     (dict(prep_bytes=3327), ssm.ERR_WORKSPACE),
+    (dict(lanes=32), ssm.ERR_INVALID_ARGUMENT),            # layouts: 0 (chosen), 16 or 64
+    (dict(lanes=-1), ssm.ERR_INVALID_ARGUMENT),
+    (dict(lanes=16, N=65), ssm.ERR_INVALID_ARGUMENT),      # 16-lane groups hold at most 64 states
 ])
 def test_step_prepared_rejects_before_launch(kw, code):
     a = dict(Bsz=2, H=1, N=4, r=1, T=16, prep=FAKE, prep_bytes=1 << 20, D=None, u=FAKE, y=FAKE, x=FAKE,
-             status=None)
+             status=None, lanes=0)
     a.update(kw)
     assert ssm.lib.ssm_step_prepared(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["prep"], a["prep_bytes"], a["D"],
-                                     a["u"], a["y"], a["x"], a["status"], None) == code
+                                     a["u"], a["y"], a["x"], a["status"], a["lanes"], None) == code
 
 
 # --------------------------------------------------------------------------

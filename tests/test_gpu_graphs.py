@@ -125,10 +125,11 @@ def test_step_replays_continue_the_stream():
     assert np.isfinite(y.cpu().numpy()).all()
 
 
-def test_step_prepared_replays():
+@pytest.mark.parametrize("lanes", [64, 16])
+def test_step_prepared_replays(lanes):
     """The prepared form under capture: one ssm_step_prepare outside the
     graph, a captured ssm_step_prepared of T = 1 (a decode step) replayed as
-    a stream; each replay equals an eager ssm_step call bit for bit."""
+    a stream; each replay equals an eager ssm_step_prepared call bit for bit."""
     ssm = _ssm()
     H, N, r, Bsz = 8, 64, 1, 2
     p = I.random_params(61, H, N, r, 16)
@@ -139,7 +140,7 @@ def test_step_prepared_replays():
     x = torch.zeros((Bsz, H, N), dtype=torch.complex64, device=DEV)
     y = torch.empty_like(u)
     status = torch.empty(H, dtype=torch.int32, device=DEV)
-    call = lambda: ssm.step_prepared(prep, d["D"], u, x=x, y=y, status=status)
+    call = lambda: ssm.step_prepared(prep, d["D"], u, x=x, y=y, status=status, lanes=lanes)
     g, _ = _capture(call)
     x.zero_()
     xr = torch.zeros_like(x)
@@ -148,7 +149,7 @@ def test_step_prepared_replays():
         _eager_noise()
         g.replay()
         torch.cuda.synchronize()
-        ref = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], steps[k], x=xr)
+        ref = ssm.step_prepared(prep, d["D"], steps[k], x=xr, lanes=lanes)
         torch.cuda.synchronize()
         assert torch.equal(y, ref["y"]), f"replay {k}"
         assert torch.equal(x, xr), f"state after replay {k}"

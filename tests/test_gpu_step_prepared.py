@@ -1,10 +1,12 @@
 """GPU checks of the step mode in two calls (ssm_step_prepare once per
 parameter set, then ssm_step_prepared per chunk of the stream), through the C
-ABI.  The prepared calls run the same float32 recurrence from the same float32
-constants as ssm_step, so their y, final state and statuses must equal
-ssm_step's bit for bit (NaN where ssm_step gives NaN); one case is also
-compared with the complex128 oracle's recurrence (max error <= 2e-4 x
-max|reference| per batch row)."""
+ABI, in both layouts.  With 64 lanes per sequence the prepared calls run
+ssm_step's float32 recurrence from the same float32 constants, so y, final
+state and statuses equal ssm_step's bit for bit.  With 16-lane groups (N <=
+64, four sequences per wave) the sums run in another order: y and the final
+state are then compared with the complex128 oracle's recurrence (max error
+<= 2e-4 x max|reference| per batch row) and with ssm_step (same bound);
+statuses and NaN positions are exact."""
 import ctypes
 
 import numpy as np
@@ -34,14 +36,14 @@ def _random_state(seed, Bsz, H, N):
     return (rng.normal(size=(Bsz, H, N)) + 1j * rng.normal(size=(Bsz, H, N))).astype(np.complex64)
 
 
-def _both(p, u, x0):
+def _both(p, u, x0, lanes=64):
     """(ssm_step result, prepared result, prepare status) on the same inputs."""
     ssm = _ssm()
     d = ssm.to_device(p, DEV)
     ut = torch.from_numpy(u).to(DEV)
     ref = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], ut, x=torch.from_numpy(x0).to(DEV))
     prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
-    out = ssm.step_prepared(prep, d["D"], ut, x=torch.from_numpy(x0).to(DEV))
+    out = ssm.step_prepared(prep, d["D"], ut, x=torch.from_numpy(x0).to(DEV), lanes=lanes)
     torch.cuda.synchronize()
     return ref, out, _np(prep["status"])
 
@@ -52,30 +54,63 @@ def _assert_same(ref, out):
     assert np.array_equal(_np(out["x"]), _np(ref["x"]), equal_nan=True)
 
 
+def _assert_oracle(p, u, x0, out, channels=None):
+    """y and final state of the given channels against the oracle's recurrence."""
+    y, xT = _np(out["y"]), _np(out["x"])
+    for h in (range(p.H) if channels is None else channels):
+        c = p.channel(h)
+        Abar, Bbar, st = O.bilinear(O.dplr_matrix(c["Lambda"], c["P"], c["Q"]), c["B"], float(c["dt"]))
+        assert st == O.OK
+        yr, xr = [], []
+        for b in range(u.shape[0]):
+            yb, xb = O.recurrence_from(Abar, Bbar, c["C"], float(c["D"]), u[b, h], x0[b, h])
+            yr.append(yb.real)
+            xr.append(xb)
+        assert_rows_close(y[:, h, :], np.array(yr), what=f"y h{h}")
+        assert_rows_close(xT[:, h, :], np.array(xr), what=f"final state h{h}")
+
+
+def _assert_grouped(p, u, x0, ref, out, channels=None):
+    """N <= 64: exact statuses and NaN positions; values against the oracle
+    and, to the same bound, against ssm_step."""
+    assert np.array_equal(_np(out["status"]), _np(ref["status"]))
+    for k in ("y", "x"):
+        assert np.array_equal(np.isnan(_np(out[k])), np.isnan(_np(ref[k])))
+    _assert_oracle(p, u, x0, out, channels)
+    hs = range(p.H) if channels is None else channels
+    for h in hs:
+        assert_rows_close(_np(out["y"])[:, h, :], _np(ref["y"])[:, h, :], what=f"y vs ssm_step h{h}")
+
+
 @pytest.mark.parametrize("H,N,r,T,Bsz,kind", [
-    (3, 8, 1, 200, 3, "random"),    # several 64-step blocks and a ragged tail
-    (3, 64, 2, 130, 2, "s4"),       # one state per lane, rank 2
-    (2, 100, 1, 64, 2, "random"),   # two states per lane (one partly empty)
+    (3, 8, 1, 200, 3, "random"),    # groups: one state per lane, 9 sequences (a ragged last wave)
+    (3, 64, 2, 130, 2, "s4"),       # groups: four states per lane, rank 2
+    (5, 30, 3, 70, 1, "random"),    # groups: two states per lane, rank 3, 5 sequences
+    (2, 64, 4, 33, 3, "s4"),        # groups: rank 4
+    (2, 100, 1, 64, 2, "random"),   # 64 lanes only: two states per lane (one partly empty)
     (2, 256, 1, 70, 1, "s4"),       # four states per lane
-    (2, 17, 3, 65, 2, "random"),    # rank 3
     (2, 9, 4, 1, 1, "random"),      # rank 4, a single step
     (2, 200, 4, 5, 3, "s4"),        # four states per lane, rank 4
 ])
-def test_prepared_equals_step(H, N, r, T, Bsz, kind):
+def test_prepared_matches_step_and_oracle(H, N, r, T, Bsz, kind):
     p = I.random_params(100 * H + N + T, H, N, r, T, lambda_kind=kind)
     u = I.random_input(N + T, Bsz, H, T)
     x0 = _random_state(N + r, Bsz, H, N)
-    ref, out, pst = _both(p, u, x0)
+    ref, out, pst = _both(p, u, x0, lanes=64)
     assert np.all(pst == 0)
     _assert_same(ref, out)
+    if N <= 64:
+        ref, out, pst = _both(p, u, x0, lanes=16)
+        _assert_grouped(p, u, x0, ref, out)
 
 
-def test_prepared_matches_oracle():
+@pytest.mark.parametrize("lanes", [64, 16])
+def test_prepared_matches_oracle(lanes):
     H, N, r, T, Bsz = 2, 64, 1, 150, 2
     p = I.random_params(5, H, N, r, T)
     u = I.random_input(6, Bsz, H, T)
     x0 = _random_state(7, Bsz, H, N)
-    _, out, _ = _both(p, u, x0)
+    _, out, _ = _both(p, u, x0, lanes)
     y, xT = _np(out["y"]), _np(out["x"])
     for h in range(H):
         c = p.channel(h)
@@ -97,45 +132,83 @@ def test_prepared_bordered_and_statuses():
     p = _golden_case("bordered", T)
     u = I.random_input(9, Bsz, 1, T)
     x0 = _random_state(10, Bsz, 1, p.Lambda.shape[1])
-    ref, out, pst = _both(p, u, x0)
-    assert list(pst) == [0]
-    _assert_same(ref, out)
+    for lanes in (64, 16):
+        ref, out, pst = _both(p, u, x0, lanes)
+        assert list(pst) == [0]
+        _assert_same(ref, out) if lanes == 64 else _assert_grouped(p, u, x0, ref, out)
 
     p = I.random_params(11, 3, 6, 1, 70)
     p.dt[1] = 0.0
     u = I.random_input(12, Bsz, 3, 70)
     x0 = _random_state(13, Bsz, 3, 6)
-    ref, out, pst = _both(p, u, x0)
-    assert list(pst) == [0, ssm.ST_INVALID_STEP, 0]
-    _assert_same(ref, out)
-    assert np.isnan(_np(out["y"])[:, 1]).all()
+    for lanes in (64, 16):
+        ref, out, pst = _both(p, u, x0, lanes)
+        assert list(pst) == [0, ssm.ST_INVALID_STEP, 0]
+        _assert_same(ref, out) if lanes == 64 else _assert_grouped(p, u, x0, ref, out, channels=[0, 2])
+        assert np.isnan(_np(out["y"])[:, 1]).all() and np.isnan(_np(out["x"])[:, 1]).all()
 
     ps = _golden_case("singular-bilinear", 70)
-    ref, out, pst = _both(ps, u[:, :1, :].copy(), x0[:, :1, :1].copy())
-    assert list(pst) == [ssm.ST_SINGULAR_BILINEAR]
-    _assert_same(ref, out)
+    for lanes in (64, 16):
+        ref, out, pst = _both(ps, u[:, :1, :].copy(), x0[:, :1, :1].copy(), lanes)
+        assert list(pst) == [ssm.ST_SINGULAR_BILINEAR]
+        _assert_same(ref, out)
 
 
-def test_prepared_streaming_equals_one_step_call():
+def test_prepared_mixed_wave():
+    """One wave holding a bordered channel (lambda_5 = 2/dt, so d_5 = 0
+    exactly) beside Woodbury channels: the whole wave takes the bordered loop,
+    and every channel still matches the oracle.  P_5 = Q_5 = 3 move the
+    eigenvalue of A near lambda_5 to about -5, so that the channel is stable
+    (the largest |eigenvalue| of Abar is 0.998 here) and 90 steps stay finite."""
+    H, N, r, T, Bsz = 4, 16, 1, 90, 1
+    p = I.random_params(31, H, N, r, T)
+    p.dt[2] = 0.5
+    p.Lambda[2, 5] = 4.0
+    p.P[2, 5, 0] = 3.0
+    p.Q[2, 5, 0] = 3.0
+    u = I.random_input(32, Bsz, H, T)
+    x0 = _random_state(33, Bsz, H, N)
+    for lanes in (64, 16):
+        ref, out, pst = _both(p, u, x0, lanes)
+        assert np.all(pst == 0)
+        _assert_same(ref, out) if lanes == 64 else _assert_grouped(p, u, x0, ref, out)
+
+
+@pytest.mark.parametrize("N,lanes", [(64, 16), (64, 64), (100, 64), (64, 0)])
+def test_prepared_streaming_equals_one_call(N, lanes):
     """One prepare, then a stream split into prepared calls of varied lengths
-    (T = 1 included) and two batch sizes sharing the constants: each equals
-    the corresponding ssm_step call bit for bit."""
+    (T = 1 included) and two batch sizes sharing the constants: in a fixed
+    layout each equals one prepared call over the whole stream bit for bit
+    (and ssm_step's: bit for bit with 64 lanes, to the parity bound with
+    16).  With the layout left to the library (lanes = 0) short and long
+    calls may take different layouts: the split stream then stays within
+    the parity bound of the one call."""
     ssm = _ssm()
-    H, N, r, T = 4, 64, 1, 300
+    H, r, T = 4, 1, 300
     p = I.random_params(77, H, N, r, T)
     d = ssm.to_device(p, DEV)
     prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
     for Bsz in (2, 5):
         u = torch.from_numpy(I.random_input(78 + Bsz, Bsz, H, T)).to(DEV)
-        one = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u)
+        one = ssm.step_prepared(prep, d["D"], u, lanes=lanes)
+        st = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u)
         x = torch.zeros((Bsz, H, N), dtype=torch.complex64, device=DEV)
         parts = []
         for a, b in [(0, 1), (1, 50), (50, 177), (177, 178), (178, 300)]:
-            o = ssm.step_prepared(prep, d["D"], u[:, :, a:b].contiguous(), x=x)
+            o = ssm.step_prepared(prep, d["D"], u[:, :, a:b].contiguous(), x=x, lanes=lanes)
             parts.append(_np(o["y"]))
         torch.cuda.synchronize()
-        assert np.array_equal(np.concatenate(parts, axis=2), _np(one["y"]))
-        assert np.array_equal(_np(x), _np(one["x"]))
+        ys = np.concatenate(parts, axis=2)
+        if lanes:
+            assert np.array_equal(ys, _np(one["y"]))
+            assert np.array_equal(_np(x), _np(one["x"]))
+        for h in range(H):
+            assert_rows_close(ys[:, h, :], _np(one["y"])[:, h, :], what=f"split vs one call h{h}")
+        if lanes == 64:
+            assert np.array_equal(_np(one["y"]), _np(st["y"]))
+        else:
+            for h in range(H):
+                assert_rows_close(_np(one["y"])[:, h, :], _np(st["y"])[:, h, :], what=f"vs ssm_step h{h}")
 
 
 def test_unprepared_blocks():
@@ -148,10 +221,11 @@ def test_unprepared_blocks():
     u = torch.from_numpy(I.random_input(22, Bsz, H, T)).to(DEV)
     nbytes = ssm.workspace_bytes(ssm.OP_STEP_PREPARED, 0, H, N, r, 0)
     blank = dict(prep=torch.zeros(nbytes, dtype=torch.uint8, device=DEV), H=H, N=N, r=r)
-    out = ssm.step_prepared(blank, d["D"], u)
-    torch.cuda.synchronize()
-    assert np.all(_np(out["status"]) == ssm.ST_UNPREPARED)
-    assert np.isnan(_np(out["y"])).all() and np.isnan(_np(out["x"])).all()
+    for lanes in (64, 16):
+        out = ssm.step_prepared(blank, d["D"], u, lanes=lanes)
+        torch.cuda.synchronize()
+        assert np.all(_np(out["status"]) == ssm.ST_UNPREPARED)
+        assert np.isnan(_np(out["y"])).all() and np.isnan(_np(out["x"])).all()
 
     # written for N = 64, called with N = 32 (same block size per channel)
     prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
@@ -161,9 +235,12 @@ def test_unprepared_blocks():
     y = torch.empty_like(u)
     st = torch.empty(H, dtype=torch.int32, device=DEV)
     vp = lambda t: ctypes.c_void_p(t.data_ptr())
-    rc = ssm.lib.ssm_step_prepared(Bsz, H, N2, r, T, vp(prep["prep"]), nbytes, vp(d["D"]), vp(u), vp(y), vp(x),
-                                   vp(st), ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
-    assert rc == ssm.OK
-    torch.cuda.synchronize()
-    assert np.all(_np(st) == ssm.ST_UNPREPARED)
-    assert np.isnan(_np(y)).all() and np.isnan(_np(x)).all()
+    for lanes in (64, 16):
+        rc = ssm.lib.ssm_step_prepared(Bsz, H, N2, r, T, vp(prep["prep"]), nbytes, vp(d["D"]), vp(u), vp(y), vp(x),
+                                       vp(st), lanes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        assert rc == ssm.OK
+        torch.cuda.synchronize()
+        assert np.all(_np(st) == ssm.ST_UNPREPARED)
+        assert np.isnan(_np(y)).all() and np.isnan(_np(x)).all()
+        x.zero_()
+        y.zero_()
