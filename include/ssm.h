@@ -224,6 +224,16 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
  *   u, y [Bsz,H,T] float: y_t = Re(C^* x_t) + D u_t
  *   x    [Bsz,H,N] complex64, in/out (zeros for a fresh stream)
  *   D    [H] float, nullable (= 0); status [H] int32, nullable
+ *   lanes  lanes of a wave per sequence: 64 (one sequence per wave, which
+ *          runs its channel's set-up itself), 16 (N <= 64 only: four
+ *          sequences per wave, fewer instructions per step; the wave runs its
+ *          four channels' set-ups in turn, and the sums are taken in another
+ *          order, so the float32 results differ from the 64-lane ones by
+ *          rounding), or 0 (chosen per call: 16 when N <= 64, T >= 32 and
+ *          Bsz * H is at least three sequences per SIMD of the device, else
+ *          64).  A stream split into calls repeats one call's results bit for
+ *          bit when every call takes the same layout.  Anything else:
+ *          SSM_ERR_INVALID_ARGUMENT.
  * Statuses: invalid-step, singular-bilinear (as ssm_discretize); a failing
  * channel's y and x are filled with NaN.  Sizes: as above with T in place of
  * L (T >= 1, any length below 2^31) and N <= 256.  No workspace.
@@ -231,7 +241,8 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
 int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
              const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
              const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D,
-             const float* u, float* y, ssm_c64* x, int32_t* status, void* stream);
+             const float* u, float* y, ssm_c64* x, int32_t* status, int32_t lanes,
+             void* stream);
 
 /*
  * The recurrent mode in two calls, for streaming decode: the channel set-up
@@ -251,17 +262,10 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T,
  *                      A channel whose block holds a failure status gets it
  *                      again with NaN y and x; a block not written for these
  *                      N and r gives SSM_ST_UNPREPARED, NaN y and x.
- *   lanes              lanes of a wave per sequence: 64 (one sequence per
- *                      wave: ssm_step's recurrence, so y and x equal its own
- *                      bit for bit), 16 (N <= 64 only: four sequences per
- *                      wave, fewer instructions per step, the sums taken in
- *                      another order, so the float32 results differ from
- *                      ssm_step's by rounding), or 0 (chosen per call: 16
- *                      when N <= 64, T >= 8 and Bsz * H is at least three
- *                      sequences per SIMD of the device, else 64).  A stream
- *                      split into calls repeats one call's results bit for
- *                      bit when every call takes the same layout; pass 16 or
- *                      64 to fix it.  Anything else: SSM_ERR_INVALID_ARGUMENT.
+ *   lanes              as ssm_step's, with 0 choosing 16 from T >= 8 (no
+ *                      set-up to amortise).  In either fixed layout y and x
+ *                      equal ssm_step's in that layout bit for bit (the same
+ *                      float32 constants and recurrence).
  * Sizes as ssm_step.  SSM_ERR_WORKSPACE when prep_bytes is below the size.
  */
 int ssm_step_prepare(int64_t H, int64_t N, int64_t r, const ssm_c64* Lambda, const ssm_c64* P,

@@ -39,7 +39,8 @@ hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const f
                              float2* Abar, float2* Ct, int32_t* status, hipStream_t stream);
 hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
                        const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
-                       const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream);
+                       const float* D, const float* u, float* y, float2* x, int32_t* status, int lanes,
+                       hipStream_t stream);
 size_t step_prepared_channel_bytes(int64_t N, int64_t r);
 hipError_t launch_step_prepare(int64_t H, int64_t N, int64_t r, const float2* Lambda, const float2* P,
                                const float2* Q, const float2* Bv, const float2* C, const float* dt, uint8_t* prep,
@@ -446,10 +447,28 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
     return device_status(e);
 }
 
+// The step layout for lanes = 0.  16-lane groups issue fewer instructions per
+// sequence step but put four sequences in a wave: they pay once at least
+// three sequences per SIMD keep every SIMD busy and the call has at least
+// min_T steps (to amortise a longer first step, and in ssm_step the wave's
+// four set-ups).  Returns SSM_OK and sets *lanes, or SSM_ERR_DEVICE.
+static int choose_step_lanes(int64_t Bsz, int64_t H, int64_t N, int64_t T, int64_t min_T, int32_t* lanes) {
+    *lanes = 64;
+    if (N <= 64 && T >= min_T) {
+        int dev = 0, cus = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return SSM_ERR_DEVICE;
+        if (Bsz * H >= (int64_t)3 * 4 * cus) *lanes = 16;
+    }
+    return SSM_OK;
+}
+
 int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const ssm_c64* Lambda, const ssm_c64* P,
              const ssm_c64* Q, const ssm_c64* B, const ssm_c64* C, const float* dt, const float* D, const float* u,
-             float* y, ssm_c64* x, int32_t* status, void* stream) {
+             float* y, ssm_c64* x, int32_t* status, int32_t lanes, void* stream) {
     if (Bsz < 1 || H < 1 || N < 1 || r < 1 || T < 1) return SSM_ERR_INVALID_ARGUMENT;
+    if (!(lanes == 0 || lanes == 64 || (lanes == 16 && N <= 64))) return SSM_ERR_INVALID_ARGUMENT;
     if (r > kMaxR || N > kMaxNStep || H >= kMaxDim || Bsz >= kMaxDim || T >= kMaxDim || Bsz * H >= kMaxDim ||
         Bsz * H > ((int64_t)1 << 62) / T)
         return SSM_ERR_UNSUPPORTED;
@@ -459,8 +478,12 @@ int ssm_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const ssm_
         if (!aligned(p, 8)) return SSM_ERR_INVALID_ARGUMENT;
     if (!aligned(dt, 4) || !aligned(D, 4) || !aligned(u, 4) || !aligned(y, 4) || !aligned(status, 4))
         return SSM_ERR_INVALID_ARGUMENT;
+    if (lanes == 0) {
+        const int rc = choose_step_lanes(Bsz, H, N, T, 32, &lanes);
+        if (rc != SSM_OK) return rc;
+    }
     return device_status(launch_step(Bsz, H, N, r, T, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                     (const float2*)B, (const float2*)C, dt, D, u, y, (float2*)x, status,
+                                     (const float2*)B, (const float2*)C, dt, D, u, y, (float2*)x, status, lanes,
                                      (hipStream_t)stream));
 }
 
@@ -494,18 +517,8 @@ int ssm_step_prepared(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, c
         return SSM_ERR_INVALID_ARGUMENT;
     if (prep_bytes < (size_t)H * step_prepared_channel_bytes(N, r)) return SSM_ERR_WORKSPACE;
     if (lanes == 0) {
-        // 16-lane groups issue fewer instructions per sequence step but put
-        // four sequences in a wave: they pay once at least three sequences
-        // per SIMD keep every SIMD busy and the call is long enough to amortise
-        // their longer first step
-        lanes = 64;
-        if (N <= 64 && T >= 8) {
-            int dev = 0, cus = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-                return SSM_ERR_DEVICE;
-            if (Bsz * H >= (int64_t)3 * 4 * cus) lanes = 16;
-        }
+        const int rc = choose_step_lanes(Bsz, H, N, T, 8, &lanes);
+        if (rc != SSM_OK) return rc;
     }
     return device_status(launch_step_prepared(Bsz, H, N, r, T, (const uint8_t*)prep, D, u, y, (float2*)x, status,
                                               lanes, (hipStream_t)stream));

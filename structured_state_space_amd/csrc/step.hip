@@ -669,46 +669,31 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
     }
 }
 
+// One group's sequence from its channel's constants: cst holds the 64-slot
+// arrays of the prepared layout (d^{-1}, conj C, Bbar, Q^* D^{-1}, alpha
+// D^{-1} P), mbq the order r + s inverse (in LDS), st, s_in and zin the
+// channel's status, |Z| and Z.  A group past the end (live false) runs
+// along without storing.  Every lane of the wave must call it together (the
+// sums are row-wise DPP, the choice of loop wave-uniform).
 template <int S, int RK>
-__global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H, int N, int T,
-                                                                const uint8_t* __restrict__ prep, size_t chan_bytes,
-                                                                const float* __restrict__ D,
-                                                                const float* __restrict__ u, float* __restrict__ y,
-                                                                float2* __restrict__ x,
-                                                                int32_t* __restrict__ status) {
-    constexpr int kGroups = kWave / kGroup;
-    __shared__ float2 mbf[kGroups][kMaxOrder * kMaxOrder];
-    const int lane = threadIdx.x;
-    const int q = lane / kGroup, g = lane % kGroup;
-    const int seq_raw = blockIdx.x * kGroups + q;
-    const bool live = seq_raw < nseq;
-    const int seq = live ? seq_raw : nseq - 1;  // a group past the end shadows the last sequence, storing nothing
-    const int h = seq % H;
-    const int b = seq / H;
-    const size_t xb = (size_t)seq * N;
-    const size_t ub = (size_t)seq * T;
-    const uint8_t* base = prep + (size_t)h * chan_bytes;
-    const int32_t* hd = reinterpret_cast<const int32_t*>(base);
-    int st = hd[3];
-    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
+__device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bool live, int st, int s_in,
+                                               const int (&zin)[kMaxRank], const float2* mbq, const float2* cst,
+                                               float Dh, size_t ub, size_t xb, int32_t* status_slot,
+                                               const float* __restrict__ u, float* __restrict__ y,
+                                               float2* __restrict__ x) {
     const bool ok = st == SSM_ST_OK;
     if (live && !ok) {  // NaN outputs now; the loop below stores nothing for this group
         const float nanf = __builtin_nanf("");
         for (int t = g; t < T; t += kGroup) y[ub + t] = nanf;
         for (int j = g; j < N; j += kGroup) x[xb + j] = c_nan();
     }
-    if (live && g == 0 && b == 0 && status) status[h] = st;
-    const int s = ok ? min(max(hd[4], 0), RK) : 0;
+    if (g == 0 && status_slot) *status_slot = st;
+    const int s = ok ? min(max(s_in, 0), RK) : 0;
     int zidx[kMaxRank];
 #pragma unroll
-    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(hd[5 + zz], 0), S * kGroup - 1);
-    const float2* mb = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4);
-#pragma unroll
-    for (int i = 0; i < kMaxOrder * kMaxOrder / kGroup; ++i)
-        mbf[q][g + kGroup * i] = ok ? mb[g + kGroup * i] : make_float2(0.0f, 0.0f);
-    // constants of states g + 16 e (slots of the 64-slot arrays; zero past N),
-    // all zero for a failing group so that it runs the loop harmlessly
-    const float2* cst = reinterpret_cast<const float2*>(base + kPrepConstOffset);
+    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(zin[zz], 0), S * kGroup - 1);
+    // constants of states g + 16 e (zero past N), all zero for a failing
+    // group so that it runs the loop harmlessly
     constexpr int NS = kWave;
     const float2 zero = make_float2(0.0f, 0.0f);
     float2 qd[S][RK], pa[S][RK], dv[S], cc[S], bb[S], xs[S];
@@ -739,14 +724,11 @@ __global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H,
         zl[zz] = j % kGroup;
         ze[zz] = j / kGroup;
     }
-    const float Dh = D ? D[h] : 0.0f;
     const bool store = live && ok;
-    __syncthreads();
     if (__ballot(s > 0) == 0)
-        recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbf[q], zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
+        recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
     else
-        recur16<S, RK, kMaxRank>(T, g, lane, ub, RK + s, mbf[q], zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y,
-                                 xs);
+        recur16<S, RK, kMaxRank>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
     if (store) {
 #pragma unroll
         for (int e = 0; e < S; ++e) {
@@ -754,6 +736,122 @@ __global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H,
             if (j < N) x[xb + j] = xs[e];
         }
     }
+}
+
+// the group's sequence index, clamped to the last one past the end
+struct GroupSeq {
+    int seq, h, b;
+    bool live;
+    __device__ GroupSeq(int wave, int q, int nseq, int H) {
+        const int raw = wave * (kWave / kGroup) + q;
+        live = raw < nseq;
+        seq = live ? raw : nseq - 1;
+        h = seq % H;
+        b = seq / H;
+    }
+};
+
+template <int S, int RK>
+__global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H, int N, int T,
+                                                                const uint8_t* __restrict__ prep, size_t chan_bytes,
+                                                                const float* __restrict__ D,
+                                                                const float* __restrict__ u, float* __restrict__ y,
+                                                                float2* __restrict__ x,
+                                                                int32_t* __restrict__ status) {
+    constexpr int kGroups = kWave / kGroup;
+    __shared__ float2 mbf[kGroups][kMaxOrder * kMaxOrder];
+    const int lane = threadIdx.x;
+    const int q = lane / kGroup, g = lane % kGroup;
+    const GroupSeq gs(blockIdx.x, q, nseq, H);
+    const uint8_t* base = prep + (size_t)gs.h * chan_bytes;
+    const int32_t* hd = reinterpret_cast<const int32_t*>(base);
+    int st = hd[3];
+    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
+    int zin[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) zin[zz] = hd[5 + zz];
+    const float2* mb = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4);
+#pragma unroll
+    for (int i = 0; i < kMaxOrder * kMaxOrder / kGroup; ++i)
+        mbf[q][g + kGroup * i] = st == SSM_ST_OK ? mb[g + kGroup * i] : make_float2(0.0f, 0.0f);
+    __syncthreads();
+    group_sequence<S, RK>(T, N, g, lane, gs.live, st, hd[4], zin, mbf[q],
+                          reinterpret_cast<const float2*>(base + kPrepConstOffset), D ? D[gs.h] : 0.0f,
+                          (size_t)gs.seq * T, (size_t)gs.seq * N,
+                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u, y, x);
+}
+
+// ssm_step in 16-lane groups: the wave runs the float64 set-up of its four
+// sequences' channels one after another (the one-wave set-up, N <= 64),
+// leaves the constants in LDS in the prepared layout, then each group runs
+// its sequence exactly as the prepared kernel does (the same values, bit for
+// bit, as ssm_step_prepare + ssm_step_prepared in this layout).
+template <int S, int RK>
+__global__ __launch_bounds__(kWave) void step16_kernel(int nseq, int H, int N, int T,
+                                                       const float2* __restrict__ Lambda,
+                                                       const float2* __restrict__ P, const float2* __restrict__ Q,
+                                                       const float2* __restrict__ Bv, const float2* __restrict__ C,
+                                                       const float* __restrict__ dt, const float* __restrict__ D,
+                                                       const float* __restrict__ u, float* __restrict__ y,
+                                                       float2* __restrict__ x, int32_t* __restrict__ status) {
+    constexpr int kGroups = kWave / kGroup;
+    constexpr int NS = kWave;
+    __shared__ StepSetup sm;
+    __shared__ float2 cstl[kGroups][(3 + 2 * RK) * NS];
+    __shared__ float2 mbl[kGroups][kMaxOrder * kMaxOrder];
+    __shared__ int hdl[kGroups][2 + kMaxRank];
+    const int lane = threadIdx.x;
+    const float2 zero = make_float2(0.0f, 0.0f);
+    for (int qq = 0; qq < kGroups; ++qq) {
+        const GroupSeq gq(blockIdx.x, qq, nseq, H);
+        float2 qd[1][RK], pa[1][RK], dv[1], cc[1], bb[1];
+        const int stq = channel_setup<1, RK>(gq.h, N, lane, Lambda, P, Q, Bv, C, dt, sm, qd, pa, dv, cc, bb);
+        const bool okq = stq == SSM_ST_OK;
+        const int sq = okq ? sm.s : 0;
+        cstl[qq][lane] = okq ? dv[0] : zero;
+        cstl[qq][NS + lane] = okq ? cc[0] : zero;
+        cstl[qq][2 * NS + lane] = okq ? bb[0] : zero;
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            cstl[qq][(3 + a) * NS + lane] = okq ? qd[0][a] : zero;
+            cstl[qq][(3 + RK + a) * NS + lane] = okq ? pa[0][a] : zero;
+        }
+        {
+            const int i = lane / kMaxOrder, j = lane % kMaxOrder, n = RK + sq;
+            mbl[qq][lane] = okq && i < n && j < n ? sm.Mbf[lane] : zero;
+        }
+        if (lane == 0) {
+            hdl[qq][0] = stq;
+            hdl[qq][1] = sq;
+            for (int zz = 0; zz < kMaxRank; ++zz) hdl[qq][2 + zz] = zz < sq ? sm.zidx[zz] : 0;
+        }
+        __syncthreads();  // the next set-up reuses sm
+    }
+    const int q = lane / kGroup, g = lane % kGroup;
+    const GroupSeq gs(blockIdx.x, q, nseq, H);
+    int zin[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) zin[zz] = hdl[q][2 + zz];
+    group_sequence<S, RK>(T, N, g, lane, gs.live, hdl[q][0], hdl[q][1], zin, mbl[q], cstl[q],
+                          D ? D[gs.h] : 0.0f, (size_t)gs.seq * T, (size_t)gs.seq * N,
+                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u, y, x);
+}
+
+template <int S>
+hipError_t launch_step16(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
+                         const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
+                         const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream) {
+    const int64_t nseq = Bsz * H;
+    const unsigned waves = (unsigned)((nseq + kWave / kGroup - 1) / (kWave / kGroup));
+#define SSM_STEP16(RK)                                                                                           \
+    if (r == RK) {                                                                                               \
+        hipLaunchKernelGGL((step16_kernel<S, RK>), dim3(waves), dim3(kWave), 0, stream, (int)nseq, (int)H,       \
+                           (int)N, (int)T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status);                         \
+        return hipGetLastError();                                                                                \
+    }
+    SSM_STEP16(1) SSM_STEP16(2) SSM_STEP16(3) SSM_STEP16(4)
+#undef SSM_STEP16
+    return hipErrorInvalidValue;
 }
 
 template <int S>
@@ -822,9 +920,18 @@ hipError_t launch_prepared_npl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int
 
 constexpr int64_t kStepMaxN = 4 * kWave;
 
+// lanes: 16 (N <= 64: four sequences per wave) or 64 (one per wave)
 hipError_t launch_step(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t T, const float2* Lambda,
                        const float2* P, const float2* Q, const float2* Bv, const float2* C, const float* dt,
-                       const float* D, const float* u, float* y, float2* x, int32_t* status, hipStream_t stream) {
+                       const float* D, const float* u, float* y, float2* x, int32_t* status, int lanes,
+                       hipStream_t stream) {
+    if (lanes == kGroup) {
+        if (N <= kGroup) return launch_step16<1>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+        if (N <= 2 * kGroup)
+            return launch_step16<2>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+        if (N <= kWave) return launch_step16<4>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
+        return hipErrorInvalidValue;
+    }
     if (N <= kWave) return launch_npl<1>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
     if (N <= 2 * kWave) return launch_npl<2>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);
     if (N <= kStepMaxN) return launch_npl<4>(Bsz, H, N, r, T, Lambda, P, Q, Bv, C, dt, D, u, y, x, status, stream);

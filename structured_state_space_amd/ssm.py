@@ -70,7 +70,7 @@ def _load():
     lib.ssm_forward.restype = i32
     lib.ssm_forward_profiled.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp, sz, vp, vp, ctypes.c_int32]
     lib.ssm_forward_profiled.restype = i32
-    lib.ssm_step.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
+    lib.ssm_step.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [ctypes.c_int32, vp]
     lib.ssm_step.restype = i32
     lib.ssm_step_prepare.argtypes = [i64, i64, i64] + [vp] * 7 + [sz, vp, vp]
     lib.ssm_step_prepare.restype = i32
@@ -274,10 +274,11 @@ def forward_complex(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, worksp
     return dict(y_re=y_re, y_im=y_im, K=K_out, status=status)
 
 
-def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):
+def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None, lanes=0):
     """ssm_step: T steps of the recurrence from the state x (zeros when None);
     returns dict(y [Bsz,H,T] f32, x [Bsz,H,N] c64 (the state after the last
-    step, updated in place when given), status [H] i32)."""
+    step, updated in place when given), status [H] i32).  lanes: 64 (one
+    sequence per wave), 16 (N <= 64: four per wave) or 0 (chosen per call)."""
     H, N, r, dev = _params(Lambda, P, Q, B, C, dt)
     Bsz, H2, T = u.shape
     if H2 != H:
@@ -294,7 +295,7 @@ def step(Lambda, P, Q, B, C, dt, D, u, x=None, y=None, status=None):
         status = torch.empty((H,), dtype=torch.int32, device=dev)
     _check(status, "status", torch.int32, (H,), dev)
     rc = lib.ssm_step(Bsz, H, N, r, T, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(C), _ptr(dt), _ptr(D), _ptr(u),
-                      _ptr(y), _ptr(x), _ptr(status), _stream(dev))
+                      _ptr(y), _ptr(x), _ptr(status), int(lanes), _stream(dev))
     if rc != OK:
         raise SSMError("ssm_step", rc)
     return dict(y=y, x=x, status=status)
@@ -324,9 +325,8 @@ def step_prepare(Lambda, P, Q, B, C, dt, prep=None, status=None):
 def step_prepared(prepared, D, u, x=None, y=None, status=None, lanes=0):
     """ssm_step_prepared: T steps of the recurrence from the state x (zeros
     when None) with the constants of step_prepare's result `prepared`;
-    returns dict(y, x, status) as step does.  lanes: 64 (step's recurrence,
-    the same values bit for bit), 16 (N <= 64: four sequences per wave,
-    equal up to float32 rounding) or 0 (chosen by the library per call)."""
+    returns dict(y, x, status) as step does, bit for bit in the same layout.
+    lanes: 64, 16 (N <= 64) or 0 (chosen by the library per call)."""
     prep, H, N, r = prepared["prep"], prepared["H"], prepared["N"], prepared["r"]
     dev = prep.device
     Bsz, H2, T = u.shape

@@ -83,10 +83,14 @@ int main(void) {
            SSM_ERR_INVALID_ARGUMENT, "complex null y_im");
     expect(ssm_forward_complex(2, 3, 4, 5, 16, c, c, c, c, c, f, NULL, f, fo, fo, NULL, NULL, FAKE, 1 << 30, NULL),
            SSM_ERR_UNSUPPORTED, "complex r");
-    expect(ssm_step(2, 3, 257, 1, 16, c, c, c, c, c, f, NULL, f, fo, co, NULL, NULL), SSM_ERR_UNSUPPORTED, "step N");
-    expect(ssm_step(2, 3, 4, 1, 0, c, c, c, c, c, f, NULL, f, fo, co, NULL, NULL), SSM_ERR_INVALID_ARGUMENT, "step T");
-    expect(ssm_step(2, 3, 4, 1, 16, c, c, c, c, c, f, NULL, f, fo, (ssm_c64*)FAKE_OFF(4), NULL, NULL),
+    expect(ssm_step(2, 3, 257, 1, 16, c, c, c, c, c, f, NULL, f, fo, co, NULL, 0, NULL), SSM_ERR_UNSUPPORTED,
+           "step N");
+    expect(ssm_step(2, 3, 4, 1, 0, c, c, c, c, c, f, NULL, f, fo, co, NULL, 0, NULL), SSM_ERR_INVALID_ARGUMENT,
+           "step T");
+    expect(ssm_step(2, 3, 4, 1, 16, c, c, c, c, c, f, NULL, f, fo, (ssm_c64*)FAKE_OFF(4), NULL, 0, NULL),
            SSM_ERR_INVALID_ARGUMENT, "step align");
+    expect(ssm_step(2, 3, 4, 1, 16, c, c, c, c, c, f, NULL, f, fo, co, NULL, 48, NULL), SSM_ERR_INVALID_ARGUMENT,
+           "step lanes");
     expect(ssm_workspace_bytes(SSM_OP_STEP_PREPARED, 0, 5, 256, 4, 0, &bytes), SSM_OK, "workspace prepared");
     expect(ssm_workspace_bytes(SSM_OP_STEP_PREPARED, 0, 5, 257, 4, 0, &bytes), SSM_ERR_UNSUPPORTED,
            "workspace prepared N");

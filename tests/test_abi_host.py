@@ -163,13 +163,15 @@ def test_forward_complex_workspace_and_rejects():
     (dict(x=None), ssm.ERR_INVALID_ARGUMENT),
     (dict(x=FAKE + 4), ssm.ERR_INVALID_ARGUMENT),    # state not 8-byte aligned
     (dict(u=FAKE + 2), ssm.ERR_INVALID_ARGUMENT),
+    (dict(lanes=32), ssm.ERR_INVALID_ARGUMENT),            # layouts: 0 (chosen), 16 or 64
+    (dict(lanes=16, N=65), ssm.ERR_INVALID_ARGUMENT),      # 16-lane groups hold at most 64 states
 ])
 def test_step_rejects_before_launch(kw, code):
     a = dict(Bsz=2, H=3, N=4, r=1, T=16, Lambda=FAKE, P=FAKE, Q=FAKE, B=FAKE, C=FAKE, dt=FAKE, D=None, u=FAKE,
-             y=FAKE, x=FAKE, status=None)
+             y=FAKE, x=FAKE, status=None, lanes=0)
     a.update(kw)
     assert ssm.lib.ssm_step(a["Bsz"], a["H"], a["N"], a["r"], a["T"], a["Lambda"], a["P"], a["Q"], a["B"], a["C"],
-                            a["dt"], a["D"], a["u"], a["y"], a["x"], a["status"], None) == code
+                            a["dt"], a["D"], a["u"], a["y"], a["x"], a["status"], a["lanes"], None) == code
 
 
 # --------------------------------------------------------------------------

@@ -53,14 +53,20 @@ def _oracle(p, h, u_rows, x0_rows):
     (2, 17, 3, 65, 2, "random"),    # rank 3
     (2, 9, 4, 1, 1, "random"),      # rank 4, a single step
 ])
-def test_step_matches_oracle(H, N, r, T, Bsz, kind):
+@pytest.mark.parametrize("lanes", [64, 16])
+def test_step_matches_oracle(H, N, r, T, Bsz, kind, lanes):
+    """Both layouts: one sequence per wave, and (N <= 64) four per wave in
+    16-lane groups."""
+    if lanes == 16 and N > 64:
+        pytest.skip("16-lane groups hold at most 64 states")
     ssm = _ssm()
     p = I.random_params(100 * H + N + T, H, N, r, T, lambda_kind=kind)
     u = I.random_input(N + T, Bsz, H, T)
     x0 = _random_state(N + r, Bsz, H, N)
     d = ssm.to_device(p, DEV)
     xt = torch.from_numpy(x0).to(DEV)
-    out = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], torch.from_numpy(u).to(DEV), x=xt)
+    out = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], torch.from_numpy(u).to(DEV), x=xt,
+                   lanes=lanes)
     torch.cuda.synchronize()
     assert np.all(_np(out["status"]) == 0)
     y, xT = _np(out["y"]), _np(out["x"])
@@ -157,3 +163,33 @@ def test_step_statuses():
     st, y, xT = _run(ps, u[:, :1, :].copy(), x0[:, :1, :1].copy())
     assert list(st) == [ssm.ST_SINGULAR_BILINEAR]
     assert np.isnan(y).all() and np.isnan(xT).all()
+
+
+def test_step_layout_choice():
+    """lanes = 0: 16-lane groups from three sequences per SIMD (4 SIMDs per
+    compute unit) and T >= 32 for ssm_step (T >= 8 for ssm_step_prepared),
+    else one sequence per wave; each call equals the fixed layout it picks,
+    bit for bit."""
+    ssm = _ssm()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    H, N, r = 64, 16, 1
+    Bsz = -(-3 * 4 * cus // H)           # just enough sequences
+    p = I.random_params(91, H, N, r, 40)
+    d = ssm.to_device(p, DEV)
+    prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+    for T, want_step, want_prep in [(40, 16, 16), (20, 64, 16), (4, 64, 64)]:
+        u = torch.from_numpy(I.random_input(92 + T, Bsz, H, T)).to(DEV)
+        run = lambda lanes: ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u, lanes=lanes)
+        runp = lambda lanes: ssm.step_prepared(prep, d["D"], u, lanes=lanes)
+        auto, fixed = run(0), run(want_step)
+        pauto, pfixed = runp(0), runp(want_prep)
+        torch.cuda.synchronize()
+        assert torch.equal(auto["y"], fixed["y"]) and torch.equal(auto["x"], fixed["x"]), f"ssm_step T={T}"
+        assert torch.equal(pauto["y"], pfixed["y"]) and torch.equal(pauto["x"], pfixed["x"]), f"prepared T={T}"
+    # one sequence fewer per SIMD budget: one sequence per wave throughout
+    Bsz_small = (3 * 4 * cus - 1) // H
+    u = torch.from_numpy(I.random_input(99, Bsz_small, H, 40)).to(DEV)
+    a = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u, lanes=0)
+    b = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u, lanes=64)
+    torch.cuda.synchronize()
+    assert torch.equal(a["y"], b["y"])
