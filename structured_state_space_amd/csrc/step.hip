@@ -548,6 +548,17 @@ __device__ __forceinline__ void row_allsum(float (&v)[K]) {
     for (int i = 0; i < K; ++i) v[i] += dpp_get<0x140>(v[i]);  // row_mirror
 }
 
+// c + a b and c - a b as four fused multiply-adds (a separate product and
+// sum would take two multiplies, two FMAs and two adds)
+__device__ __forceinline__ float2 c_fma(float2 a, float2 b, float2 c) {
+    return make_float2(fmaf(-a.y, b.y, fmaf(a.x, b.x, c.x)), fmaf(a.y, b.x, fmaf(a.x, b.y, c.y)));
+}
+__device__ __forceinline__ float2 c_fnma(float2 a, float2 b, float2 c) {
+    return make_float2(fmaf(a.y, b.y, fmaf(-a.x, b.x, c.x)), fmaf(-a.y, b.x, fmaf(-a.x, b.y, c.y)));
+}
+// Re(c + a b)
+__device__ __forceinline__ float c_fma_re(float2 a, float2 b, float c) { return fmaf(-a.y, b.y, fmaf(a.x, b.x, c)); }
+
 // value of lane (own group, index k) for every lane
 __device__ __forceinline__ float group_read(float v, int lane, int k) {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & ~(kGroup - 1)) | k) << 2, __float_as_int(v)));
@@ -583,14 +594,15 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
         const int k = t & (kGroup - 1);
         const float ut = group_read(ucur, lane, k);  // needed only at the end of the step
         // the lane's partial sums, seeded with its first state's terms
-        float2 sq[RK], sc = c_mul(cc[0], xs[0]);
+        float2 sq[RK];
+        float scr = c_fma_re(cc[0], xs[0], 0.0f);
 #pragma unroll
         for (int a = 0; a < RK; ++a) sq[a] = c_mul(qd[0][a], xs[0]);
 #pragma unroll
         for (int e = 1; e < S; ++e) {
 #pragma unroll
-            for (int a = 0; a < RK; ++a) sq[a] = c_add(sq[a], c_mul(qd[e][a], xs[e]));
-            sc = c_add(sc, c_mul(cc[e], xs[e]));
+            for (int a = 0; a < RK; ++a) sq[a] = c_fma(qd[e][a], xs[e], sq[a]);
+            scr = c_fma_re(cc[e], xs[e], scr);
         }
         {
             float v[2 * RK + 1];
@@ -599,15 +611,15 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
                 v[2 * a] = sq[a].x;
                 v[2 * a + 1] = sq[a].y;
             }
-            v[2 * RK] = sc.x;
+            v[2 * RK] = scr;
             row_allsum<2 * RK + 1>(v);
 #pragma unroll
             for (int a = 0; a < RK; ++a) sq[a] = make_float2(v[2 * a], v[2 * a + 1]);
-            sc.x = v[2 * RK];
+            scr = v[2 * RK];
         }
         if (t > 0) {  // y_{t-1} = Re(C^* x_{t-1}) + D u_{t-1}
             const int kp = (t - 1) & (kGroup - 1);
-            if (g == kp) yblk = sc.x + Dh * uprev;
+            if (g == kp) yblk = scr + Dh * uprev;
             if (kp == kGroup - 1 || t == T) {
                 const int t0 = (t - 1) & ~(kGroup - 1);
                 if (store && t0 + g < T) y[ub + t0 + g] = yblk;
@@ -622,9 +634,9 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
         if constexpr (NZ == 0) {
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
-                float2 acc = make_float2(0.0f, 0.0f);
+                float2 acc = c_mul(Mr[i][0], sq[0]);
 #pragma unroll
-                for (int j = 0; j < RK; ++j) acc = c_add(acc, c_mul(Mr[i][j], sq[j]));
+                for (int j = 1; j < RK; ++j) acc = c_fma(Mr[i][j], sq[j], acc);
                 sol[i] = acc;
             }
         } else {
@@ -657,7 +669,7 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
         for (int e = 0; e < S; ++e) {
             float2 gv = c_mul(dv[e], xs[e]);
 #pragma unroll
-            for (int a = 0; a < RK; ++a) gv = c_sub(gv, c_mul(pa[e][a], sol[a]));
+            for (int a = 0; a < RK; ++a) gv = c_fnma(pa[e][a], sol[a], gv);
             if constexpr (NZ > 0) {
 #pragma unroll
                 for (int zz = 0; zz < NZ; ++zz)
