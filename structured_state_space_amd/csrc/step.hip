@@ -73,6 +73,17 @@ __device__ __forceinline__ void wave_allsum(float (&v)[K]) {
     for (int i = 0; i < K; ++i) v[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), 63));
 }
 
+// c + a b and c - a b as four fused multiply-adds (a separate product and
+// sum would take two multiplies, two FMAs and two adds)
+__device__ __forceinline__ float2 c_fma(float2 a, float2 b, float2 c) {
+    return make_float2(fmaf(-a.y, b.y, fmaf(a.x, b.x, c.x)), fmaf(a.y, b.x, fmaf(a.x, b.y, c.y)));
+}
+__device__ __forceinline__ float2 c_fnma(float2 a, float2 b, float2 c) {
+    return make_float2(fmaf(a.y, b.y, fmaf(-a.x, b.x, c.x)), fmaf(-a.y, b.x, fmaf(-a.x, b.y, c.y)));
+}
+// Re(c + a b)
+__device__ __forceinline__ float c_fma_re(float2 a, float2 b, float c) { return fmaf(-a.y, b.y, fmaf(a.x, b.x, c)); }
+
 // The recurrence for one sequence: T steps from the state xs (updated in
 // place).  NZ: room for the bordered form's states in Z (0: Woodbury form).
 template <int NPL, int RK, int NZ>
@@ -97,32 +108,34 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
     float yblk = 0.0f;  // outputs of steps [t0, t0 + 64), lane = step - t0
     float uprev = 0.0f;
     for (int t = 0; t <= T; ++t) {
-        // sums over x_{t-1}: Q^* D^{-1} x (r of them) and C^* x
-        float2 sq[RK], sc = make_float2(0.0f, 0.0f);
+        // sums over x_{t-1}: Q^* D^{-1} x (r of them) and the real part of
+        // C^* x (the only part y uses), seeded with the first state's terms
+        float2 sq[RK];
+        float scr = c_fma_re(cc[0], xs[0], 0.0f);
 #pragma unroll
-        for (int a = 0; a < RK; ++a) sq[a] = make_float2(0.0f, 0.0f);
+        for (int a = 0; a < RK; ++a) sq[a] = c_mul(qd[0][a], xs[0]);
 #pragma unroll
-        for (int e = 0; e < NPL; ++e) {
+        for (int e = 1; e < NPL; ++e) {
 #pragma unroll
-            for (int a = 0; a < RK; ++a) sq[a] = c_add(sq[a], c_mul(qd[e][a], xs[e]));
-            sc = c_add(sc, c_mul(cc[e], xs[e]));
+            for (int a = 0; a < RK; ++a) sq[a] = c_fma(qd[e][a], xs[e], sq[a]);
+            scr = c_fma_re(cc[e], xs[e], scr);
         }
-        {  // the r sums and the real part of C^* x (the only part y uses)
+        {
             float v[2 * RK + 1];
 #pragma unroll
             for (int a = 0; a < RK; ++a) {
                 v[2 * a] = sq[a].x;
                 v[2 * a + 1] = sq[a].y;
             }
-            v[2 * RK] = sc.x;
+            v[2 * RK] = scr;
             wave_allsum<2 * RK + 1>(v);
 #pragma unroll
             for (int a = 0; a < RK; ++a) sq[a] = make_float2(v[2 * a], v[2 * a + 1]);
-            sc.x = v[2 * RK];
+            scr = v[2 * RK];
         }
         if (t > 0) {  // y_{t-1} = Re(C^* x_{t-1}) + D u_{t-1}
             const int k = (t - 1) & (kWave - 1);
-            if (lane == k) yblk = sc.x + Dh * uprev;
+            if (lane == k) yblk = scr + Dh * uprev;
             if (k == kWave - 1 || t == T) {
                 const int t0 = (t - 1) & ~(kWave - 1);
                 if (t0 + lane < T) y[ub + t0 + lane] = yblk;
@@ -140,9 +153,9 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
         if constexpr (NZ == 0) {
 #pragma unroll
             for (int i = 0; i < RK; ++i) {
-                float2 acc = make_float2(0.0f, 0.0f);
+                float2 acc = c_mul(Mr[i][0], sq[0]);
 #pragma unroll
-                for (int j = 0; j < RK; ++j) acc = c_add(acc, c_mul(Mr[i][j], sq[j]));
+                for (int j = 1; j < RK; ++j) acc = c_fma(Mr[i][j], sq[j], acc);
                 sol[i] = acc;
             }
         } else {
@@ -181,7 +194,7 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
         for (int e = 0; e < NPL; ++e) {
             float2 g = c_mul(dv[e], xs[e]);
 #pragma unroll
-            for (int a = 0; a < RK; ++a) g = c_sub(g, c_mul(pa[e][a], sol[a]));
+            for (int a = 0; a < RK; ++a) g = c_fnma(pa[e][a], sol[a], g);
             if constexpr (NZ > 0) {
 #pragma unroll
                 for (int zz = 0; zz < NZ; ++zz)
@@ -547,17 +560,6 @@ __device__ __forceinline__ void row_allsum(float (&v)[K]) {
 #pragma unroll
     for (int i = 0; i < K; ++i) v[i] += dpp_get<0x140>(v[i]);  // row_mirror
 }
-
-// c + a b and c - a b as four fused multiply-adds (a separate product and
-// sum would take two multiplies, two FMAs and two adds)
-__device__ __forceinline__ float2 c_fma(float2 a, float2 b, float2 c) {
-    return make_float2(fmaf(-a.y, b.y, fmaf(a.x, b.x, c.x)), fmaf(a.y, b.x, fmaf(a.x, b.y, c.y)));
-}
-__device__ __forceinline__ float2 c_fnma(float2 a, float2 b, float2 c) {
-    return make_float2(fmaf(a.y, b.y, fmaf(-a.x, b.x, c.x)), fmaf(-a.y, b.x, fmaf(-a.x, b.y, c.y)));
-}
-// Re(c + a b)
-__device__ __forceinline__ float c_fma_re(float2 a, float2 b, float c) { return fmaf(-a.y, b.y, fmaf(a.x, b.x, c)); }
 
 // value of lane (own group, index k) for every lane
 __device__ __forceinline__ float group_read(float v, int lane, int k) {
