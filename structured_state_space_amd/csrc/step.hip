@@ -497,18 +497,10 @@ __global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, in
     const size_t ub = (size_t)seq * T;
     const uint8_t* base = prep + (size_t)h * chan_bytes;
     const int32_t* hd = reinterpret_cast<const int32_t*>(base);
-    int st = hd[3];
-    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
-    if (st != SSM_ST_OK) {
-        fail_sequence(lane, N, T, ub, xb, y, x);
-        if (lane == 0 && b == 0 && status) status[h] = st;
-        return;
-    }
-    const int s = min(max(hd[4], 0), RK);
-    int zidx[kMaxRank];
-#pragma unroll
-    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(hd[5 + zz], 0), NPL * kWave - 1);
-    mbf[lane] = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4)[lane];
+    // every load is issued before the header is looked at (the block and
+    // the state are in bounds whatever it holds), so that a short call
+    // waits for one memory round trip instead of two
+    const float2 mbv = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4)[lane];
     const float2* cst = reinterpret_cast<const float2*>(base + kPrepConstOffset);
     constexpr int NS = NPL * kWave;
     float2 qd[NPL][RK], pa[NPL][RK], dv[NPL], cc[NPL], bb[NPL], xs[NPL];
@@ -525,9 +517,21 @@ __global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, in
         }
         xs[e] = j < N ? x[xb + j] : make_float2(0.0f, 0.0f);
     }
+    const float Dh = D ? D[h] : 0.0f;
+    int st = hd[3];
+    if (hd[0] != kPrepMagic || hd[1] != N || hd[2] != RK) st = SSM_ST_UNPREPARED;
+    if (st != SSM_ST_OK) {
+        fail_sequence(lane, N, T, ub, xb, y, x);
+        if (lane == 0 && b == 0 && status) status[h] = st;
+        return;
+    }
+    const int s = min(max(hd[4], 0), RK);
+    int zidx[kMaxRank];
+#pragma unroll
+    for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(hd[5 + zz], 0), NPL * kWave - 1);
+    mbf[lane] = mbv;
     int zs[NPL], zl[kMaxRank], ze[kMaxRank];
     z_slots<NPL>(lane, s, zidx, zs, zl, ze);
-    const float Dh = D ? D[h] : 0.0f;
     __syncthreads();
     if (s == 0)
         recur<NPL, RK, 0>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
@@ -685,7 +689,8 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
 
 // One group's sequence from its channel's constants: cst holds the 64-slot
 // arrays of the prepared layout (d^{-1}, conj C, Bbar, Q^* D^{-1}, alpha
-// D^{-1} P), mbq the order r + s inverse (in LDS), st, s_in and zin the
+// D^{-1} P), mbq the order r + s inverse (in LDS, written by the caller;
+// this routine meets the barrier after its own loads), st, s_in and zin the
 // channel's status, |Z| and Z.  A group past the end (live false) runs
 // along without storing.  Every lane of the wave must call it together (the
 // sums are row-wise DPP, the choice of loop wave-uniform).
@@ -696,6 +701,33 @@ __device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bo
                                                const float* __restrict__ u, float* __restrict__ y,
                                                float2* __restrict__ x) {
     const bool ok = st == SSM_ST_OK;
+    // constants of states g + 16 e (zero past N), all zero for a failing
+    // group so that it runs the loop harmlessly; loaded whatever the status
+    // (in bounds either way) and selected after
+    constexpr int NS = kWave;
+    const float2 zero = make_float2(0.0f, 0.0f);
+    float2 qd[S][RK], pa[S][RK], dv[S], cc[S], bb[S], xs[S];
+#pragma unroll
+    for (int e = 0; e < S; ++e) {
+        const int j = g + kGroup * e;
+        dv[e] = cst[j];
+        cc[e] = cst[NS + j];
+        bb[e] = cst[2 * NS + j];
+#pragma unroll
+        for (int a = 0; a < RK; ++a) {
+            qd[e][a] = cst[(3 + a) * NS + j];
+            pa[e][a] = cst[(3 + RK + a) * NS + j];
+        }
+        xs[e] = j < N ? x[xb + j] : zero;
+    }
+    if (!ok) {
+#pragma unroll
+        for (int e = 0; e < S; ++e) {
+            dv[e] = cc[e] = bb[e] = xs[e] = zero;
+#pragma unroll
+            for (int a = 0; a < RK; ++a) qd[e][a] = pa[e][a] = zero;
+        }
+    }
     if (live && !ok) {  // NaN outputs now; the loop below stores nothing for this group
         const float nanf = __builtin_nanf("");
         for (int t = g; t < T; t += kGroup) y[ub + t] = nanf;
@@ -706,24 +738,6 @@ __device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bo
     int zidx[kMaxRank];
 #pragma unroll
     for (int zz = 0; zz < kMaxRank; ++zz) zidx[zz] = min(max(zin[zz], 0), S * kGroup - 1);
-    // constants of states g + 16 e (zero past N), all zero for a failing
-    // group so that it runs the loop harmlessly
-    constexpr int NS = kWave;
-    const float2 zero = make_float2(0.0f, 0.0f);
-    float2 qd[S][RK], pa[S][RK], dv[S], cc[S], bb[S], xs[S];
-#pragma unroll
-    for (int e = 0; e < S; ++e) {
-        const int j = g + kGroup * e;
-        dv[e] = ok ? cst[j] : zero;
-        cc[e] = ok ? cst[NS + j] : zero;
-        bb[e] = ok ? cst[2 * NS + j] : zero;
-#pragma unroll
-        for (int a = 0; a < RK; ++a) {
-            qd[e][a] = ok ? cst[(3 + a) * NS + j] : zero;
-            pa[e][a] = ok ? cst[(3 + RK + a) * NS + j] : zero;
-        }
-        xs[e] = ok && j < N ? x[xb + j] : zero;
-    }
     int zs[S], zl[kMaxRank], ze[kMaxRank];
 #pragma unroll
     for (int e = 0; e < S; ++e) {
@@ -739,6 +753,7 @@ __device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bo
         ze[zz] = j / kGroup;
     }
     const bool store = live && ok;
+    __syncthreads();  // mbq (written by the caller) is complete
     if (__ballot(s > 0) == 0)
         recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
     else
@@ -786,9 +801,10 @@ __global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H,
     for (int zz = 0; zz < kMaxRank; ++zz) zin[zz] = hd[5 + zz];
     const float2* mb = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4);
 #pragma unroll
-    for (int i = 0; i < kMaxOrder * kMaxOrder / kGroup; ++i)
-        mbf[q][g + kGroup * i] = st == SSM_ST_OK ? mb[g + kGroup * i] : make_float2(0.0f, 0.0f);
-    __syncthreads();
+    for (int i = 0; i < kMaxOrder * kMaxOrder / kGroup; ++i) {
+        const float2 v = mb[g + kGroup * i];
+        mbf[q][g + kGroup * i] = st == SSM_ST_OK ? v : make_float2(0.0f, 0.0f);
+    }
     group_sequence<S, RK>(T, N, g, lane, gs.live, st, hd[4], zin, mbf[q],
                           reinterpret_cast<const float2*>(base + kPrepConstOffset), D ? D[gs.h] : 0.0f,
                           (size_t)gs.seq * T, (size_t)gs.seq * N,
