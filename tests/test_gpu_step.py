@@ -193,3 +193,35 @@ def test_step_layout_choice():
     b = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], u, lanes=64)
     torch.cuda.synchronize()
     assert torch.equal(a["y"], b["y"])
+
+
+def test_step_full_size_grouped_layout():
+    """s4-h512-l3k at full size (16 x 512 sequences of 3000 steps, N = 64),
+    the layout left to the library (16-lane groups here), for ssm_step and
+    ssm_step_prepared: from a zero state every row must reproduce the
+    filter path's output (ssm_forward, itself checked against the oracle at
+    this size), and sampled sequences also the oracle's recurrence."""
+    from tests.parity import sample_channels
+    ssm = _ssm()
+    w, p, u = I.workload("s4-h512-l3k")
+    d = ssm.to_device(p, DEV)
+    ut = torch.from_numpy(u).to(DEV)
+    Ct = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], p.L, want_bbar=False)["Ctilde"]
+    yf = _np(ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut)["y"])
+    st = ssm.step(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"], ut)
+    prep = ssm.step_prepare(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"])
+    sp = ssm.step_prepared(prep, d["D"], ut)
+    torch.cuda.synchronize()
+    for name, out in (("ssm_step", st), ("ssm_step_prepared", sp)):
+        assert int(out["status"].abs().max()) == 0
+        ys = _np(out["y"])
+        for h in range(w.H):
+            assert_rows_close(ys[:, h, :], yf[:, h, :], what=f"{name} vs forward h{h}")
+    # ssm_step and ssm_step_prepared take the same layout here: equal bit for bit
+    assert torch.equal(st["y"], sp["y"]) and torch.equal(st["x"], sp["x"])
+    ys, xs = _np(st["y"]), _np(st["x"])
+    for h in sample_channels(w.H, 3):
+        b = int(h) % w.Bsz
+        yr, xr = _oracle(p, int(h), u[b:b + 1, h, :], np.zeros((1, w.N), np.complex64))
+        assert_rows_close(ys[b:b + 1, h, :], yr, what=f"y b{b} h{h}")
+        assert_rows_close(xs[b:b + 1, h, :], xr, what=f"final state b{b} h{h}")
