@@ -22,7 +22,11 @@ Source pages (cited by title and block):
          - block for S4 Algorithm 1 / App. C: the recurrent solver, the filter
            mode with root values H(z_k), the z = -1 formula, the mu-form
            Cauchy products and the statuses resonant-diagonal,
-           resonant-correction and singular-bilinear-matrix.
+           resonant-correction and singular-bilinear-matrix;
+         - block on the Cauchy matrix-vector product at the roots of unity
+           and the theorem on its operation count: the balanced product
+           tree, the fold modulo z^M - 1, the odd-s reindexing and the
+           collision status.
   [EX]   "Recurrent, LSTM, and structured state-space models -- Examples",
          the scalar example A = 0, B = C = 1, dt = 1, D = 0 (S4 sec. 2.3-2.4).
 
@@ -33,9 +37,10 @@ Readings where the pages are silent (each also listed in the design notes):
     standard form (D + U V^*)^{-1} = D^{-1} - D^{-1} U W^{-1} V^* D^{-1},
     W = I_r + V^* D^{-1} U, is used.
 
-Parity pins for every function live in tests/test_oracle_pins.py; each is
-checked against closed forms, the worked example, brute force on tiny inputs
-or an independent library routine.  No function here is "parity unpinned".
+Parity pins for every function live in tests/test_oracle_pins.py (the
+product tree's in tests/test_product_tree_oracle.py); each is checked against
+closed forms, the worked example, brute force on tiny inputs or an
+independent library routine.  No function here is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -360,6 +365,143 @@ def root_values_cauchy(Lambda, P, Q, B, Ctilde, dt, M):
             status = worst_status(status, RESONANT_CORRECTION)
             continue
         out[k] = S_CB - beta * (S_CP @ x)
+    return out, status
+
+
+# ---------------------------------------------------------------------------
+# Roots-of-unity Cauchy product by the balanced product tree
+# ([RSS] block on the Cauchy matrix-vector product at the roots of unity, and
+# the theorem on its operation count)
+# ---------------------------------------------------------------------------
+COLLISION = "collision"
+
+
+def _tree(mu, a, lo, hi):
+    """(D_I, P_I) for the index interval [lo, hi) as ascending coefficient
+    arrays: a leaf j gives D = z - mu_j, P = a_j; an internal node splits its
+    interval into halves whose sizes differ by at most one and combines
+    D = D1 D2, P = P1 D2 + D1 P2 (np.convolve is the polynomial product)."""
+    if hi - lo == 1:
+        return np.array([-mu[lo], 1.0 + 0.0j]), np.array([a[lo]], np.complex128)
+    mid = lo + (hi - lo) // 2
+    D1, P1 = _tree(mu, a, lo, mid)
+    D2, P2 = _tree(mu, a, mid, hi)
+    D = np.convolve(D1, D2)
+    P12, P21 = np.convolve(P1, D2), np.convolve(D1, P2)
+    P = np.zeros(max(len(P12), len(P21)), np.complex128)
+    P[:len(P12)] += P12
+    P[:len(P21)] += P21
+    return D, P
+
+
+def _fold(c, M):
+    """Coefficients modulo z^M - 1: degree r collects every degree = r mod M."""
+    out = np.zeros(M, np.complex128)
+    for d, v in enumerate(c):
+        out[d % M] += v
+    return out
+
+
+def cauchy_product_tree(mu, a, M, omega=None):
+    """y_k = sum_j a_j / (omega^k - mu_j), 0 <= k < M = 2^q, by the balanced
+    product tree: the root's D and P folded modulo z^M - 1, both evaluated at
+    omega_0^j (omega_0 = e^{-2 pi i / M}) by the radix-two DFT, and, for a
+    primitive root omega other than omega_0, reindexed through the odd s
+    with omega = omega_0^s (value at index s k mod M goes to output k).
+    Repeated poles are allowed; n = 0 gives zeros.  A zero D(omega^k) gives
+    the status collision (values NaN).  Returns (y [M] complex128, status).
+
+    Readings: omega defaults to omega_0; the search for s compares the M
+    powers of omega_0 with omega to within 1e-12 (exact equality is not
+    available in floating point) and requires exactly one odd match."""
+    if M < 1 or (M & (M - 1)) != 0:
+        raise ValueError("M must be a power of two")
+    mu = np.asarray(mu, np.complex128).ravel()
+    a = np.asarray(a, np.complex128).ravel()
+    n = len(mu)
+    if n == 0:
+        return np.zeros(M, np.complex128), OK
+    D, P = _tree(mu, a, 0, n)
+    Dv = radix2_dft(_fold(D, M))
+    Pv = radix2_dft(_fold(P, M))
+    if M > 1:
+        w0 = _primitive_root(M, False)
+        w = w0 if omega is None else complex(omega)
+        powers = [w0 ** m for m in range(M)]
+        odd = [m for m in range(1, M, 2) if abs(powers[m] - w) <= 1e-12]
+        if len(odd) != 1:
+            raise ValueError("omega is not a primitive M-th root of unity")
+        sidx = odd[0]
+        idx = [(sidx * k) % M for k in range(M)]
+        Dv, Pv = Dv[idx], Pv[idx]
+    if np.any(Dv == 0):
+        return np.full(M, np.nan + 0j), COLLISION
+    return Pv / Dv, OK
+
+
+def root_values_product_tree(Lambda, P, Q, B, Ctilde, dt, M):
+    """H(z_k) as root_values_cauchy, each scalar Cauchy product S_uv by the
+    balanced product tree (poles mu_j, weights -2 conj(u_j) v_j / (a +
+    lambda_j)) plus the constant of the states with lambda_j = -a.  A
+    collision (some mu_j equal to a root) gives resonant-diagonal at every
+    root (the tree reports it for the whole grid); the root -1 is handled
+    directly.  Returns (values, status)."""
+    lam = np.asarray(Lambda, np.complex128)
+    N = len(lam)
+    P = np.asarray(P, np.complex128).reshape(N, -1)
+    Q = np.asarray(Q, np.complex128).reshape(N, -1)
+    B = np.asarray(B, np.complex128)
+    Ct = np.asarray(Ctilde, np.complex128)
+    r = P.shape[1]
+    a = 2.0 / dt
+    exc = lam == -a
+    reg = ~exc
+    mu = (a - lam[reg]) / (a + lam[reg])
+    z = roots_of_unity(M)
+
+    def S(uvec, vvec):
+        w = uvec.conj() * vvec
+        y, st = cauchy_product_tree(mu, -2.0 * w[reg] / (a + lam[reg]), M)
+        return y + (dt / 2.0) * np.sum(w[exc]), st
+
+    fams = {}
+    status = OK
+    for key, (uu, vv) in {"CB": (Ct, B)}.items():
+        fams[key], st = S(uu, vv)
+        if st != OK:
+            status = RESONANT_DIAGONAL
+    S_CP = []
+    S_QB = []
+    S_QP = [[None] * r for _ in range(r)]
+    for b in range(r):
+        y, st = S(Ct, P[:, b])
+        S_CP.append(y)
+        status = RESONANT_DIAGONAL if st != OK else status
+        y, st = S(Q[:, b], B)
+        S_QB.append(y)
+        status = RESONANT_DIAGONAL if st != OK else status
+        for c in range(r):
+            y, st = S(Q[:, b], P[:, c])
+            S_QP[b][c] = y
+            status = RESONANT_DIAGONAL if st != OK else status
+    out = np.full(M, np.nan + 0j)
+    if status != OK:
+        for k in range(M):
+            if _is_minus_one(M, k):
+                out[k] = (dt / 2.0) * np.vdot(Ct, B)
+        return out, status
+    for k in range(M):
+        if _is_minus_one(M, k):
+            out[k] = (dt / 2.0) * np.vdot(Ct, B)
+            continue
+        beta = (1.0 + z[k]) / 2.0
+        W = np.eye(r, dtype=np.complex128) + beta * np.array([[S_QP[i][j][k] for j in range(r)] for i in range(r)])
+        try:
+            x = np.linalg.solve(W, np.array([S_QB[i][k] for i in range(r)]))
+        except np.linalg.LinAlgError:
+            status = worst_status(status, RESONANT_CORRECTION)
+            continue
+        out[k] = fams["CB"][k] - beta * (np.array([S_CP[i][k] for i in range(r)]) @ x)
     return out, status
 
 
