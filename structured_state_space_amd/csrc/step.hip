@@ -18,11 +18,14 @@
 // Q^* D^{-1} x_{t-1} and C^* x_{t-1}, which gives y_{t-1}), reads x_{t-1} at Z,
 // solves with Mb^{-1} and updates its states.
 //
-// Work split: one 64-lane wave per sequence (batch row b, channel h); lane l
-// holds states l + 64 e, e < NPL.  The channel's set-up (d, Z, Mb^{-1}, Bbar)
-// is computed in float64 by the wave itself; the recurrence runs in float32.
-// Inputs and outputs move in blocks of 64 steps (one coalesced load or store
-// per block, the next input block fetched one block ahead).
+// Work split, two layouts.  One 64-lane wave per sequence (batch row b,
+// channel h): lane l holds states l + 64 e, e < NPL; the channel's set-up
+// (d, Z, Mb^{-1}, Bbar) is computed in float64 by the wave itself; inputs and
+// outputs move in blocks of 64 steps (one coalesced load or store per block,
+// the next input block fetched one block ahead).  Or, for N <= 64, 16-lane
+// groups with four sequences per wave (below).  The recurrence runs in
+// float32.  The set-up can also be written once to a buffer (the prepared
+// layout) and read by later calls.
 #include <float.h>
 
 #include "bilinear.hpp"
