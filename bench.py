@@ -11,7 +11,7 @@ reported separately.  All inputs are resident in HBM before timing starts.
 Prints one JSON line: the headline metric (channel-steps/s = Bsz*H*L per
 second), the roofline of the dominant kernel measured live with HIP events on
 the launch stream, and the complex128 CPU oracle timed on a bounded sample on
-this host.  --gpus N > 1 exits: this build runs on one GPU.
+this host.  --gpus N > 1 exits: the benchmark measures one GPU.
 """
 from __future__ import annotations
 
@@ -407,7 +407,7 @@ def main():
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: the S4 filter path shards over channels with no exchange, "
-              "and this build measures the one-GPU share (use --gpus 1).", file=sys.stderr)
+              "and the benchmark measures the one-GPU share (use --gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np
