@@ -87,14 +87,24 @@ __device__ __forceinline__ float2 c_fnma(float2 a, float2 b, float2 c) {
 // Re(c + a b)
 __device__ __forceinline__ float c_fma_re(float2 a, float2 b, float c) { return fmaf(-a.y, b.y, fmaf(a.x, b.x, c)); }
 
+// The first two blocks of a sequence's inputs, lane i holding step i and
+// step B + i of blocks of B steps (indexes past the end clamped to the last)
+template <int B>
+__device__ __forceinline__ void first_inputs(const float* __restrict__ u, size_t ub, int T, int i, float& ucur,
+                                             float& unext) {
+    ucur = u[ub + min(i, T - 1)];
+    unext = u[ub + min(B + i, T - 1)];
+}
+
 // The recurrence for one sequence: T steps from the state xs (updated in
 // place).  NZ: room for the bordered form's states in Z (0: Woodbury form).
 template <int NPL, int RK, int NZ>
 __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const float2* Mbf, const int (&zl)[kMaxRank],
                                       const int (&ze)[kMaxRank], const float2 (&qd)[NPL][RK],
                                       const float2 (&pa)[NPL][RK], const float2 (&dv)[NPL], const float2 (&cc)[NPL],
-                                      const float2 (&bb)[NPL], const int (&zs)[NPL], float Dh,
-                                      const float* __restrict__ u, float* __restrict__ y, float2 (&xs)[NPL]) {
+                                      const float2 (&bb)[NPL], const int (&zs)[NPL], float Dh, float ucur,
+                                      float unext, const float* __restrict__ u, float* __restrict__ y,
+                                      float2 (&xs)[NPL]) {
     constexpr int NO = RK + NZ;  // largest order of the small solve
     float2 Mr[NZ == 0 ? RK : 1][NZ == 0 ? RK : 1];
     if constexpr (NZ == 0) {
@@ -103,11 +113,9 @@ __device__ __forceinline__ void recur(int T, int lane, size_t ub, int n, const f
 #pragma unroll
             for (int j = 0; j < RK; ++j) Mr[i][j] = Mbf[i * kMaxOrder + j];
     }
-    // inputs of steps [t0, t0 + 64) and the next block; lanes past the end
-    // read the last input instead (never used), so the loads carry no branch
-    // and are waited for only where used
-    float ucur = u[ub + min(lane, T - 1)];
-    float unext = u[ub + min(kWave + lane, T - 1)];
+    // ucur, unext: inputs of steps [0, 64) and [64, 128), loaded by the
+    // caller (first_inputs) as early as it can; lanes past the end hold the
+    // last input instead (never used), so the loads carry no branch
     float yblk = 0.0f;  // outputs of steps [t0, t0 + 64), lane = step - t0
     float uprev = 0.0f;
     for (int t = 0; t <= T; ++t) {
@@ -413,10 +421,12 @@ __global__ __launch_bounds__(kWave) void step_kernel(int Bsz, int H, int N, int 
     // channels with no zero d_j (the usual case) take the Woodbury form, whose
     // r x r inverse stays in registers; the bordered form re-reads its order
     // r + s inverse from LDS every step
+    float u0, u1;
+    first_inputs<kWave>(u, ub, T, lane, u0, u1);
     if (s == 0)
-        recur<NPL, RK, 0>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, 0>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u0, u1, u, y, xs);
     else
-        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, sm.Mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u0, u1, u, y, xs);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
         const int j = lane + kWave * e;
@@ -500,9 +510,11 @@ __global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, in
     const size_t ub = (size_t)seq * T;
     const uint8_t* base = prep + (size_t)h * chan_bytes;
     const int32_t* hd = reinterpret_cast<const int32_t*>(base);
-    // every load is issued before the header is looked at (the block and
-    // the state are in bounds whatever it holds), so that a short call
-    // waits for one memory round trip instead of two
+    // every load is issued before the header is looked at (the block, the
+    // state and the inputs are in bounds whatever it holds), so that a short
+    // call waits for one memory round trip instead of two
+    float u0, u1;
+    first_inputs<kWave>(u, ub, T, lane, u0, u1);
     const float2 mbv = reinterpret_cast<const float2*>(base + kPrepHeaderWords * 4)[lane];
     const float2* cst = reinterpret_cast<const float2*>(base + kPrepConstOffset);
     constexpr int NS = NPL * kWave;
@@ -537,9 +549,9 @@ __global__ __launch_bounds__(kWave) void step_prepared_kernel(int Bsz, int H, in
     z_slots<NPL>(lane, s, zidx, zs, zl, ze);
     __syncthreads();
     if (s == 0)
-        recur<NPL, RK, 0>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, 0>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u0, u1, u, y, xs);
     else
-        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u, y, xs);
+        recur<NPL, RK, kMaxRank>(T, lane, ub, RK + s, mbf, zl, ze, qd, pa, dv, cc, bb, zs, Dh, u0, u1, u, y, xs);
 #pragma unroll
     for (int e = 0; e < NPL; ++e) {
         const int j = lane + kWave * e;
@@ -583,8 +595,8 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
                                         const int (&zl)[kMaxRank], const int (&ze)[kMaxRank],
                                         const float2 (&qd)[S][RK], const float2 (&pa)[S][RK], const float2 (&dv)[S],
                                         const float2 (&cc)[S], const float2 (&bb)[S], const int (&zs)[S], float Dh,
-                                        bool store, const float* __restrict__ u, float* __restrict__ y,
-                                        float2 (&xs)[S]) {
+                                        bool store, float ucur, float unext, const float* __restrict__ u,
+                                        float* __restrict__ y, float2 (&xs)[S]) {
     constexpr int NO = RK + NZ;
     float2 Mr[NZ == 0 ? RK : 1][NZ == 0 ? RK : 1];
     if constexpr (NZ == 0) {
@@ -593,10 +605,9 @@ __device__ __forceinline__ void recur16(int T, int g, int lane, size_t ub, int n
 #pragma unroll
             for (int j = 0; j < RK; ++j) Mr[i][j] = Mbf[i * kMaxOrder + j];
     }
-    // inputs of steps [t0, t0 + 16) (lane g holds step t0 + g) and the next
-    // block; indexes past the end read the last input (never used)
-    float ucur = u[ub + min(g, T - 1)];
-    float unext = u[ub + min(kGroup + g, T - 1)];
+    // ucur, unext: inputs of steps [0, 16) and [16, 32) (lane g holds step
+    // t0 + g), loaded by the caller; indexes past the end hold the last
+    // input (never used)
     float yblk = 0.0f;
     float uprev = 0.0f;
     for (int t = 0; t <= T; ++t) {
@@ -701,8 +712,8 @@ template <int S, int RK>
 __device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bool live, int st, int s_in,
                                                const int (&zin)[kMaxRank], const float2* mbq, const float2* cst,
                                                float Dh, size_t ub, size_t xb, int32_t* status_slot,
-                                               const float* __restrict__ u, float* __restrict__ y,
-                                               float2* __restrict__ x) {
+                                               float u0, float u1, const float* __restrict__ u,
+                                               float* __restrict__ y, float2* __restrict__ x) {
     const bool ok = st == SSM_ST_OK;
     // constants of states g + 16 e (zero past N), all zero for a failing
     // group so that it runs the loop harmlessly; loaded whatever the status
@@ -758,9 +769,11 @@ __device__ __forceinline__ void group_sequence(int T, int N, int g, int lane, bo
     const bool store = live && ok;
     __syncthreads();  // mbq (written by the caller) is complete
     if (__ballot(s > 0) == 0)
-        recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
+        recur16<S, RK, 0>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u0, u1, u, y,
+                          xs);
     else
-        recur16<S, RK, kMaxRank>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u, y, xs);
+        recur16<S, RK, kMaxRank>(T, g, lane, ub, RK + s, mbq, zl, ze, qd, pa, dv, cc, bb, zs, Dh, store, u0, u1, u,
+                                 y, xs);
     if (store) {
 #pragma unroll
         for (int e = 0; e < S; ++e) {
@@ -795,6 +808,8 @@ __global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H,
     const int lane = threadIdx.x;
     const int q = lane / kGroup, g = lane % kGroup;
     const GroupSeq gs(blockIdx.x, q, nseq, H);
+    float u0, u1;
+    first_inputs<kGroup>(u, (size_t)gs.seq * T, T, g, u0, u1);
     const uint8_t* base = prep + (size_t)gs.h * chan_bytes;
     const int32_t* hd = reinterpret_cast<const int32_t*>(base);
     int st = hd[3];
@@ -811,7 +826,7 @@ __global__ __launch_bounds__(kWave) void step_prepared16_kernel(int nseq, int H,
     group_sequence<S, RK>(T, N, g, lane, gs.live, st, hd[4], zin, mbf[q],
                           reinterpret_cast<const float2*>(base + kPrepConstOffset), D ? D[gs.h] : 0.0f,
                           (size_t)gs.seq * T, (size_t)gs.seq * N,
-                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u, y, x);
+                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u0, u1, u, y, x);
 }
 
 // ssm_step in 16-lane groups: the wave runs the float64 set-up of its four
@@ -862,12 +877,14 @@ __global__ __launch_bounds__(kWave) void step16_kernel(int nseq, int H, int N, i
     }
     const int q = lane / kGroup, g = lane % kGroup;
     const GroupSeq gs(blockIdx.x, q, nseq, H);
+    float u0, u1;
+    first_inputs<kGroup>(u, (size_t)gs.seq * T, T, g, u0, u1);
     int zin[kMaxRank];
 #pragma unroll
     for (int zz = 0; zz < kMaxRank; ++zz) zin[zz] = hdl[q][2 + zz];
     group_sequence<S, RK>(T, N, g, lane, gs.live, hdl[q][0], hdl[q][1], zin, mbl[q], cstl[q],
                           D ? D[gs.h] : 0.0f, (size_t)gs.seq * T, (size_t)gs.seq * N,
-                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u, y, x);
+                          gs.live && gs.b == 0 && status ? status + gs.h : nullptr, u0, u1, u, y, x);
 }
 
 template <int S>
