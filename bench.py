@@ -32,7 +32,7 @@ UNIT = "channel-steps/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3       # MI355X FP32: dense matrix (MFMA) and vector peaks are both 157.3
 PEAK_FP64_TFLOPS = 78.6        # MI355X FP64 vector
-DEFAULT_WORKLOAD = "s4-h256-l1k"
+DEFAULT_WORKLOAD = "s4-h1k-l16k"   # the largest workload: most channel-steps and bytes
 
 KERNEL_SOURCES = {
     "filter": ["single_launch.hip", "roots.hpp", "fft.hpp", "common.hpp"],
@@ -89,23 +89,74 @@ def read_traffic(kernel, workload):
     return (fetch + write) * 1024.0
 
 
-def cpu_baseline(w, p, u, seconds):
-    """The oracle as it stands, one thread, on a bounded channel sample."""
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_workers():
+    """Worker processes for the CPU baseline: the cores this process may run
+    on, at most 16 (the host share of one GPU)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
+
+
+_CPU_JOB = {}
+
+
+def _cpu_worker(args):
+    """One worker: whole channels of the shard, one BLAS thread, until the time
+    budget is spent (at least one channel)."""
     from threadpoolctl import threadpool_limits
 
     import oracle as O
-    done = 0
-    t0 = time.perf_counter()
+    chans, seconds = args
+    p, u = _CPU_JOB["p"], _CPU_JOB["u"]
+    done, t0 = 0, time.perf_counter()
     with threadpool_limits(limits=1):
-        while done < w.H and time.perf_counter() - t0 < seconds:
-            c = p.channel(done)
-            O.channel_reference(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], c["D"], u[:, done, :], p.L)
+        for h in chans:
+            c = p.channel(int(h))
+            O.channel_reference(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], c["D"], u[:, int(h), :], p.L)
             done += 1
-    dt = time.perf_counter() - t0
-    return {"value": done * w.Bsz * w.L / dt, "unit": UNIT, "cores": 1, "kind": "oracle",
-            "sample": f"{done} of {w.H} channels x {w.Bsz} rows x {w.L} steps of workload {w.name}: "
-                      f"complex128 dense discretisation, kernel by matrix iteration, time-stepped recurrence "
-                      f"({dt:.1f} s, one thread)"}
+            if time.perf_counter() - t0 >= seconds:
+                break
+    return done, time.perf_counter() - t0
+
+
+def cpu_baseline(w, p, u, seconds):
+    """The oracle as it stands on this host's cores: one worker process per
+    core (one BLAS thread each), channels sharded round-robin, each worker
+    stopping after about `seconds`.  Runs before the GPU is touched, so the
+    workers are plain forks of a process with no device state."""
+    import multiprocessing as mp
+
+    nw = host_workers()
+    shards = [list(range(i, w.H, nw)) for i in range(nw)]
+    shards = [s for s in shards if s]
+    _CPU_JOB.update(p=p, u=u)
+    t0 = time.perf_counter()
+    with mp.get_context("fork").Pool(len(shards)) as pool:
+        res = pool.map(_cpu_worker, [(s, seconds) for s in shards])
+    wall = time.perf_counter() - t0
+    _CPU_JOB.clear()
+    chans = sum(d for d, _ in res)
+    busy = max(t for _, t in res)
+    return {"value": chans * w.Bsz * w.L / busy, "unit": UNIT, "cores": len(shards), "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{chans} of {w.H} channels x {w.Bsz} rows x {w.L} steps of workload {w.name} on "
+                      f"{len(shards)} worker processes (one BLAS thread each, channels sharded round-robin, each "
+                      f"worker stopping after ~{seconds:.0f} s): complex128 dense discretisation, kernel by matrix "
+                      f"iteration, time-stepped recurrence; rate = channel-steps done / longest worker time "
+                      f"({busy:.1f} s; {wall:.1f} s wall with pool start-up)"}
 
 
 STEP_METRIC = "channel-steps/sec (B·H·T) for the S4 recurrent step mode; % FP32 roofline"
@@ -413,6 +464,15 @@ def main():
     import numpy as np
     import torch
 
+    cpu_line = None
+    if args.op == "forward" and not args.no_cpu_baseline and not args.calibrate_copy:
+        # the oracle on the host cores first: forked workers of a process that
+        # has not touched the GPU yet
+        from structured_state_space_amd import inputs as I
+        w0, p0, u0 = I.workload(args.workload)
+        cpu_line = cpu_baseline(w0, p0, u0, args.cpu_seconds)
+        del w0, p0, u0
+
     dev = torch.device("cuda:0")
     if args.calibrate_copy:
         n = args.calibrate_copy * (1 << 20) // 4
@@ -514,11 +574,22 @@ def main():
         achieved = a["work"] * a["scale"] / (phase_ms[k] * 1e-3)
         phases[k] = {"bound": a["bound"], "achieved": achieved, "peak": a["peak"], "unit": a["unit"],
                      "frac": achieved / a["peak"], "ms": phase_ms[k], "work_per_launch": a["work"]}
+    if "conv" in phases:
+        # the convolution sits near the ridge: its transform flops (FFTW
+        # convention, n = n_fft) against the FP32 peak, beside its HBM rating
+        conv_flops = w.Bsz * w.H * (5 * n_fft * int(math.log2(max(n_fft, 2))) + 6 * (n_fft // 2 + 1))
+        tf = conv_flops * 1e-12 / (phase_ms["conv"] * 1e-3)
+        phases["conv"]["transform_flops_per_launch"] = conv_flops
+        phases["conv"]["transform_tflops"] = tf
+        phases["conv"]["transform_frac_fp32"] = tf / PEAK_FP32_TFLOPS
     dom = max(names, key=lambda k: phase_ms[k])
     traffic = read_traffic(dom, w.name)
     roofline = {"bound": phases[dom]["bound"], "achieved": phases[dom]["achieved"], "peak": phases[dom]["peak"],
                 "unit": phases[dom]["unit"], "frac": phases[dom]["frac"], "traffic": traffic, "kernel": dom}
     troof_ms = (alg["cauchy"]["work"] / (PEAK_FP32_TFLOPS * 1e12) + alg["conv"]["work"] / (PEAK_HBM_GBS * 1e9)) * 1e3
+    # the whole step against its composite roofline: the root values' flops at
+    # the FP32 peak plus the convolution's bytes at the HBM peak (serial phases)
+    phases["composite"] = {"t_roof_ms": troof_ms, "ms": ms_per_step, "frac": troof_ms / ms_per_step}
 
     # the other entry points of the path as whole calls: the kernel alone
     # (root values and its transform) and the convolution with a given kernel
@@ -558,9 +629,8 @@ def main():
         "discretize_ms_off_timer": discretize_ms,
         "calls_ms_off_timer": calls_ms,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, p, u, args.cpu_seconds)
-        out["cpu_baseline"]["cores_on_host"] = os.cpu_count()
+    if cpu_line is not None:
+        out["cpu_baseline"] = cpu_line
     print(json.dumps(out))
     return 0
 

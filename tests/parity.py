@@ -23,9 +23,19 @@ def assert_rows_close(got, ref, tol=TOL, what=""):
     return worst
 
 
-def sample_channels(H, k, seed=0):
+def sample_channels(H, k, seed=0, forced=()):
+    """k channels: the first, the last and a seeded random draw, plus every
+    channel listed in `forced` (e.g. those with the smallest and largest step)."""
     if H <= k:
         return np.arange(H)
     rng = np.random.default_rng(1234 + seed)
     chans = set(rng.choice(H, size=k - 2, replace=False).tolist()) | {0, H - 1}
+    chans |= {int(h) for h in forced}
     return np.array(sorted(chans))
+
+
+def extreme_step_channels(dt):
+    """The channels with the smallest and the largest step size (the smallest
+    step puts the roots' Cauchy denominators closest together in float32)."""
+    dt = np.asarray(dt)
+    return (int(np.argmin(dt)), int(np.argmax(dt)))

@@ -9,7 +9,9 @@ import pytest
 
 import oracle as O
 from structured_state_space_amd import inputs as I
-from tests.parity import TOL, assert_rows_close, sample_channels
+import sys
+
+from tests.parity import TOL, assert_rows_close, extreme_step_channels, sample_channels
 
 pytestmark = pytest.mark.gpu
 
@@ -46,7 +48,7 @@ def _oracle_channel(params, h, u_rows=None, taps=None):
 @functools.lru_cache(maxsize=None)
 def _oracle_for(idx, nsample, with_y):
     w, p, u = _workload(idx)
-    chans = sample_channels(p.H, nsample, seed=idx)
+    chans = sample_channels(p.H, nsample, seed=idx, forced=extreme_step_channels(p.dt))
     refs = {int(h): _oracle_channel(p, int(h), u[:, h, :] if with_y else None) for h in chans}
     return chans, refs
 
@@ -186,8 +188,11 @@ def test_discretize_register_and_lds_paths(N, r, L, bordered):
         assert_rows_close(Ct[h][None], ref["Ctilde"][None], what=f"C~ h{h}")
 
 
-@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 12), (2, 3), (3, 3), (4, 2)])
+@pytest.mark.parametrize("idx,nsample", [(0, 1), (1, 12), (2, 3), (3, 3),
+                                         pytest.param(4, 2, marks=pytest.mark.timeout(600))])
 def test_forward_end_to_end(idx, nsample):
+    """Whole rows of K and y against the oracle on sampled channels; the
+    channels with the smallest and the largest step are always among them."""
     ssm = _ssm()
     w, p, u = _workload(idx)
     chans, refs = _oracle_for(idx, nsample, True)
@@ -205,15 +210,19 @@ def test_forward_end_to_end(idx, nsample):
         r = refs[int(h)]
         worst_k = max(worst_k, assert_rows_close(K[h][None], r["K"][None], what=f"K ch{h}"))
         worst_y = max(worst_y, assert_rows_close(y[:, h, :], r["y"], what=f"y ch{h}"))
-    print(f"workload {w.name}: worst K err {worst_k:.2e}, worst y err {worst_y:.2e}")
+    # on the real stderr, so the margin under the tolerance shows in any run log
+    sys.__stderr__.write(f"[parity] workload {w.name}: channels {[int(h) for h in chans]} "
+                         f"(dt {float(p.dt[chans].min()):.3g}..{float(p.dt[chans].max()):.3g}): "
+                         f"worst K err {worst_k:.3e}, worst y err {worst_y:.3e}\n")
+    sys.__stderr__.flush()
 
 
 # ---------------------------------------------------------------------------
 # the convolution on its own
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("Bsz,H,L", [(1, 1, 1), (1, 1, 2), (3, 2, 3), (2, 3, 17), (5, 4, 100), (2, 9, 1000),
-                                     (4, 8, 1024), (3, 5, 3000), (2, 3, 8192), (1, 2, 16384), (3, 2, 20000),
-                                     (2, 1, 65536)])
+                                     (4, 8, 1024), (3, 5, 3000), (2, 3, 8192), (1, 2, 16384), (4, 2, 16384),
+                                     (3, 2, 20000), (2, 1, 65536)])
 def test_fftconv_matches_direct_sum(Bsz, H, L):
     ssm = _ssm()
     rng = np.random.default_rng(L * 7 + H)
@@ -221,17 +230,14 @@ def test_fftconv_matches_direct_sum(Bsz, H, L):
     D = rng.standard_normal(H).astype(np.float32)
     u = rng.standard_normal((Bsz, H, L)).astype(np.float32)
     y = _np(ssm.fftconv(torch.from_numpy(K).to(DEV), torch.from_numpy(u).to(DEV), torch.from_numpy(D).to(DEV)))
+    # every row in full against the direct sum, 2e-4 x max|y| per row (at
+    # L = 65536 the oracle's lag loop takes a few seconds per channel)
+    worst = 0.0
     for h in range(H):
-        if L <= 3000:
-            ref = O.causal_conv(K[h].astype(np.float64), u[:, h, :], float(D[h])).real
-            assert_rows_close(y[:, h, :], ref, what=f"conv h{h}")
-        else:
-            ts = sorted({0, 1, L // 3, L // 2, L - 2, L - 1})
-            for b in range(Bsz):
-                for t in ts:
-                    ref = O.causal_conv_at(K[h].astype(np.float64), u[b, h], float(D[h]), t)
-                    scale = np.abs(u[b, h]).max() * np.abs(K[h]).sum() + abs(D[h]) * np.abs(u[b, h]).max()
-                    assert abs(y[b, h, t] - ref) <= TOL * scale
+        ref = O.causal_conv(K[h].astype(np.float64), u[:, h, :], float(D[h])).real
+        worst = max(worst, assert_rows_close(y[:, h, :], ref, what=f"conv h{h}"))
+    sys.__stderr__.write(f"[parity] fftconv Bsz={Bsz} H={H} L={L}: worst y err {worst:.3e}\n")
+    sys.__stderr__.flush()
 
 
 def test_fftconv_complex_kernel_uses_real_part():
