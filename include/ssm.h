@@ -58,6 +58,8 @@ typedef struct ssm_c64 {
 #define SSM_ERR_WORKSPACE 2        /* ws_bytes below ssm_workspace_bytes() */
 #define SSM_ERR_DEVICE 3           /* a HIP call or kernel launch failed */
 #define SSM_ERR_UNSUPPORTED 4      /* valid for the method, above this library's caps */
+#define SSM_ERR_SCRATCH_LIMIT 5    /* ssm_forward_noalloc: the shape needs more scratch than
+                                      SSM_NOALLOC_SCRATCH_BYTES */
 
 /* Per-channel statuses (device int32).  When several hold, the largest code
  * is reported. */
@@ -209,6 +211,26 @@ int ssm_forward_profiled(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L
                          const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
                          const float* u, float* y, ssm_c64* K_out, int32_t* status,
                          void* ws, size_t ws_bytes, void* stream, void* const* events, int32_t repeat);
+
+/*
+ * ssm_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same computation, results and arguments as ssm_forward except that there is
+ * no workspace argument.  The scratch lives in a fixed device array of
+ * SSM_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held from the
+ * first call on that GPU until the process ends; the call itself allocates and
+ * frees nothing.  Shapes whose ssm_workspace_bytes(SSM_OP_FORWARD, ...) exceeds
+ * that size give SSM_ERR_SCRATCH_LIMIT (nothing enqueued).  Every call on one
+ * GPU uses the same array: calls that overlap on one GPU (several streams or
+ * threads at once) race and must be ordered by the caller, e.g. on one stream.
+ * The first call on a device must not be made during graph capture (it looks
+ * up the array's device address once, a host-side query).
+ */
+#define SSM_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int ssm_forward_noalloc(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
+                        const ssm_c64* Lambda, const ssm_c64* P, const ssm_c64* Q,
+                        const ssm_c64* B, const ssm_c64* Ctilde, const float* dt, const float* D,
+                        const float* u, float* y, ssm_c64* K_out, int32_t* status, void* stream);
 
 /*
  * Recurrent (step) mode ([RSS] DPLR block: x_t = Abar x_{t-1} + Bbar u_t,

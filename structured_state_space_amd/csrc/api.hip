@@ -4,6 +4,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "common.hpp"
 
 namespace ssm {
@@ -169,6 +171,7 @@ const char* ssm_status_string(int code) {
         case SSM_ERR_WORKSPACE: return "workspace too small";
         case SSM_ERR_DEVICE: return "device error";
         case SSM_ERR_UNSUPPORTED: return "unsupported size";
+        case SSM_ERR_SCRATCH_LIMIT: return "shape needs more than the fixed no-allocation scratch";
         case SSM_ST_RESONANT_CORRECTION: return "resonant-correction";
         case SSM_ST_RESONANT_DIAGONAL: return "resonant-diagonal";
         case SSM_ST_SINGULAR_BILINEAR: return "singular-bilinear-matrix";
@@ -445,6 +448,49 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
         e = large ? launch_conv_large(Bsz, H, L, M, u, y_im, khat, (float2*)(base + w.big), twtab, s)
                   : launch_conv(Bsz, H, L, M, u, y_im, khat, twtab, s);
     return device_status(e);
+}
+
+}  // extern "C"
+
+// Scratch of ssm_forward_noalloc: one fixed array per GPU (each device that
+// loads the library holds its own copy until the process ends).  Its name is a
+// host-side stand-in in host code; kernels get the device address that
+// hipGetSymbolAddress returns for the current device, looked up once per device.
+static __device__ __align__(256) unsigned char scratch[SSM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// device address of the current device's scratch array, or null on failure
+void* scratch_for_current_device() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int ssm_forward_noalloc(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* Lambda,
+                        const ssm_c64* P, const ssm_c64* Q, const ssm_c64* B, const ssm_c64* Ctilde, const float* dt,
+                        const float* D, const float* u, float* y, ssm_c64* K_out, int32_t* status, void* stream) {
+    const int rc = check_sizes(Bsz, H, N, r, L, true, true);
+    if (rc != SSM_OK) return rc;
+    // every workspace region the forward path reads is written earlier in the
+    // same call, so the array needs no clearing between calls
+    if (layout(SSM_OP_FORWARD, Bsz, H, N, r, L).total > SSM_NOALLOC_SCRATCH_BYTES) return SSM_ERR_SCRATCH_LIMIT;
+    void* ws = scratch_for_current_device();
+    if (!ws) return SSM_ERR_DEVICE;
+    return forward_impl(Bsz, H, N, r, L, Lambda, P, Q, B, Ctilde, dt, D, u, y, K_out, status, ws,
+                        SSM_NOALLOC_SCRATCH_BYTES, stream, nullptr, 1);
 }
 
 // The step layout for lanes = 0.  16-lane groups issue fewer instructions per

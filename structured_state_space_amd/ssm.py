@@ -24,6 +24,8 @@ ERR_INVALID_ARGUMENT = 1
 ERR_WORKSPACE = 2
 ERR_DEVICE = 3
 ERR_UNSUPPORTED = 4
+ERR_SCRATCH_LIMIT = 5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 ST_OK = 0
 ST_RESONANT_CORRECTION = 16
 ST_RESONANT_DIAGONAL = 17
@@ -37,7 +39,8 @@ HIPPO_KINDS = {"legs": HIPPO_LEGS, "legt": HIPPO_LEGT, "lagt": HIPPO_LAGT}
 
 EXPORTS = ("ssm_workspace_bytes", "ssm_transform_lengths", "ssm_forward_form", "ssm_status_string",
            "ssm_discretize", "ssm_kernel_gen", "ssm_fftconv", "ssm_forward", "ssm_forward_profiled", "ssm_step",
-           "ssm_forward_complex", "ssm_hippo_dplr", "ssm_step_prepare", "ssm_step_prepared")
+           "ssm_forward_complex", "ssm_hippo_dplr", "ssm_step_prepare", "ssm_step_prepared",
+           "ssm_forward_noalloc")
 
 
 class SSMError(RuntimeError):
@@ -78,6 +81,8 @@ def _load():
     lib.ssm_step_prepared.restype = i32
     lib.ssm_forward_complex.argtypes = [i64, i64, i64, i64, i64] + [vp] * 12 + [vp, sz, vp]
     lib.ssm_forward_complex.restype = i32
+    lib.ssm_forward_noalloc.argtypes = [i64, i64, i64, i64, i64] + [vp] * 11 + [vp]
+    lib.ssm_forward_noalloc.restype = i32
     lib.ssm_hippo_dplr.argtypes = [i32, i64, ctypes.c_double, i64, vp, i64, vp] + [vp] * 5 + [vp, sz, vp]
     lib.ssm_hippo_dplr.restype = i32
     return lib
@@ -249,6 +254,30 @@ def forward(Lambda, P, Q, B, Ctilde, dt, D, u, want_kernel=False, y=None, K_out=
         name = "ssm_forward_profiled"
     if rc != OK:
         raise SSMError(name, rc)
+    return dict(y=y, K=K_out, status=status)
+
+
+def forward_noalloc(Lambda, P, Q, B, Ctilde, dt, D, u, y=None, K_out=None, status=None):
+    """ssm_forward_noalloc: ssm_forward with the library's fixed per-GPU scratch
+    instead of a workspace (the call allocates nothing when y, K_out and status
+    are given).  Returns dict(y, K, status) as forward does."""
+    H, N, r, dev = _params(Lambda, P, Q, B, Ctilde, dt)
+    Bsz, H2, L = u.shape
+    if H2 != H:
+        raise ValueError("u: channel count does not match the parameters")
+    _check(u, "u", torch.float32, (Bsz, H, L), dev)
+    _check(D, "D", torch.float32, (H,), dev)
+    if y is None:
+        y = torch.empty_like(u)
+    _check(y, "y", torch.float32, (Bsz, H, L), dev)
+    _check(K_out, "K_out", torch.complex64, (H, L), dev)
+    if status is None:
+        status = torch.empty((H,), dtype=torch.int32, device=dev)
+    _check(status, "status", torch.int32, (H,), dev)
+    rc = lib.ssm_forward_noalloc(Bsz, H, N, r, L, _ptr(Lambda), _ptr(P), _ptr(Q), _ptr(B), _ptr(Ctilde), _ptr(dt),
+                                 _ptr(D), _ptr(u), _ptr(y), _ptr(K_out), _ptr(status), _stream(dev))
+    if rc != OK:
+        raise SSMError("ssm_forward_noalloc", rc)
     return dict(y=y, K=K_out, status=status)
 
 

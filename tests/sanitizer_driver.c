@@ -79,6 +79,10 @@ int main(void) {
            "forward workspace");
     expect(ssm_forward(2, 3, 4, 1, 16, c, c, c, c, c, f, NULL, f, NULL, NULL, NULL, FAKE, 1 << 30, NULL),
            SSM_ERR_INVALID_ARGUMENT, "forward null y");
+    expect(ssm_forward_noalloc(2, 0, 4, 1, 16, c, c, c, c, c, f, NULL, f, fo, NULL, NULL, NULL),
+           SSM_ERR_INVALID_ARGUMENT, "noalloc H");
+    expect(ssm_forward_noalloc(2, 1024, 4, 1, 16384, c, c, c, c, c, f, NULL, f, fo, NULL, NULL, NULL),
+           SSM_ERR_SCRATCH_LIMIT, "noalloc scratch limit");
     expect(ssm_forward_complex(2, 3, 4, 1, 16, c, c, c, c, c, f, NULL, f, fo, NULL, NULL, NULL, FAKE, 1 << 30, NULL),
            SSM_ERR_INVALID_ARGUMENT, "complex null y_im");
     expect(ssm_forward_complex(2, 3, 4, 5, 16, c, c, c, c, c, f, NULL, f, fo, fo, NULL, NULL, FAKE, 1 << 30, NULL),
