@@ -34,6 +34,12 @@ hipError_t launch_conv_fused(int64_t Bsz, int64_t H, int64_t L, int64_t M, int64
 hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                                  float2* B1, const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                                  float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
+bool wave_path_fits(int64_t M);
+hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
+                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
+                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
+hipError_t launch_wconv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
+                        const float2* twtab, hipStream_t stream);
 hipError_t launch_conv_large(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y,
                              const float2* khat, float2* Z, const float2* twtab, hipStream_t stream);
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
@@ -281,6 +287,12 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
         if (e != hipSuccess) return SSM_ERR_DEVICE;
         return device_status(launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)((char*)ws + w.big), twtab, s));
     }
+    if (wave_path_fits(M)) {
+        hipError_t e = launch_wspectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat,
+                                        twtab, s);
+        if (e != hipSuccess) return SSM_ERR_DEVICE;
+        return device_status(launch_wconv(Bsz, H, L, M, u, y, khat, twtab, s));
+    }
     hipError_t e =
         launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, twtab, s);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
@@ -348,6 +360,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
     const bool fused = form == 2;
+    const bool wave = !large && !fused && wave_path_fits(M);
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
     for (int i = 0; i < repeat && e == hipSuccess && !fused; ++i) {
@@ -355,16 +368,19 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
             e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                               (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
         if (e != hipSuccess) break;
-        e = large ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
-                                          (float2*)K_out, status, khat, twtab, s)
-                  : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
-                                    (float2*)K_out, status, khat, twtab, s);
+        e = large  ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
+                                           (float2*)K_out, status, khat, twtab, s)
+            : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
+                                      (float2*)K_out, status, khat, twtab, s)
+                   : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
+                                     (float2*)K_out, status, khat, twtab, s);
     }
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = large   ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
             : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out,
                                         status, u, y, twtab, s)
+            : wave  ? launch_wconv(Bsz, H, L, M, u, y, khat, twtab, s)
                     : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
     if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
     return SSM_OK;
