@@ -37,9 +37,10 @@ hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t 
 bool wave_path_fits(int64_t M);
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
+                            float2* K_out, int32_t* status, float2* khat, const float2* twtab, float2* tw4,
+                            hipStream_t stream);
 hipError_t launch_wconv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
-                        const float2* twtab, hipStream_t stream);
+                        const float2* tw4, hipStream_t stream);
 hipError_t launch_conv_large(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y,
                              const float2* khat, float2* Z, const float2* twtab, hipStream_t stream);
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
@@ -128,6 +129,11 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
             w.big_bytes = (size_t)(npairs < kConvChunkPairs ? npairs : kConvChunkPairs) * 2 * M * sizeof(float2);
         }
         off = align256(off + w.big_bytes);
+    }
+    if ((op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) && wave_path_fits(M)) {
+        w.tw4 = off;
+        w.tw4_bytes = (size_t)2 * M * sizeof(float2);
+        off = align256(off + w.tw4_bytes);
     }
     if (op == SSM_OP_FORWARD_COMPLEX) {
         w.kbuf = off;
@@ -288,10 +294,11 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
         return device_status(launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)((char*)ws + w.big), twtab, s));
     }
     if (wave_path_fits(M)) {
+        float2* tw4 = (float2*)((char*)ws + w.tw4);
         hipError_t e = launch_wspectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat,
-                                        twtab, s);
+                                        twtab, tw4, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
-        return device_status(launch_wconv(Bsz, H, L, M, u, y, khat, twtab, s));
+        return device_status(launch_wconv(Bsz, H, L, M, u, y, khat, tw4, s));
     }
     hipError_t e =
         launch_spectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat, twtab, s);
@@ -371,7 +378,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
         e = large  ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
                                            (float2*)K_out, status, khat, twtab, s)
             : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
-                                      (float2*)K_out, status, khat, twtab, s)
+                                      (float2*)K_out, status, khat, twtab, (float2*)(base + w.tw4), s)
                    : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
                                      (float2*)K_out, status, khat, twtab, s);
     }
@@ -380,7 +387,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
         e = large   ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
             : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out,
                                         status, u, y, twtab, s)
-            : wave  ? launch_wconv(Bsz, H, L, M, u, y, khat, twtab, s)
+            : wave  ? launch_wconv(Bsz, H, L, M, u, y, khat, (const float2*)(base + w.tw4), s)
                     : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
     if (e != hipSuccess || mark(3) != hipSuccess) return SSM_ERR_DEVICE;
     return SSM_OK;

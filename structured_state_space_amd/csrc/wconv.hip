@@ -7,15 +7,20 @@
 // radix-two DFT block (an exact polynomial product by zero padding to a
 // radix-two length >= 2n - 1).
 //
-// The zero-padded length-2M product is split into its even and odd frequencies
-// (cyclic and twisted halves, tw_j = exp(-i pi j/M)):
-//   y = IFFT_M(FFT_M(z) . FFT_M(k)) + conj(tw) . IFFT_M(FFT_M(tw . z) . FFT_M(tw . k))
-// on j < M, with both spectra scaled by 1/(2M).  Two batch rows of one channel
-// go through at once as z = u_b + i u_{b+1} (the kernel is real, so the real
-// and imaginary parts of y are the two rows).  The spectra are stored in the
-// transform's scrambled order (wfft.hpp), so the convolution multiplies and
-// transforms back without ever unscrambling, and each lane's spectrum loads
-// are coalesced.
+// The zero-padded product is taken modulo z^(2M) + 1 (negacyclic; the linear
+// product has degree < 2M - 1, so nothing wraps), split by z^(2M) + 1 =
+// (z^M - i)(z^M + i) into two M-point halves with the twists psi^1 and psi^3,
+// psi_j = exp(-i pi j/(2M)):
+//   y = conj(psi) . IFFT_M(FFT_M(psi . z) . S_A) + conj(psi^3) . IFFT_M(FFT_M(psi^3 . z) . S_B)
+// on j < M, with S_A = FFT_M(psi . k)/(2M) and S_B = FFT_M(psi^3 . k)/(2M).
+// For a real kernel k, S_B[j] = conj(S_A[M - 1 - j]), so only S_A is formed
+// and stored (M complex per channel): in the transform's scrambled order the
+// partner M - 1 - j of a position is the position with every index complemented
+// (wfft.hpp), and a lane's reads of S_B are S_A read backwards, conjugated.
+// Two batch rows of one channel go through at once as z = u_b + i u_{b+1}
+// (the kernel is real, so the real and imaginary parts of y are the two rows).
+// The convolution multiplies in the scrambled order and transforms back
+// without ever unscrambling; each lane's spectrum loads are coalesced.
 #include "common.hpp"
 #include "fft.hpp"
 #include "wfft.hpp"
@@ -24,25 +29,27 @@ namespace ssm {
 
 namespace {
 
-// Spectra of one channel's real kernel k (taps >= L zero, D at tap 0), scaled
-// 1/(2M), into khat[h][0] (cyclic) and khat[h][1] (twisted), scrambled order.
-// FROM_ROOTS: k = Re K, K the first L taps of the inverse transform of the root
-// values (also written to K_out); the per-channel status is reduced from the
-// root-value kernel's tile statuses, and a failing channel gets NaN spectra
+// Spectrum S_A of one channel's real kernel k (taps >= L zero, D at tap 0),
+// scaled 1/(2M), into khat[h] (M complex, scrambled order).  FROM_ROOTS:
+// k = Re K, K the first L taps of the inverse transform of the root values
+// (also written to K_out); the per-channel status is reduced from the
+// root-value kernel's tile statuses, and a failing channel gets a NaN spectrum
 // and kernel.  Otherwise k is read from a caller's kernel (stride kstride).
+// twtab: exp(-i pi j/M), j < M (the inverse transform); tw4: exp(-i pi j/(2M)),
+// j < 2M (the wave-structured transform).
 template <int LOGM, bool FROM_ROOTS>
 __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4))) void wspec_kernel(
     int L, int tiles, const float2* __restrict__ roots, const int32_t* __restrict__ tile_status,
     const float* __restrict__ Kin, int64_t kstride, const float* __restrict__ D, float2* __restrict__ K_out,
-    int32_t* __restrict__ status, float2* __restrict__ khat, const float2* __restrict__ twtab) {
+    int32_t* __restrict__ status, float2* __restrict__ khat, const float2* __restrict__ twtab,
+    const float2* __restrict__ tw4) {
     using G = WGeo<LOGM>;
     constexpr int M = G::M, T = G::T;
     __shared__ float2 lds[G::LDS > lds_padded_size(M) ? G::LDS : lds_padded_size(M)];
     __shared__ int sst;
     const int h = blockIdx.x;
     const int t = threadIdx.x;
-    float2* kh0 = khat + (size_t)h * 2 * M;
-    float2* kh1 = kh0 + M;
+    float2* kh = khat + (size_t)h * M;
     float kr[16];
     if constexpr (FROM_ROOTS) {
         if (t == 0) sst = 0;
@@ -56,10 +63,7 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
         if (st != 0) {  // uniform: NaN-fill this channel's outputs
             for (int j = t; j < L; j += T)
                 if (K_out) K_out[(size_t)h * L + j] = c_nan();
-            for (int j = t; j < M; j += T) {
-                kh0[j] = c_nan();
-                kh1[j] = c_nan();
-            }
+            for (int j = t; j < M; j += T) kh[j] = c_nan();
             return;
         }
         // the inverse transform of the root values in natural order (Stockham,
@@ -87,19 +91,14 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
     }
     if (t == 0 && D) kr[0] += D[h];
     const float sc = 1.0f / (float)(2 * M);
-    const rsrc_t rk = make_rsrc(kh0, 2 * M * sizeof(float2));
+    const rsrc_t rk = make_rsrc(kh, M * sizeof(float2));
     const uint32_t vo = (uint32_t)wf_pos(t, 0) * sizeof(float2);
     float2 w[16];
 #pragma unroll
     for (int e = 0; e < 16; ++e) w[e] = make_float2(kr[e] * sc, 0.0f);
-    wf_forward<LOGM, false>(w, lds, twtab, t);
+    wf_forward<LOGM, 1>(w, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) buf_st_c64(w[e], rk, vo, e * 64 * sizeof(float2));
-#pragma unroll
-    for (int e = 0; e < 16; ++e) w[e] = make_float2(kr[e] * sc, 0.0f);
-    wf_forward<LOGM, true>(w, lds, twtab, t);
-#pragma unroll
-    for (int e = 0; e < 16; ++e) buf_st_c64(w[e], rk, vo, (M + e * 64) * sizeof(float2));
 }
 
 // One workgroup (T = M/16 threads) per pair of batch rows (b, b+1) of one
@@ -108,7 +107,7 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
 template <int LOGM>
 __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4))) void wconv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
-    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ twtab) {
+    float* __restrict__ y, const float2* __restrict__ khat, const float2* __restrict__ tw4) {
     using G = WGeo<LOGM>;
     constexpr int M = G::M, T = G::T;
     __shared__ float2 lds[G::LDS];
@@ -131,9 +130,12 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
     const rsrc_t r2 = make_rsrc(u + row1 + (has2 ? (size_t)H * L : 0), (uint32_t)L * sizeof(float));
     const rsrc_t o1 = make_rsrc(y + row1, (uint32_t)L * sizeof(float));
     const rsrc_t o2 = make_rsrc(y + row1 + (has2 ? (size_t)H * L : 0), (uint32_t)L * sizeof(float));
-    const rsrc_t rk = make_rsrc(khat + (size_t)h * 2 * M, 2 * M * sizeof(float2));
+    const rsrc_t rk = make_rsrc(khat + (size_t)h * M, M * sizeof(float2));
     const uint32_t vt = (uint32_t)t * sizeof(float);
+    const int wv = t >> 6, lane = t & 63;
     const uint32_t vk = (uint32_t)wf_pos(t, 0) * sizeof(float2);
+    // the complemented position (G::W - 1 - wv, 15 - e, 63 - lane), register e at uniform offset (15 - e) 64
+    const uint32_t vkm = (uint32_t)((G::W - 1 - wv) * 16 * 64 + 63 - lane) * sizeof(float2);
 
     float2 z[16];
 #pragma unroll
@@ -145,22 +147,22 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
         }
     }
     float2 v[16], out[16];
-    // cyclic half
+    // half A: twist psi
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = z[e];
-    wf_forward<LOGM, false>(v, lds, twtab, t);
+    wf_forward<LOGM, 1>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], buf_ld_c64(rk, vk, e * 64 * sizeof(float2)));
-    wf_inverse<LOGM, false>(v, lds, twtab, t);
+    wf_inverse<LOGM, 1>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[e] = v[e];
-    // twisted half (the twist and untwist are inside the transforms)
+    // half B: twist psi^3, spectrum S_B = conj(S_A) at the complemented position
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = z[e];
-    wf_forward<LOGM, true>(v, lds, twtab, t);
+    wf_forward<LOGM, 3>(v, lds, tw4, t);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], buf_ld_c64(rk, vk, (M + e * 64) * sizeof(float2)));
-    wf_inverse<LOGM, true>(v, lds, twtab, t);
+    for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], c_conj(buf_ld_c64(rk, vkm, (15 - e) * 64 * sizeof(float2))));
+    wf_inverse<LOGM, 3>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         if (t + T * e < L) {
@@ -171,43 +173,41 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
     }
 }
 
-// tab[j] = exp(-i pi j/M) in float64, rounded (the given-kernel path, where no
-// root-value kernel writes it)
-__global__ __launch_bounds__(256) void wtwiddle_kernel(int M, float2* __restrict__ twtab) {
-    for (int j = blockIdx.x * 256 + threadIdx.x; j < M; j += gridDim.x * 256) {
+// tab[j] = exp(-i pi j/(2M)), j < 2M, in float64, rounded
+__global__ __launch_bounds__(256) void wtwiddle4_kernel(int M, float2* __restrict__ tw4) {
+    for (int j = blockIdx.x * 256 + threadIdx.x; j < 2 * M; j += gridDim.x * 256) {
         double sn, cs;
-        sincospi((double)j / (double)M, &sn, &cs);
-        twtab[j] = make_float2((float)cs, (float)-sn);
+        sincospi((double)j / (double)(2 * M), &sn, &cs);
+        tw4[j] = make_float2((float)cs, (float)-sn);
     }
 }
 
 template <int LOGM>
 hipError_t wspec_launch(bool from_roots, int64_t H, int64_t L, int64_t tiles, const float2* roots,
                         const int32_t* tstat, const float* Kin, int64_t kstride, const float* D, float2* K_out,
-                        int32_t* status, float2* khat, float2* twtab, hipStream_t stream) {
+                        int32_t* status, float2* khat, const float2* twtab, float2* tw4, hipStream_t stream) {
     using G = WGeo<LOGM>;
-    if (from_roots) {
+    hipLaunchKernelGGL(wtwiddle4_kernel, dim3((unsigned)((2 * G::M + 255) / 256)), dim3(256), 0, stream, G::M, tw4);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (from_roots)
         hipLaunchKernelGGL((wspec_kernel<LOGM, true>), dim3((unsigned)H), dim3(G::T), 0, stream, (int)L, (int)tiles,
-                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab);
-    } else {
-        hipLaunchKernelGGL(wtwiddle_kernel, dim3((unsigned)((G::M + 255) / 256)), dim3(256), 0, stream, G::M, twtab);
-        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab, (const float2*)tw4);
+    else
         hipLaunchKernelGGL((wspec_kernel<LOGM, false>), dim3((unsigned)H), dim3(G::T), 0, stream, (int)L, (int)tiles,
-                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab);
-    }
+                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab, (const float2*)tw4);
     return hipGetLastError();
 }
 
 template <int LOGM>
 hipError_t wconv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y, const float2* khat,
-                        const float2* twtab, hipStream_t stream) {
+                        const float2* tw4, hipStream_t stream) {
     using G = WGeo<LOGM>;
     const int64_t npb = (Bsz + 1) / 2;
     const int64_t npairs = npb * H;
     int remap = 0;
     if (H % 8 == 0) remap = (int)npb;
     hipLaunchKernelGGL((wconv_kernel<LOGM>), dim3((unsigned)npairs), dim3(G::T), 0, stream, (int)Bsz, (int)H, (int)L,
-                       (int)npb, npairs, remap, u, y, khat, twtab);
+                       (int)npb, npairs, remap, u, y, khat, tw4);
     return hipGetLastError();
 }
 
@@ -218,12 +218,13 @@ bool wave_path_fits(int64_t M) { return M >= 1024 && M <= 16384; }
 
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream) {
+                            float2* K_out, int32_t* status, float2* khat, const float2* twtab, float2* tw4,
+                            hipStream_t stream) {
     switch (ilog2_exact(M)) {
 #define SSM_WSPEC_CASE(LG)                                                                                       \
     case LG:                                                                                                     \
         return wspec_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat,    \
-                                twtab, stream);
+                                twtab, tw4, stream);
         SSM_WSPEC_CASE(10) SSM_WSPEC_CASE(11) SSM_WSPEC_CASE(12) SSM_WSPEC_CASE(13) SSM_WSPEC_CASE(14)
 #undef SSM_WSPEC_CASE
         default: return hipErrorInvalidValue;
@@ -231,10 +232,10 @@ hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, in
 }
 
 hipError_t launch_wconv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
-                        const float2* twtab, hipStream_t stream) {
+                        const float2* tw4, hipStream_t stream) {
     switch (ilog2_exact(M)) {
 #define SSM_WCONV_CASE(LG) \
-    case LG: return wconv_launch<LG>(Bsz, H, L, u, y, khat, twtab, stream);
+    case LG: return wconv_launch<LG>(Bsz, H, L, u, y, khat, tw4, stream);
         SSM_WCONV_CASE(10) SSM_WCONV_CASE(11) SSM_WCONV_CASE(12) SSM_WCONV_CASE(13) SSM_WCONV_CASE(14)
 #undef SSM_WCONV_CASE
         default: return hipErrorInvalidValue;

@@ -27,14 +27,15 @@
 // order, run through the exact mirror of the forward steps with conjugate
 // constants (wf_inverse), gives the unscaled inverse transform in natural order.
 //
-// TWIST folds the twist x_n exp(-i pi n/M) into stage A (the constant
-// exp(-2 pi i e/32) per register and exp(-i pi t (2k+1)/M) as the stage
-// twiddle), so wf_forward<.., true> is FFT_M(tw . x) and wf_inverse<.., true>
-// is conj(tw) . IFFT_M (unscaled): the odd bins of the zero-padded 2M-point
-// product.
+// TW folds a twist x_n exp(-2 pi i TW n/(4M)) (TW = 1 or 3) into stage A: the
+// constant exp(-2 pi i TW e/64) per register and exp(-2 pi i t (TW + 4k)/(4M))
+// as the stage twiddle.  So wf_forward<.., TW> is FFT_M(x . psi^TW) with
+// psi_n = exp(-i pi n/(2M)), and wf_inverse<.., TW> is conj(psi^TW) . IFFT_M
+// (unscaled): the two halves (bins 4j+1 and 4j+3 of the 4M-point transform)
+// of a zero-padded negacyclic product of length 2M.
 //
-// Twiddles come from the table tab[j] = exp(-i pi j/M), j < M (float64-accurate),
-// one entry per stage and thread; the powers are formed by products.
+// Twiddles come from the table tab[j] = exp(-i pi j/(2M)), j < 2M (float64-
+// accurate), one entry per stage and thread; the powers are formed by products.
 #pragma once
 
 #include "common.hpp"
@@ -58,63 +59,79 @@ struct WGeo {
 // per-wave LDS slice of stage C2: element (lane, e) at lane + 65 e (< 1039)
 constexpr int kSlice = 1040;
 
-// exp(-+2 pi i K/32), K < 16: (cos, sin) of 2 pi K/32
-template <int K>
-struct Root32 {
-    static constexpr float tabc[9] = {1.0f,
-                                      0.98078528040323044913f,
-                                      0.92387953251128675613f,
-                                      0.83146961230254523708f,
-                                      0.70710678118654752440f,
-                                      0.55557023301960222474f,
-                                      0.38268343236508977173f,
-                                      0.19509032201612826785f,
-                                      0.0f};
-    static constexpr float c = K <= 8 ? tabc[K] : -tabc[16 - K];
-    static constexpr float s = K <= 8 ? tabc[8 - K] : tabc[K - 8];
-};
+// (cos, sin) of 2 pi K/64, K < 64
+constexpr float kCos64[17] = {1.0f,
+                              0.99518472667219688624f,
+                              0.98078528040323044913f,
+                              0.95694033573220886494f,
+                              0.92387953251128675613f,
+                              0.88192126434835502971f,
+                              0.83146961230254523708f,
+                              0.77301045336273696081f,
+                              0.70710678118654752440f,
+                              0.63439328416364549822f,
+                              0.55557023301960222474f,
+                              0.47139673682599764856f,
+                              0.38268343236508977173f,
+                              0.29028467725446236764f,
+                              0.19509032201612826785f,
+                              0.09801714032956060199f,
+                              0.0f};
+constexpr float cos64(int k) {
+    k &= 63;
+    return k <= 16 ? kCos64[k] : k <= 32 ? -kCos64[32 - k] : k <= 48 ? -kCos64[k - 32] : kCos64[64 - k];
+}
+constexpr float sin64(int k) { return cos64(k - 16); }
 
+// a * exp(-+2 pi i K/64) for a compile-time K
 template <int K, bool INV>
-__device__ __forceinline__ float2 mul_root32(float2 a) {
-    if constexpr (K == 0) {
+__device__ __forceinline__ float2 mul_root64(float2 a) {
+    constexpr int k = K & 63;
+    if constexpr (k == 0) {
         return a;
-    } else if constexpr (K == 8) {
+    } else if constexpr (k == 16) {
         return c_mul_mi<INV>(a);
+    } else if constexpr (k == 32) {
+        return make_float2(-a.x, -a.y);
+    } else if constexpr (k == 48) {
+        return c_mul_mi<!INV>(a);
     } else {
-        return c_mul(a, make_float2(Root32<K>::c, INV ? Root32<K>::s : -Root32<K>::s));
+        return c_mul(a, make_float2(cos64(k), INV ? sin64(k) : -sin64(k)));
     }
 }
 
-template <bool INV, int K = 0>
-__device__ __forceinline__ void pretwist32(float2 (&v)[16]) {
+// v[e] *= exp(-+2 pi i TW e/64)
+template <int TW, bool INV, int K = 0>
+__device__ __forceinline__ void pretwist64(float2 (&v)[16]) {
     if constexpr (K < 16) {
-        v[K] = mul_root32<K, INV>(v[K]);
-        pretwist32<INV, K + 1>(v);
+        v[K] = mul_root64<TW * K, INV>(v[K]);
+        pretwist64<TW, INV, K + 1>(v);
     }
 }
 
 // ---- stage A: DFT_16 over the register index, twiddle exp(-2 pi i t k/M)
-//      (TWIST: exp(-i pi t (2k+1)/M) and the per-register constant first) ----
-template <int LOGM, bool TWIST, bool INV>
+//      (TW: exp(-2 pi i t (TW + 4k)/(4M)), the per-register constant first) ----
+template <int LOGM, int TW, bool INV>
 __device__ __forceinline__ void wf_twiddle_a(float2 (&v)[16], const float2* __restrict__ tab, int t) {
-    float2 base = tab[TWIST ? t : 2 * t];  // exp(-i pi t/M) or exp(-2 pi i t/M)
-    if (INV) base.y = -base.y;
+    float2 step = tab[4 * t];  // exp(-2 pi i t/M)
+    if (INV) step.y = -step.y;
     // keep the powers per call (not hoisted and kept live across stages)
-    asm volatile("" : "+v"(base.x), "+v"(base.y));
-    if constexpr (TWIST) {
-        const float2 step = c_mul(base, base);
-        float2 p = base;
+    asm volatile("" : "+v"(step.x), "+v"(step.y));
+    if constexpr (TW != 0) {
+        float2 u = tab[t];  // exp(-2 pi i t/(4M))
+        if (INV) u.y = -u.y;
+        float2 p = TW == 1 ? u : c_mul(c_mul(u, u), u);
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             v[k] = c_mul(v[k], p);
             if (k < 15) p = c_mul(p, step);
         }
     } else {
-        float2 p = base;
+        float2 p = step;
 #pragma unroll
         for (int k = 1; k < 16; ++k) {
             v[k] = c_mul(v[k], p);
-            if (k < 15) p = c_mul(p, base);
+            if (k < 15) p = c_mul(p, step);
         }
     }
 }
@@ -137,7 +154,7 @@ __device__ __forceinline__ void wf_dft_waves(float2 (&v)[16]) {
 template <int LOGM, bool INV>
 __device__ __forceinline__ void wf_twiddle_b(float2 (&v)[16], const float2* __restrict__ tab, int lane) {
     using G = WGeo<LOGM>;
-    float2 base = tab[lane * 32];  // exp(-2 pi i lane/T), T = 64 W = 2M/32
+    float2 base = tab[lane * 64];  // exp(-2 pi i lane/T), T = 64 W = 4M/64
     if (INV) base.y = -base.y;
     asm volatile("" : "+v"(base.x), "+v"(base.y));
     float2 p = base;
@@ -188,7 +205,7 @@ __device__ __forceinline__ void wf_dft4_groups(float2 (&v)[16]) {
 template <int LOGM, bool INV>
 __device__ __forceinline__ void wf_twiddle_c1(float2 (&v)[16], const float2* __restrict__ tab, int lane) {
     using G = WGeo<LOGM>;
-    float2 base = tab[(lane & 15) * 32 * G::W];  // exp(-2 pi i (lane mod 16)/64)
+    float2 base = tab[(lane & 15) * 64 * G::W];  // exp(-2 pi i (lane mod 16)/64), 4M/64 = 64 W
     if (INV) base.y = -base.y;
     asm volatile("" : "+v"(base.x), "+v"(base.y));
     const float2 b2 = c_mul(base, base), b3 = c_mul(b2, base);
@@ -254,14 +271,14 @@ __device__ __forceinline__ void exchange_waves(float2 (&v)[16], float2* __restri
 // Forward transform (see the header comment).  lds: WGeo::LDS complex, shared by the
 // T = 64 W threads of the transform (threadIdx.x < T), every one of which
 // must call it.  t = threadIdx.x.
-template <int LOGM, bool TWIST>
+template <int LOGM, int TW>
 __device__ __forceinline__ void wf_forward(float2 (&v)[16], float2* __restrict__ lds, const float2* __restrict__ tab,
                                            int t) {
     using G = WGeo<LOGM>;
     const int lane = t & 63, wv = t >> 6;
-    if constexpr (TWIST) pretwist32<false>(v);
+    if constexpr (TW != 0) pretwist64<TW, false>(v);
     dft_reg<16, false>(v);
-    wf_twiddle_a<LOGM, TWIST, false>(v, tab, t);
+    wf_twiddle_a<LOGM, TW, false>(v, tab, t);
     if constexpr (G::W > 1) {
         exchange_waves<LOGM, false>(v, lds, lane, wv);
         wf_dft_waves<LOGM, false>(v);
@@ -276,7 +293,7 @@ __device__ __forceinline__ void wf_forward(float2 (&v)[16], float2* __restrict__
 
 // The exact mirror of wf_forward with conjugate constants: from the scrambled
 // order back to natural order, unscaled (M x the inverse transform).
-template <int LOGM, bool TWIST>
+template <int LOGM, int TW>
 __device__ __forceinline__ void wf_inverse(float2 (&v)[16], float2* __restrict__ lds, const float2* __restrict__ tab,
                                            int t) {
     using G = WGeo<LOGM>;
@@ -291,13 +308,31 @@ __device__ __forceinline__ void wf_inverse(float2 (&v)[16], float2* __restrict__
         wf_dft_waves<LOGM, true>(v);
         exchange_waves<LOGM, true>(v, lds, lane, wv);
     }
-    wf_twiddle_a<LOGM, TWIST, true>(v, tab, t);
+    wf_twiddle_a<LOGM, TW, true>(v, tab, t);
     dft_reg<16, true>(v);
-    if constexpr (TWIST) pretwist32<true>(v);
+    if constexpr (TW != 0) pretwist64<TW, true>(v);
 }
 
 // position of register e of thread t in a spectrum stored in the scrambled order
 __device__ __forceinline__ int wf_pos(int t, int e) { return ((t >> 6) * 16 + e) * 64 + (t & 63); }
+
+// The frequency index held at position ((16 wave + e) 64 + lane): stage A leaves
+// the DFT_16 output k1 in the registers; the exchange moves its top log2(W)
+// bits to the wave index and the stage-B output k2a into the top register
+// bits; stage C1 moves register bits 0-1 to lane bits 4-5 and leaves k2b_a in
+// register bits 0-1; stage C2 moves register bits 0-3 to lane bits 0-3 and
+// leaves k2b_b in the registers.  k = k1 + 16 (k2a + W (k2b_a + 4 k2b_b)).
+// Complementing every digit (k -> M - 1 - k) complements the wave, register and
+// lane indices.
+template <int LOGM>
+__host__ __device__ constexpr int wf_freq(int wave, int e, int lane) {
+    constexpr int LOGW = LOGM - 10, W = 1 << LOGW, SB = 4 - LOGW;  // register bits of k1 left after the exchange
+    const int rb = ((lane >> 4) & 3) | (((lane >> 2) & 3) << 2);  // register index before stage C1
+    const int k1 = (rb & ((1 << SB) - 1)) | (wave << SB);
+    const int k2a = rb >> SB;
+    const int k2b_a = lane & 3, k2b_b = e;
+    return k1 + 16 * (k2a + W * (k2b_a + 4 * k2b_b));
+}
 
 // ---- raw buffer access: the base and size in scalar registers, one 32-bit
 //      lane offset, and a uniform offset per register (so a thread's 16
