@@ -37,8 +37,9 @@ DEFAULT_WORKLOAD = "s4-h1k-l16k"   # the largest workload: most channel-steps an
 KERNEL_SOURCES = {
     "filter": ["single_launch.hip", "roots.hpp", "fft.hpp", "common.hpp"],
     "cauchy": ["cauchy.hip", "roots.hpp", "common.hpp"],
-    "spectrum": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
-    "conv": ["spectrum_conv.hip", "fft.hpp", "common.hpp"],
+    "spectrum": ["wconv.hip", "wlarge.hip", "multipass.hip", "spectrum_conv.hip", "wfft.hpp", "fft.hpp",
+                 "common.hpp"],
+    "conv": ["wconv.hip", "wlarge.hip", "spectrum_conv.hip", "wfft.hpp", "fft.hpp", "common.hpp"],
 }
 
 
@@ -59,7 +60,8 @@ def algorithmic(w, M, fused):
     out = {
         "cauchy": dict(bound="mfma", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
                        peak=PEAK_FP32_TFLOPS),
-        "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * 2 * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
+        # the root values read, one spectrum of M complex written per channel
+        "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
         "conv": dict(bound="hbm", unit="GB/s", work=8 * B * H * L + 4 * H * L + 4 * H, scale=1e-9,
                      peak=PEAK_HBM_GBS),
     }

@@ -12,7 +12,7 @@ namespace ssm {
 int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream);
+                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream, bool scrambled);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -37,10 +37,14 @@ hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t 
 bool wave_path_fits(int64_t M);
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, const float2* twtab, float2* tw4,
-                            hipStream_t stream);
+                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream);
 hipError_t launch_wconv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                         const float2* tw4, hipStream_t stream);
+hipError_t launch_wl_spectrum(int64_t H, int64_t L, int64_t M, int64_t tiles, float2* roots, const int32_t* tstat,
+                              int32_t* status, const float* Kin, int64_t kstride, const float* D, float2* K_out,
+                              float2* S, float2* tw4Q, float2* tw4M, hipStream_t stream);
+hipError_t launch_wl_conv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* S,
+                          float2* Z, const float2* tw4Q, const float2* tw4M, hipStream_t stream);
 hipError_t launch_conv_large(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y,
                              const float2* khat, float2* Z, const float2* twtab, hipStream_t stream);
 hipError_t launch_discretize(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
@@ -135,6 +139,12 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.tw4_bytes = (size_t)2 * M * sizeof(float2);
         off = align256(off + w.tw4_bytes);
     }
+    if ((op == SSM_OP_FFTCONV || op == SSM_OP_FORWARD) && M > ((int64_t)1 << kMaxLdsLogM)) {
+        // the inner transforms' table (2 x 16384 entries), then the whole length's (2M)
+        w.tw4 = off;
+        w.tw4_bytes = (size_t)(2 * ((int64_t)1 << kMaxLdsLogM) + 2 * M) * sizeof(float2);
+        off = align256(off + w.tw4_bytes);
+    }
     if (op == SSM_OP_FORWARD_COMPLEX) {
         w.kbuf = off;
         w.kbuf_bytes = (size_t)H * L * sizeof(float2);
@@ -150,6 +160,16 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
 }
 
 int device_status(hipError_t e) { return e == hipSuccess ? SSM_OK : SSM_ERR_DEVICE; }
+
+// M > 16384 in the forward path: the kernel transform from the scrambled root
+// values (in place on them; K written to K_out when given), then the spectrum
+// of Re K + D delta_0
+hipError_t launch_spectrum_wl(int64_t H, int64_t L, int64_t M, int64_t tiles, float2* roots, const int32_t* tstat,
+                              const float* D, float2* K_out, int32_t* status, float2* khat, float2* tw4,
+                              hipStream_t s) {
+    return launch_wl_spectrum(H, L, M, tiles, roots, tstat, status, nullptr, 1, D, K_out, khat, tw4,
+                              tw4 + 2 * ((int64_t)1 << kMaxLdsLogM), s);
+}
 
 }  // namespace
 
@@ -260,7 +280,8 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     int32_t* tstat = (int32_t*)(base + w.tstat);
     float2* twtab = (float2*)(base + w.tw);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s,
+                                 false);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {  // kernel transform only: no spectra
         if (M > ((int64_t)1 << kMaxLdsLogM))
@@ -288,15 +309,18 @@ int ssm_fftconv(int64_t Bsz, int64_t H, int64_t L, const float* K, int64_t k_str
     float2* khat = (float2*)((char*)ws + w.khat);
     float2* twtab = (float2*)((char*)ws + w.tw);
     if (M > ((int64_t)1 << kMaxLdsLogM)) {
-        hipError_t e = launch_spectrum_large(false, H, L, M, 0, nullptr, nullptr, nullptr, K, k_stride, D, nullptr,
-                                             nullptr, khat, twtab, s);
+        float2* tw4Q = (float2*)((char*)ws + w.tw4);
+        float2* tw4M = tw4Q + 2 * ((int64_t)1 << kMaxLdsLogM);
+        hipError_t e = launch_wl_spectrum(H, L, M, 0, nullptr, nullptr, nullptr, K, k_stride, D, nullptr, khat, tw4Q,
+                                          tw4M, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
-        return device_status(launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)((char*)ws + w.big), twtab, s));
+        return device_status(
+            launch_wl_conv(Bsz, H, L, M, u, y, khat, (float2*)((char*)ws + w.big), tw4Q, tw4M, s));
     }
     if (wave_path_fits(M)) {
         float2* tw4 = (float2*)((char*)ws + w.tw4);
         hipError_t e = launch_wspectrum(false, H, L, M, 0, nullptr, nullptr, K, k_stride, D, nullptr, nullptr, khat,
-                                        twtab, tw4, s);
+                                        tw4, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
         return device_status(launch_wconv(Bsz, H, L, M, u, y, khat, tw4, s));
     }
@@ -361,30 +385,34 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
             return SSM_ERR_DEVICE;
         return SSM_OK;
     }
-    for (int i = 0; i < repeat && e == hipSuccess; ++i)
-        e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
-                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
-    if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
     const bool fused = form == 2;
     const bool wave = !large && !fused && wave_path_fits(M);
+    // the wave-structured transforms take the root values in their own order
+    const bool scrambled = large || wave;
+    for (int i = 0; i < repeat && e == hipSuccess; ++i)
+        e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
+                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s, scrambled);
+    if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
     for (int i = 0; i < repeat && e == hipSuccess && !fused; ++i) {
         if (large && i > 0)
             e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s);
+                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s,
+                              scrambled);
         if (e != hipSuccess) break;
-        e = large  ? launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, roots, tstat, nullptr, 1, D,
-                                           (float2*)K_out, status, khat, twtab, s)
+        e = large  ? launch_spectrum_wl(H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out, status,
+                                        khat, (float2*)(base + w.tw4), s)
             : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
-                                      (float2*)K_out, status, khat, twtab, (float2*)(base + w.tw4), s)
+                                      (float2*)K_out, status, khat, (float2*)(base + w.tw4), s)
                    : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
                                      (float2*)K_out, status, khat, twtab, s);
     }
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
-        e = large   ? launch_conv_large(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), twtab, s)
+        e = large   ? launch_wl_conv(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), (const float2*)(base + w.tw4),
+                                     (const float2*)(base + w.tw4) + 2 * ((int64_t)1 << kMaxLdsLogM), s)
             : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out,
                                         status, u, y, twtab, s)
             : wave  ? launch_wconv(Bsz, H, L, M, u, y, khat, (const float2*)(base + w.tw4), s)
@@ -441,7 +469,7 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
     const int64_t tiles = cauchy_tiles(H, r, M);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab,
-                                 (double*)(base + w.tant), s);
+                                 (double*)(base + w.tant), s, false);
     // real part: the spectra of Re K + D delta_0 from the root values (K written on the way)
     if (e == hipSuccess)
         e = large ? launch_spectrum_large(true, H, L, M, tiles, roots, roots, tstat, nullptr, 1, D, K, status, khat,

@@ -28,6 +28,7 @@
 
 #include "common.hpp"
 #include "roots.hpp"
+#include "wfft.hpp"
 
 namespace ssm {
 
@@ -49,7 +50,7 @@ template <int RK, int RPT>
 // rank 1: registers capped for four waves per SIMD (fits without spills;
 // measured faster than three waves with more registers)
 __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(RK == 1 ? 4 : 1))) void cauchy_roots_kernel(
-    int M, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
+    int M, int scr_logm, int N, int tiles, const float2* __restrict__ Lambda, const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, float2* __restrict__ roots, int32_t* __restrict__ tile_status,
     const double* __restrict__ tant, float2* __restrict__ twtab) {
@@ -88,11 +89,16 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 
     const double a = 2.0 / (double)dtv;
     float st[RPT], tf[RPT];
-    int kk[RPT];
+    int kk[RPT], kf[RPT];
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-        const int k = tile * (kCauchyThreads * RPT) + i * kCauchyThreads + tid;
-        kk[i] = k;
+        // the output position; the root it holds is the same index in natural
+        // order, or (scr_logm > 0) the frequency of that position in the
+        // wave-structured transforms' scrambled order
+        const int pos = tile * (kCauchyThreads * RPT) + i * kCauchyThreads + tid;
+        const int k = (scr_logm > 0 && pos < M) ? wf_freq_rt(scr_logm, pos) : pos;
+        kk[i] = pos;
+        kf[i] = k;
         st[i] = 0.0f;
         tf[i] = 0.0f;
         if (k < M) {
@@ -153,7 +159,8 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     if constexpr (FAIR) __builtin_amdgcn_s_setprio(0);
     // reduce the z = -1 partial sums when this tile holds k = M/2 (uniform test)
     const int k_lo = tile * (kCauchyThreads * RPT);
-    const bool has_m1 = M >= 2 && k_lo <= M / 2 && M / 2 < k_lo + kCauchyThreads * RPT;
+    const int pos_m1 = scr_logm > 0 ? 512 : M / 2;  // where the root z = -1 (k = M/2) is stored
+    const bool has_m1 = M >= 2 && k_lo <= pos_m1 && pos_m1 < k_lo + kCauchyThreads * RPT;
     double2 m1 = make_double2(0.0, 0.0);
     if (has_m1) {
 #pragma unroll
@@ -175,11 +182,11 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     for (int i = 0; i < RPT; ++i) {
         float2 sums[F];
         acc_unpack<RK>(acc[i], sums);  // every lane, before the range test
-        const int k = kk[i];
-        if (k >= M) continue;
+        const int pos = kk[i], k = kf[i];
+        if (pos >= M) continue;
         const float2 H = 2 * k == M ? make_float2((float)(0.5 * dtv * m1.x), (float)(0.5 * dtv * m1.y))
                                     : finish_root<RK>(sums, st[i], tf[i], N, hbase, Lambda, P, Q, Bv, Ct, my_status);
-        roots[(size_t)h * M + k] = H;
+        roots[(size_t)h * M + pos] = H;
     }
     if (my_status) atomicMax(&blk_status, my_status);
     __syncthreads();
@@ -187,9 +194,9 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 }
 
 template <int RK, int RPT>
-hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, const float2* P, const float2* Q,
-                     const float2* Bv, const float2* Ct, const float* dt, float2* roots, int32_t* tstat,
-                     float2* twtab, double* tant, hipStream_t stream) {
+hipError_t launch_rk(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
+                     const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
+                     int32_t* tstat, float2* twtab, double* tant, hipStream_t stream) {
     if (RPT >= 4) {
         hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M, tant,
                            twtab);
@@ -198,7 +205,7 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, const float2* Lambda, cons
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
     const int64_t blocks = H * tiles;
     hipLaunchKernelGGL((cauchy_roots_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream,
-                       (int)M, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat, tant, twtab);
+                       (int)M, scr_logm, (int)N, tiles, Lambda, P, Q, Bv, Ct, dt, roots, tstat, tant, twtab);
     return hipGetLastError();
 }
 
@@ -220,13 +227,18 @@ int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
     return (M + per - 1) / per;
 }
 
+// scrambled: store the root values in the order the wave-structured
+// transforms take them (M >= 1024), not in natural order
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream) {
+                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream, bool scrambled) {
     const int rpt = cauchy_rpt(H, r, M);
+    const int scr_logm = scrambled ? ilog2_exact(M) : 0;
+    if (scrambled && M < 1024) return hipErrorInvalidValue;
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
     if (r == RK && rpt == RPT)                                                                                \
-        return launch_rk<RK, RPT>(H, N, M, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, stream);
+        return launch_rk<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, \
+                                  stream);
     SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
     SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY

@@ -32,20 +32,19 @@ namespace {
 // Spectrum S_A of one channel's real kernel k (taps >= L zero, D at tap 0),
 // scaled 1/(2M), into khat[h] (M complex, scrambled order).  FROM_ROOTS:
 // k = Re K, K the first L taps of the inverse transform of the root values
-// (also written to K_out); the per-channel status is reduced from the
-// root-value kernel's tile statuses, and a failing channel gets a NaN spectrum
-// and kernel.  Otherwise k is read from a caller's kernel (stride kstride).
-// twtab: exp(-i pi j/M), j < M (the inverse transform); tw4: exp(-i pi j/(2M)),
-// j < 2M (the wave-structured transform).
+// (stored in the transform's scrambled order; K is also written to K_out);
+// the per-channel status is reduced from the root-value kernel's tile
+// statuses, and a failing channel gets a NaN spectrum and kernel.  Otherwise k
+// is read from a caller's kernel (stride kstride).  tw4: exp(-i pi j/(2M)),
+// j < 2M.
 template <int LOGM, bool FROM_ROOTS>
 __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4))) void wspec_kernel(
     int L, int tiles, const float2* __restrict__ roots, const int32_t* __restrict__ tile_status,
     const float* __restrict__ Kin, int64_t kstride, const float* __restrict__ D, float2* __restrict__ K_out,
-    int32_t* __restrict__ status, float2* __restrict__ khat, const float2* __restrict__ twtab,
-    const float2* __restrict__ tw4) {
+    int32_t* __restrict__ status, float2* __restrict__ khat, const float2* __restrict__ tw4) {
     using G = WGeo<LOGM>;
     constexpr int M = G::M, T = G::T;
-    __shared__ float2 lds[G::LDS > lds_padded_size(M) ? G::LDS : lds_padded_size(M)];
+    __shared__ float2 lds[G::LDS];
     __shared__ int sst;
     const int h = blockIdx.x;
     const int t = threadIdx.x;
@@ -66,19 +65,19 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
             for (int j = t; j < M; j += T) kh[j] = c_nan();
             return;
         }
-        // the inverse transform of the root values in natural order (Stockham,
-        // 16 points per thread: the same thread count as the wave layout)
-        const TwiddleRegs<LOGM, 4> tw(twtab, LOGM, t);
-        float2 v[1][16];
+        // the root values are stored in the transform's scrambled order: the
+        // mirrored steps give the inverse transform in natural order
+        const rsrc_t rr = make_rsrc(roots + (size_t)h * M, M * sizeof(float2));
+        const uint32_t vp = (uint32_t)wf_pos(t, 0) * sizeof(float2);
+        float2 v[16];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) v[0][e] = roots[(size_t)h * M + t + T * e];
-        float2* const one[1] = {lds};
-        fft_multi<1, LOGM, 4, true>(v, one, t, tw);
+        for (int e = 0; e < 16; ++e) v[e] = buf_ld_c64(rr, vp, e * 64 * sizeof(float2));
+        wf_inverse<LOGM, 0>(v, lds, tw4, t);
         const float invM = 1.0f / (float)M;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int j = t + T * e;
-            const float2 kv = c_scale(v[0][e], invM);
+            const float2 kv = c_scale(v[e], invM);
             if (K_out && j < L) K_out[(size_t)h * L + j] = kv;
             kr[e] = j < L ? kv.x : 0.0f;
         }
@@ -185,16 +184,16 @@ __global__ __launch_bounds__(256) void wtwiddle4_kernel(int M, float2* __restric
 template <int LOGM>
 hipError_t wspec_launch(bool from_roots, int64_t H, int64_t L, int64_t tiles, const float2* roots,
                         const int32_t* tstat, const float* Kin, int64_t kstride, const float* D, float2* K_out,
-                        int32_t* status, float2* khat, const float2* twtab, float2* tw4, hipStream_t stream) {
+                        int32_t* status, float2* khat, float2* tw4, hipStream_t stream) {
     using G = WGeo<LOGM>;
     hipLaunchKernelGGL(wtwiddle4_kernel, dim3((unsigned)((2 * G::M + 255) / 256)), dim3(256), 0, stream, G::M, tw4);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     if (from_roots)
         hipLaunchKernelGGL((wspec_kernel<LOGM, true>), dim3((unsigned)H), dim3(G::T), 0, stream, (int)L, (int)tiles,
-                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab, (const float2*)tw4);
+                           roots, tstat, Kin, kstride, D, K_out, status, khat, (const float2*)tw4);
     else
         hipLaunchKernelGGL((wspec_kernel<LOGM, false>), dim3((unsigned)H), dim3(G::T), 0, stream, (int)L, (int)tiles,
-                           roots, tstat, Kin, kstride, D, K_out, status, khat, twtab, (const float2*)tw4);
+                           roots, tstat, Kin, kstride, D, K_out, status, khat, (const float2*)tw4);
     return hipGetLastError();
 }
 
@@ -218,13 +217,12 @@ bool wave_path_fits(int64_t M) { return M >= 1024 && M <= 16384; }
 
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, const float2* twtab, float2* tw4,
-                            hipStream_t stream) {
+                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream) {
     switch (ilog2_exact(M)) {
 #define SSM_WSPEC_CASE(LG)                                                                                       \
     case LG:                                                                                                     \
         return wspec_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat,    \
-                                twtab, tw4, stream);
+                                tw4, stream);
         SSM_WSPEC_CASE(10) SSM_WSPEC_CASE(11) SSM_WSPEC_CASE(12) SSM_WSPEC_CASE(13) SSM_WSPEC_CASE(14)
 #undef SSM_WSPEC_CASE
         default: return hipErrorInvalidValue;

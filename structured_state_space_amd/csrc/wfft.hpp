@@ -109,6 +109,14 @@ __device__ __forceinline__ void pretwist64(float2 (&v)[16]) {
     }
 }
 
+// The next power of a twiddle is formed only after the current one has been
+// applied to `used`: an empty asm that takes `used` and passes p through.
+// Otherwise the compiler computes the whole chain of powers first (for
+// instruction-level parallelism) and holds all of them in registers.
+__device__ __forceinline__ void power_after(float2& p, const float2& used) {
+    asm volatile("" : "+v"(p.x), "+v"(p.y) : "v"(used.x), "v"(used.y));
+}
+
 // ---- stage A: DFT_16 over the register index, twiddle exp(-2 pi i t k/M)
 //      (TW: exp(-2 pi i t (TW + 4k)/(4M)), the per-register constant first) ----
 template <int LOGM, int TW, bool INV>
@@ -124,14 +132,20 @@ __device__ __forceinline__ void wf_twiddle_a(float2 (&v)[16], const float2* __re
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             v[k] = c_mul(v[k], p);
-            if (k < 15) p = c_mul(p, step);
+            if (k < 15) {
+                power_after(p, v[k]);
+                p = c_mul(p, step);
+            }
         }
     } else {
         float2 p = step;
 #pragma unroll
         for (int k = 1; k < 16; ++k) {
             v[k] = c_mul(v[k], p);
-            if (k < 15) p = c_mul(p, step);
+            if (k < 15) {
+                power_after(p, v[k]);
+                p = c_mul(p, step);
+            }
         }
     }
 }
@@ -162,7 +176,10 @@ __device__ __forceinline__ void wf_twiddle_b(float2 (&v)[16], const float2* __re
     for (int k = 1; k < G::W; ++k) {
 #pragma unroll
         for (int elo = 0; elo < G::S; ++elo) v[elo + G::S * k] = c_mul(v[elo + G::S * k], p);
-        if (k + 1 < G::W) p = c_mul(p, base);
+        if (k + 1 < G::W) {
+            power_after(p, v[G::S * k]);
+            p = c_mul(p, base);
+        }
     }
 }
 
@@ -332,6 +349,23 @@ __host__ __device__ constexpr int wf_freq(int wave, int e, int lane) {
     const int k2a = rb >> SB;
     const int k2b_a = lane & 3, k2b_b = e;
     return k1 + 16 * (k2a + W * (k2b_a + 4 * k2b_b));
+}
+
+// Run-time form for the root-value kernel: the frequency stored at position pos
+// of a channel's scrambled root values.  M <= 16384: the transform's own order;
+// M = P 16384 (P = 2, 4): slice k1 = pos / 16384 holds the frequencies P k2 + k1,
+// k2 in the order of the 16384-point transform.
+__host__ __device__ inline int wf_freq_rt(int logm, int pos) {
+    const int lq = logm < 14 ? logm : 14;
+    const int q = pos & ((1 << lq) - 1);
+    const int logw = lq - 10, sb = 4 - logw;
+    const int wave = q >> 10, e = (q >> 6) & 15, lane = q & 63;
+    const int rb = ((lane >> 4) & 3) | (((lane >> 2) & 3) << 2);
+    const int k1 = (rb & ((1 << sb) - 1)) | (wave << sb);
+    const int k2a = rb >> sb;
+    const int k = k1 + 16 * (k2a + (1 << logw) * ((lane & 3) + 4 * e));
+    if (logm <= 14) return k;
+    return (k << (logm - 14)) + (pos >> 14);
 }
 
 // ---- raw buffer access: the base and size in scalar registers, one 32-bit

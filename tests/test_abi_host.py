@@ -73,9 +73,13 @@ def test_workspace_sizes():
     assert ssm.workspace_bytes(ssm.OP_KERNEL_GEN, 1, H, 64, 1, 1024) >= H * M * 8 + M * 8
     assert ws % 256 == 0
     assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
-    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8 + M * 8
+    # fftconv for 1024 <= M <= 16384: spectra [H,2,M] c64, the table [M] c64 and the
+    # wave-structured transforms' table [2M] c64 (sizes multiples of 256 here)
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 8, H, 1, 1, 1024) == H * 2 * M * 8 + M * 8 + 2 * M * 8
     # ragged L uses M = next power of two
-    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 3000) == 3 * 2 * 4096 * 8 + 4096 * 8
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 3000) == 3 * 2 * 4096 * 8 + 4096 * 8 + 2 * 4096 * 8
+    # below 1024 points no second table
+    assert ssm.workspace_bytes(ssm.OP_FFTCONV, 1, 3, 1, 1, 512) == 3 * 2 * 512 * 8 + 512 * 8
 
 
 @pytest.mark.parametrize("args,code", [
@@ -135,14 +139,16 @@ def test_fftconv_and_kernel_gen_reject():
 
 def test_forward_complex_workspace_and_rejects():
     H, L = 256, 1000
-    fwd = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, L)
+    # the forward workspace less its wave-structured transforms' table [2M] c64,
+    # which the complex path does not use
+    fwd = ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, L) - 2 * 1024 * 8
     cpx = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, 8, H, 64, 1, L)
     assert cpx >= fwd + H * L * 8 and cpx % 256 == 0   # plus the complex kernel [H, L]
     # where the input's transforms are shared (here M = 1024) the imaginary
     # part's spectra [H, 2, M] live beside the real part's
     assert cpx >= fwd + H * L * 8 + H * 2 * 1024 * 8
     big = ssm.workspace_bytes(ssm.OP_FORWARD_COMPLEX, 8, H, 64, 1, 5000)
-    assert big - ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 5000) < H * 2 * 8192 * 8
+    assert big - (ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 1, 5000) - 2 * 8192 * 8) < H * 2 * 8192 * 8
 
     def call(r=1, y_re=FAKE, y_im=FAKE, ws_bytes=1 << 30):
         return ssm.lib.ssm_forward_complex(2, 3, 4, r, 16, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, y_re, y_im,
