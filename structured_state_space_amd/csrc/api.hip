@@ -10,9 +10,11 @@
 
 namespace ssm {
 int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
+int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream, bool scrambled);
+                         int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
+                         bool scrambled);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -101,7 +103,6 @@ int check_sizes(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, bool ne
 }
 
 WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L) {
-    (void)N;
     WsLayout w;
     const int64_t M = pow2_at_least(L);
     size_t off = 0;
@@ -116,6 +117,9 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.tant = off;
         w.tant_bytes = (size_t)M * sizeof(double);
         off = align256(off + w.tant_bytes);
+        w.cprep = off;
+        w.cprep_bytes = (size_t)cauchy_prep_bytes(H, N, r);
+        off = align256(off + w.cprep_bytes);
     }
     if (op == SSM_OP_FFTCONV || fwd) {
         w.khat = off;
@@ -280,7 +284,7 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     int32_t* tstat = (int32_t*)(base + w.tstat);
     float2* twtab = (float2*)(base + w.tw);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s,
+                                 (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s,
                                  false);
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {  // kernel transform only: no spectra
@@ -392,14 +396,14 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     const bool scrambled = large || wave;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
-                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s, scrambled);
+                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s, scrambled);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
     for (int i = 0; i < repeat && e == hipSuccess && !fused; ++i) {
         if (large && i > 0)
             e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
-                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), s,
+                              (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s,
                               scrambled);
         if (e != hipSuccess) break;
         e = large  ? launch_spectrum_wl(H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out, status,
@@ -469,7 +473,7 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
     const int64_t tiles = cauchy_tiles(H, r, M);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab,
-                                 (double*)(base + w.tant), s, false);
+                                 (double*)(base + w.tant), base + w.cprep, s, false);
     // real part: the spectra of Re K + D delta_0 from the root values (K written on the way)
     if (e == hipSuccess)
         e = large ? launch_spectrum_large(true, H, L, M, tiles, roots, roots, tstat, nullptr, 1, D, K, status, khat,

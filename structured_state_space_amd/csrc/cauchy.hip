@@ -34,16 +34,20 @@ namespace ssm {
 
 namespace {
 
-// Per-root tables, once per call: tan(pi k/M) in float64 (0 at k = M/2, which
-// takes the finite z = -1 formula) and exp(-i pi k/M) for the later transforms.
-__global__ __launch_bounds__(256) void root_tables_kernel(int M, double* __restrict__ tant,
+// Per-root tables, once per call: tan(pi k/M) in float64 for the root held at
+// each output position (0 at k = M/2, which takes the finite z = -1 formula;
+// scr_logm > 0: positions in the wave-structured transforms' order, else
+// natural order) and exp(-i pi j/M) for the later transforms.
+__global__ __launch_bounds__(256) void root_tables_kernel(int M, int scr_logm, double* __restrict__ tant,
                                                           float2* __restrict__ twtab) {
-    const int k = blockIdx.x * 256 + threadIdx.x;
-    if (k >= M) return;
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= M) return;
     double sn, cs;
-    sincospi((double)k / (double)M, &sn, &cs);
-    tant[k] = (2 * k == M) ? 0.0 : sn / cs;
-    twtab[k] = make_float2((float)cs, (float)-sn);
+    sincospi((double)j / (double)M, &sn, &cs);
+    twtab[j] = make_float2((float)cs, (float)-sn);
+    const int k = scr_logm > 0 ? wf_freq_rt(scr_logm, j) : j;
+    if (k != j) sincospi((double)k / (double)M, &sn, &cs);
+    tant[j] = (2 * k == M) ? 0.0 : sn / cs;
 }
 
 template <int RK, int RPT>
@@ -104,7 +108,7 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
         if (k < M) {
             double t;
             if constexpr (TAB) {
-                t = tant[k];
+                t = tant[pos];
             } else {
                 double sn, cs;
                 sincospi((double)k / (double)M, &sn, &cs);
@@ -193,13 +197,379 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     if (tid == 0) tile_status[blockIdx.x] = blk_status;
 }
 
+// ---------------------------------------------------------------------------
+// Ranks 2 and 3: the sums on the float16 matrix cores in split precision.
+// Per root k and state n the Cauchy entry g = 1/d, d = s_k - lambda_n, is
+// formed in float32 and scaled by the per-root sigma_k = sqrt(st^2 + X^2 + R^2)
+// (st = a t_k, X and R the largest |Re lambda| and |Im lambda| of the channel),
+// so that |d_n| <= sqrt(2) sigma_k for every state: every scaled entry has
+// |g sigma| >= 1/sqrt(2), a normal float16 value.  Near a resonance |g sigma| may
+// pass the float16 range; the conversion then gives an infinity, the sums are
+// not finite and the root takes the float32 recheck of the finish.  The weights
+// are scaled by the per-family tau_f (largest weight component), so |b| <= 1.
+// Both operands are split into float16 high and low parts, a = a_h + a_l (a_h
+// the rounding of a, a_l the rounding of the remainder a - a_h), and each
+// product is taken as a_h b_h + a_h b_l + a_l b_h with float32 accumulation:
+// three v_mfma_f32_32x32x16_f16 per block of 8 states and 32 roots.  The
+// dropped a_l b_l and the roundings of the low parts leave about 2^-21 of each
+// product.
+// Layout of one instruction: A is 32 roots x 16 (k = 2 s + c for the 8 states s
+// of the block and the components c of g = gx + i gy), B is 16 x 32 columns
+// (column 2 f + p: the real and imaginary parts p of family f), C is 32 roots x
+// 32 columns.  Lane l holds row l % 32 and k = 8 (l / 32) + 0..7 of A (four
+// states, both components), column l % 32 and the same k of B, and column
+// l % 32 of rows 8 (v / 4) + 4 (l / 32) + v % 4 of C.  Re(w g) = w.x gx - w.y gy
+// and Im(w g) = w.y gx + w.x gy give the B entries (gx row, gy row): column 2f:
+// (w.x, -w.y), column 2f + 1: (w.y, w.x).
+//
+// The per-channel part (the scales, the split weight blocks in the order the
+// sweep reads them, the state headers and the z = -1 sum) is formed once per
+// channel by a small kernel and copied to LDS by each root tile.
+// ---------------------------------------------------------------------------
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+typedef float f2v __attribute__((ext_vector_type(2)));
+typedef float f16v __attribute__((ext_vector_type(16)));
+constexpr int kHChunk = 64;  // states staged in LDS at a time (8 blocks of 8)
+constexpr int kHBlockBytes = 2048;  // one block of 8 states: [lane half][hi, lo][32 columns] x 16 bytes
+
+// One channel's record: the weight blocks (npad / 8 x 2048 bytes), the
+// headers x = -Re lambda, x^2, Im lambda (npad floats each; padding states
+// x = 0, x^2 = 1), then 128 bytes of scales: tau_f (16 floats), X^2 + R^2,
+// and the z = -1 sum C~^* B (float64).
+struct HRec {
+    int64_t npad, hdr, scal, bytes;
+    __host__ __device__ explicit HRec(int64_t N) {
+        npad = (N + 7) & ~(int64_t)7;
+        hdr = npad / 8 * kHBlockBytes;
+        scal = hdr + 3 * npad * 4;
+        bytes = scal + 128;
+    }
+};
+
+// (a, b) as float16 high and low parts: hi the rounding, lo the rounding of the
+// float32 remainder
+__device__ __forceinline__ void split_pair(float a, float b, h2& hi, h2& lo) {
+    const f2v v = {a, b};
+    hi = __builtin_convertvector(v, h2);
+    const f2v r = {a - (float)hi[0], b - (float)hi[1]};
+    lo = __builtin_convertvector(r, h2);
+}
+
+template <int RK>
+__global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2* __restrict__ Lambda,
+                                                            const float2* __restrict__ P, const float2* __restrict__ Q,
+                                                            const float2* __restrict__ Bv,
+                                                            const float2* __restrict__ Ct, char* __restrict__ prep) {
+    constexpr int F = Fam<RK>::F;
+    const HRec rec(N);
+    const int h = blockIdx.x, tid = threadIdx.x;
+    const size_t hbase = (size_t)h * N;
+    char* const out = prep + (size_t)h * rec.bytes;
+    __shared__ unsigned int mx_bits[F + 2];  // tau_f, X^2, R^2 (non-negative floats order as integers)
+    __shared__ double2 red[4];
+    if (tid < F + 2) mx_bits[tid] = 0u;
+    __syncthreads();
+    double m1x = 0.0, m1y = 0.0;
+    {
+        float tl[F + 2];
+#pragma unroll
+        for (int f = 0; f < F + 2; ++f) tl[f] = 0.0f;
+        for (int n = tid; n < N; n += 256) {
+            const size_t hn = hbase + n;
+            const float2 lam = Lambda[hn];
+            tl[F] = fmaxf(tl[F], lam.x * lam.x);
+            tl[F + 1] = fmaxf(tl[F + 1], lam.y * lam.y);
+            float2 uu[RK + 1], vv[RK + 1];
+            uu[0] = Ct[hn];
+            vv[0] = Bv[hn];
+            // z = -1 takes (dt/2) C~^* B
+            m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
+            m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                uu[1 + j] = Q[hn * RK + j];
+                vv[1 + j] = P[hn * RK + j];
+            }
+#pragma unroll
+            for (int iu = 0; iu <= RK; ++iu)
+#pragma unroll
+                for (int iv = 0; iv <= RK; ++iv) {
+                    const float2 w = c_mul(c_conj(uu[iu]), vv[iv]);
+                    const int f = iu * (RK + 1) + iv;
+                    tl[f] = fmaxf(tl[f], fmaxf(fabsf(w.x), fabsf(w.y)));
+                }
+        }
+#pragma unroll
+        for (int f = 0; f < F + 2; ++f)
+            if (tl[f] > 0.0f) atomicMax(&mx_bits[f], __float_as_uint(tl[f]));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) {
+            m1x += __shfl_xor(m1x, o, 64);
+            m1y += __shfl_xor(m1y, o, 64);
+        }
+        if ((tid & 63) == 0) red[tid >> 6] = make_double2(m1x, m1y);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float* const sc = reinterpret_cast<float*>(out + rec.scal);
+        for (int f = 0; f < 16; ++f) sc[f] = f < F ? __uint_as_float(mx_bits[f]) : 0.0f;
+        double* const sd = reinterpret_cast<double*>(out + rec.scal + 64);
+        sd[0] = (double)__uint_as_float(mx_bits[F]) + (double)__uint_as_float(mx_bits[F + 1]);
+        sd[1] = red[0].x + red[1].x + red[2].x + red[3].x;
+        sd[2] = red[0].y + red[1].y + red[2].y + red[3].y;
+    }
+    // headers
+    float* const hx = reinterpret_cast<float*>(out + rec.hdr);
+    for (int n = tid; n < rec.npad; n += 256) {
+        float2 lam = make_float2(0.0f, 0.0f);
+        float x2 = 1.0f;
+        if (n < N) {
+            lam = Lambda[hbase + n];
+            x2 = lam.x * lam.x;
+        }
+        hx[n] = -lam.x;
+        hx[rec.npad + n] = x2;
+        hx[2 * rec.npad + n] = lam.y;
+    }
+    // weight blocks: one 16-byte group (block, lane half, column) per item, hi and lo
+    const int items = (int)(rec.npad / 8) * 64;
+    for (int it = tid; it < items; it += 256) {
+        const int kb = it >> 6, lh = (it >> 5) & 1, col = it & 31, f = col >> 1;
+        float itau = 0.0f;
+        if (f < F) {
+            const float t = __uint_as_float(mx_bits[f]);
+            itau = t > 0.0f ? 1.0f / t : 0.0f;
+        }
+        h8 hi8, lo8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int n = 8 * kb + 4 * lh + q;
+            float2 w = make_float2(0.0f, 0.0f);
+            if (n < N && f < F) {
+                const size_t hn = hbase + n;
+                const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
+                w = c_mul(c_conj(fam_u<RK>(Ct, Q, hn, iu)), fam_v<RK>(Bv, P, hn, iv));
+            }
+            const float wx = w.x * itau, wy = w.y * itau;
+            h2 hi, lo;
+            if (col & 1)
+                split_pair(wy, wx, hi, lo);  // column 2f + 1: (w.y, w.x)
+            else
+                split_pair(wx, -wy, hi, lo);  // column 2f: (w.x, -w.y)
+            hi8[2 * q] = hi[0];
+            hi8[2 * q + 1] = hi[1];
+            lo8[2 * q] = lo[0];
+            lo8[2 * q + 1] = lo[1];
+        }
+        h8* const dst = reinterpret_cast<h8*>(out + (size_t)kb * kHBlockBytes + lh * 1024 + col * 16);
+        dst[0] = hi8;
+        dst[32] = lo8;
+    }
+}
+
+// Copy states [n0, n0 + 8 nkb) of a channel's record to LDS: the weight blocks
+// (all loads issued before the stores) and the three header rows.
+__device__ __forceinline__ void h_stage(char* smem, float* hx, const char* rp, int npad, int hdr, int n0, int nkb,
+                                        int tid) {
+    static_assert(kHChunk / 8 * (kHBlockBytes / 16) == 4 * kCauchyThreads, "four float4 per thread in a full chunk");
+    const float4* const src = reinterpret_cast<const float4*>(rp + (size_t)(n0 / 8) * kHBlockBytes);
+    float4* const dst = reinterpret_cast<float4*>(smem);
+    const int total = nkb * (kHBlockBytes / 16);
+    if (total == 4 * kCauchyThreads) {
+        const float4 v0 = src[tid], v1 = src[tid + kCauchyThreads], v2 = src[tid + 2 * kCauchyThreads],
+                     v3 = src[tid + 3 * kCauchyThreads];
+        dst[tid] = v0;
+        dst[tid + kCauchyThreads] = v1;
+        dst[tid + 2 * kCauchyThreads] = v2;
+        dst[tid + 3 * kCauchyThreads] = v3;
+    } else {
+        for (int i = tid; i < total; i += kCauchyThreads) dst[i] = src[i];
+    }
+    static_assert(3 * kHChunk <= kCauchyThreads, "one header value per thread");
+    const int c = tid / kHChunk, n = tid % kHChunk;
+    if (c < 3 && n < 8 * nkb) hx[c * kHChunk + n] = reinterpret_cast<const float*>(rp + hdr)[c * npad + n0 + n];
+}
+
+template <int RK, int RPT>
+__global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(3))) void cauchy_h_kernel(
+    int M, int pos_m1, int N, int tiles, int tpw, const float2* __restrict__ Lambda, const float2* __restrict__ P,
+    const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
+    const float* __restrict__ dt, const char* __restrict__ prep, const double* __restrict__ tant,
+    float2* __restrict__ roots, int32_t* __restrict__ tile_status) {
+    constexpr int F = Fam<RK>::F, NC = 2 * F;
+    static_assert(NC <= 32, "one block of 32 columns");
+    constexpr int NB = 2 * RPT;  // blocks of 32 roots per wave
+    constexpr int TILE = kCauchyThreads * RPT;
+    // the staged chunk (weight blocks, then the headers), and each wave's C
+    // block with a row per root
+    __shared__ __align__(16) char smem[kHChunk / 8 * kHBlockBytes + 3 * kHChunk * 4];
+    __shared__ float ctr_s[(kCauchyThreads / 64) * 32 * 33];
+    __shared__ int blk_status;
+    float* const hx = reinterpret_cast<float*>(smem + kHChunk / 8 * kHBlockBytes);  // x = -Re lambda
+    float* const hx2 = hx + kHChunk;                                               // x^2
+    float* const him = hx2 + kHChunk;                                              // Im lambda
+
+    // this workgroup: tiles [t0, t1) of channel h (tpw tiles per workgroup)
+    const int wpc = (tiles + tpw - 1) / tpw;
+    const int h = blockIdx.x / wpc;
+    const int t0 = (blockIdx.x - h * wpc) * tpw, t1 = min(t0 + tpw, tiles);
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int lh = lane >> 5, row = lane & 31;
+    const size_t hbase = (size_t)h * N;
+    const float dtv = dt[h];
+    if (!(dtv > 0.0f) || !(dtv <= FLT_MAX)) {  // uniform over the workgroup
+        for (int i = t0 * TILE + tid; i < t1 * TILE; i += kCauchyThreads)
+            if (i < M) roots[(size_t)h * M + i] = c_nan();
+        if (tid < t1 - t0) tile_status[(size_t)h * tiles + t0 + tid] = SSM_ST_INVALID_STEP;
+        return;
+    }
+    const HRec rec(N);
+    const char* const rp = prep + (size_t)h * rec.bytes;
+    const float xr2 = (float)*reinterpret_cast<const double*>(rp + rec.scal + 64);
+    const double a = 2.0 / (double)dtv;
+    const bool one_chunk = N <= kHChunk;
+    if (one_chunk) h_stage(smem, hx, rp, (int)rec.npad, (int)rec.hdr, 0, (N + 7) >> 3, tid);
+    float* const ctr = ctr_s + wv * (32 * 33);
+    const float* const tau = reinterpret_cast<const float*>(rp + rec.scal);  // uniform loads at the finish
+
+    for (int tile = t0; tile < t1; ++tile) {
+        if (tid == 0) blk_status = 0;
+        // this lane's roots: row l % 32 of the wave's NB blocks (vectors, not
+        // arrays: the finish selects an element per lane half)
+        typedef float fnb __attribute__((ext_vector_type(NB)));
+        fnb st, sig, tf;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int pos = tile * TILE + wv * (32 * NB) + nb * 32 + row;
+            const double t = pos < M ? tant[pos] : 0.0;
+            st[nb] = (float)(a * t);
+            tf[nb] = (float)t;
+            sig[nb] = sqrtf(fmaf(st[nb], st[nb], xr2));
+        }
+
+        f16v acc[NB];
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
+
+        for (int n0 = 0; n0 < N; n0 += kHChunk) {
+            const int nkb = (min(kHChunk, N - n0) + 7) >> 3;
+            if (!one_chunk) {
+                __syncthreads();  // the previous chunk's readers are done
+                h_stage(smem, hx, rp, (int)rec.npad, (int)rec.hdr, n0, nkb, tid);
+            }
+            __syncthreads();
+            const h8* const bsh = reinterpret_cast<const h8*>(smem) + lh * 64 + row;
+            for (int kb = 0; kb < nkb; ++kb) {
+                const float4 x4 = *reinterpret_cast<const float4*>(&hx[8 * kb + 4 * lh]);
+                const float4 q4 = *reinterpret_cast<const float4*>(&hx2[8 * kb + 4 * lh]);
+                const float4 i4 = *reinterpret_cast<const float4*>(&him[8 * kb + 4 * lh]);
+                const h8 bh = bsh[kb * 128];
+                const h8 bl = bsh[kb * 128 + 32];
+                const float xs[4] = {x4.x, x4.y, x4.z, x4.w};
+                const float x2s[4] = {q4.x, q4.y, q4.z, q4.w};
+                const float ims[4] = {i4.x, i4.y, i4.z, i4.w};
+                h8 ah[NB], al[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const float y = st[nb] - ims[q];
+                        const float inv = __builtin_amdgcn_rcpf(fmaf(y, y, x2s[q])) * sig[nb];
+                        h2 hi, lo;
+                        split_pair(xs[q] * inv, -y * inv, hi, lo);
+                        ah[nb][2 * q] = hi[0];
+                        ah[nb][2 * q + 1] = hi[1];
+                        al[nb][2 * q] = lo[0];
+                        al[nb][2 * q + 1] = lo[1];
+                    }
+                // independent accumulators back to back
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[nb], bh, acc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[nb], bl, acc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[nb], bh, acc[nb], 0, 0, 0);
+            }
+        }
+
+        // C through LDS to one root per lane (lanes 0-31 and 32-63 take the
+        // rows of alternate blocks), unscaled, then the Woodbury finish
+        int my_status = 0;
+#pragma unroll
+        for (int nb2 = 0; nb2 < NB; nb2 += 2) {
+            float2 sums[F];
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                if (row < NC) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) ctr[(8 * (v >> 2) + 4 * lh + (v & 3)) * 33 + row] = acc[nb2 + hb][v];
+                }
+                lds_sync<true>();
+                if (lh == hb) {
+                    const float us = rcp_safe(sig[nb2 + hb]);
+#pragma unroll
+                    for (int f = 0; f < F; ++f)
+                        sums[f] = make_float2(ctr[row * 33 + 2 * f] * (tau[f] * us),
+                                              ctr[row * 33 + 2 * f + 1] * (tau[f] * us));
+                }
+                lds_sync<true>();
+            }
+            const float stv = lh ? st[nb2 + 1] : st[nb2];
+            const float tfv = lh ? tf[nb2 + 1] : tf[nb2];
+            const int pos = tile * TILE + wv * (32 * NB) + (nb2 + lh) * 32 + row;
+            if (pos < M) {
+                float2 Hk;
+                if (pos == pos_m1) {
+                    const double* const m1 = reinterpret_cast<const double*>(rp + rec.scal + 72);
+                    Hk = make_float2((float)(0.5 * dtv * m1[0]), (float)(0.5 * dtv * m1[1]));
+                } else {
+                    Hk = finish_root<RK>(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                }
+                roots[(size_t)h * M + pos] = Hk;
+            }
+        }
+        __syncthreads();  // blk_status reset is visible
+        if (my_status) atomicMax(&blk_status, my_status);
+        __syncthreads();
+        if (tid == 0) tile_status[(size_t)h * tiles + tile] = blk_status;
+    }
+}
+
+template <int RK, int RPT>
+hipError_t launch_h(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
+                    const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
+                    int32_t* tstat, float2* twtab, double* tant, char* prep, hipStream_t stream) {
+    hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M, scr_logm,
+                       tant, twtab);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    hipLaunchKernelGGL((cauchy_h_prep_kernel<RK>), dim3((unsigned)H), dim3(256), 0, stream, (int)N, Lambda, P, Q, Bv,
+                       Ct, prep);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
+    // tiles per workgroup: up to 4 while the grid keeps 8192 workgroups (the
+    // staged weights are reused across a workgroup's tiles)
+    int tpw = 1;
+    while (tpw < 4 && tpw < tiles && H * ((tiles + 2 * tpw - 1) / (2 * tpw)) >= 8192) tpw *= 2;
+    const int64_t blocks = H * ((tiles + tpw - 1) / tpw);
+    const int pos_m1 = M < 2 ? -1 : scr_logm > 0 ? 512 : (int)(M / 2);  // where the root z = -1 is stored
+    hipLaunchKernelGGL((cauchy_h_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream, (int)M,
+                       pos_m1, (int)N, tiles, tpw, Lambda, P, Q, Bv, Ct, dt, prep, tant, roots, tstat);
+    return hipGetLastError();
+}
+
 template <int RK, int RPT>
 hipError_t launch_rk(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
                      const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                      int32_t* tstat, float2* twtab, double* tant, hipStream_t stream) {
     if (RPT >= 4) {
-        hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M, tant,
-                           twtab);
+        hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M,
+                           scr_logm, tant, twtab);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
@@ -211,11 +581,12 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, int scr_logm, const float2
 
 }  // namespace
 
-// roots per thread: up to 4 for r = 1 and 2 for r = 2 (more sums share each
-// staged weight row; these were measured fastest, the accumulators of more
-// roots crowd out waves), while the grid keeps at least 1024 workgroups
+// roots per thread: up to 4 for r = 1 (more sums share each staged weight row;
+// measured fastest, the accumulators of more roots crowd out waves), one for
+// the split-precision kernel of ranks 2 and 3 (64 roots per wave, four waves
+// per SIMD), while the grid keeps at least 1024 workgroups
 int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
-    const int max_rpt = r == 1 ? 4 : r == 2 ? 2 : 1;
+    const int max_rpt = r == 1 ? 4 : 1;
     int rpt = max_rpt;
     while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
         rpt >>= 1;
@@ -227,11 +598,17 @@ int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
     return (M + per - 1) / per;
 }
 
+// per-channel records of the split-precision path (ranks 2 and 3), else none
+int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r) {
+    return (r == 2 || r == 3) ? H * HRec(N).bytes : 0;
+}
+
 // scrambled: store the root values in the order the wave-structured
 // transforms take them (M >= 1024), not in natural order
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                         int32_t* tile_status, float2* twtab, double* tant, hipStream_t stream, bool scrambled) {
+                         int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
+                         bool scrambled) {
     const int rpt = cauchy_rpt(H, r, M);
     const int scr_logm = scrambled ? ilog2_exact(M) : 0;
     if (scrambled && M < 1024) return hipErrorInvalidValue;
@@ -239,9 +616,15 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
     if (r == RK && rpt == RPT)                                                                                \
         return launch_rk<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, \
                                   stream);
-    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1) SSM_CAUCHY(2, 2) SSM_CAUCHY(2, 1)
-    SSM_CAUCHY(3, 1) SSM_CAUCHY(4, 1)
+#define SSM_CAUCHY_H(RK, RPT)                                                                                  \
+    if (r == RK && rpt == RPT)                                                                                 \
+        return launch_h<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant,  \
+                                 (char*)prep, stream);
+    SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1)
+    SSM_CAUCHY_H(2, 1) SSM_CAUCHY_H(3, 1)
+    SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY
+#undef SSM_CAUCHY_H
     return hipErrorInvalidValue;
 }
 

@@ -72,6 +72,7 @@ struct WsLayout {
     size_t kbuf = 0, kbuf_bytes = 0;       // [H, L] complex64: the kernel (complex output, no K_out given)
     size_t khat2 = 0, khat2_bytes = 0;     // [H, 2, M] complex64: spectra of Im K (complex output, shared-transform lengths)
     size_t tw4 = 0, tw4_bytes = 0;         // [2M] complex64: exp(-i pi j/(2M)), the wave-structured transforms' twiddles
+    size_t cprep = 0, cprep_bytes = 0;     // [H] per-channel records of the split-precision root values (ranks 2, 3)
     size_t total = 0;
 };
 

@@ -42,9 +42,16 @@ struct Fam {
     static constexpr int KS = G <= 2 ? 2 : 1;
 };
 
+// 1/d: the hardware reciprocal (1 ulp) where d and 1/d are normal numbers,
+// the IEEE division elsewhere
+__device__ __forceinline__ float rcp_safe(float d) {
+    const float m = fabsf(d);
+    return (m >= 1e-37f && m <= 1e37f) ? __builtin_amdgcn_rcpf(d) : 1.0f / d;
+}
+
 __device__ __forceinline__ float2 cdivf(float2 a, float2 b) {
     const float den = fmaf(b.x, b.x, b.y * b.y);
-    const float inv = 1.0f / den;
+    const float inv = rcp_safe(den);
     return make_float2(fmaf(a.x, b.x, a.y * b.y) * inv, fmaf(a.y, b.x, -a.x * b.y) * inv);
 }
 

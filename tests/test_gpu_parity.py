@@ -365,6 +365,71 @@ def test_single_launch_form(r, L, Bsz, N):
 
 
 # ---------------------------------------------------------------------------
+# ranks 2 and 3: root values on the float16 matrix cores in split precision
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("r,L", [(2, 2048), (3, 2048), (2, 20000)])
+def test_split_precision_root_values_hard_cases(r, L):
+    """A state 1e-6 from a root and outside the low-rank term, so H has a pole
+    there (its scaled Cauchy entries pass the float16 range and the root takes
+    the float32 recheck; with a low-rank coupling the Woodbury terms would cancel
+    to a value the float32 inputs do not determine), weights across eight decades, B = 0
+    (every family with B vanishes), the smallest and the largest step.  Root
+    values against the oracle's resolvent expression (the near-pole root also
+    against its own magnitude, and at M <= 4096 the rest of its row against the
+    largest of the rest), the
+    kernel against the inverse transform of those, and the forward outputs
+    (wave-structured transforms) against the oracle's recurrence."""
+    ssm = _ssm()
+    H, N, Bsz = 6, 72, 2
+    p = I.random_params(900 + 10 * r + L, H, N, r, L, lambda_kind="random")
+    M = O.transform_length(L)
+    kp = M // 4
+    p.dt[0] = 0.5                                    # a = 2/dt = 4 and tan(pi/4) = 1: s(z_{M/4}) = 4i
+    p.Lambda[0, 3] = np.complex64(-1e-7 + 1j * (4.0 + 1e-6))
+    p.P[0, 3], p.Q[0, 3] = 0, 0                      # decoupled from the low-rank term: a pole of H itself
+    w = np.logspace(0, -8, N).astype(np.float32)
+    p.P[1] *= w[:, None]
+    p.Q[1] *= w[::-1, None]
+    p.B[1] *= w
+    p.B[2] = 0
+    p.dt[3], p.dt[4] = 1e-4, 1.0
+    d = _dev(p)
+    out = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_kernel=True,
+                         want_roots=True)
+    assert np.all(_np(out["status"]) == 0)
+    roots, K = _np(out["roots"]), _np(out["K"])
+    ref = []
+    for h in range(H):
+        c = p.channel(h)
+        Hk, st = O.root_values(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], M)
+        assert st == O.OK
+        ref.append(Hk)
+    ref = np.array(ref)
+    assert np.abs(ref[0, kp]) > 1e2 * np.abs(np.delete(ref[0], kp)).max()   # the pole dominates its row
+    assert abs(roots[0, kp] - ref[0, kp]) <= TOL * abs(ref[0, kp])
+    if M <= 4096:
+        # the rest of the row against its own largest value; at larger M the
+        # pole's neighbours are within ~1e-3 of it, where rounding s(z_k) = i a t_k
+        # to float32 alone moves them by more than the tolerance of that value
+        assert_rows_close(np.delete(roots[0], kp)[None], np.delete(ref[0], kp)[None], what="root values ch0 (rest)")
+    assert_rows_close(roots, ref, what="root values")
+    assert not np.any(roots[2])                      # B = 0: exactly zero
+    assert_rows_close(K, np.fft.ifft(ref, axis=1)[:, :L], what="kernel")
+    # the forward path (roots in the transforms' order for M >= 1024)
+    u = I.random_input(L + r, Bsz, H, L)
+    disc = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_bbar=False)
+    assert np.all(_np(disc["status"]) == 0)
+    fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], disc["Ctilde"], d["dt"], d["D"],
+                     torch.from_numpy(u).to(DEV), want_kernel=True)
+    assert np.all(_np(fw["status"]) == 0)
+    Kf, y = _np(fw["K"]), _np(fw["y"])
+    for h in range(H):
+        r_ = _oracle_channel(p, h, u[:, h, :])
+        assert_rows_close(Kf[h][None], r_["K"][None], what=f"forward K h{h}")
+        assert_rows_close(y[:, h, :], r_["y"], what=f"y h{h}")
+
+
+# ---------------------------------------------------------------------------
 # edge cases: ragged and tiny lengths, odd batch, any N and r, unordered poles
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("H,N,r,L,Bsz,kind", [
