@@ -266,31 +266,85 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
     const int h = blockIdx.x, tid = threadIdx.x;
     const size_t hbase = (size_t)h * N;
     char* const out = prep + (size_t)h * rec.bytes;
+    float* const hx = reinterpret_cast<float*>(out + rec.hdr);
+    const int npad = (int)rec.npad;
+    const bool one = npad <= 256;  // one chunk: the vectors loaded for the scales stay in LDS
     __shared__ unsigned int mx_bits[F + 2];  // tau_f, X^2, R^2 (non-negative floats order as integers)
     __shared__ double2 red[4];
+    __shared__ float2 sl[256], sc[256], sb[256], sp[256 * RK], sq[256 * RK];
     if (tid < F + 2) mx_bits[tid] = 0u;
-    __syncthreads();
+
+    // one chunk of 256 states: this thread's state, the vectors zero past N
+    // (its headers: x = 0, x^2 = 1 there), staged in LDS
+    auto stage = [&](int n0) {
+        const int n = n0 + tid;
+        float2 lam = make_float2(0.0f, 0.0f), c = lam, b = lam;
+        float2 pv[RK], qv[RK];
+#pragma unroll
+        for (int j = 0; j < RK; ++j) pv[j] = qv[j] = lam;
+        if (n < N) {
+            const size_t hn = hbase + n;
+            lam = Lambda[hn];
+            c = Ct[hn];
+            b = Bv[hn];
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                pv[j] = P[hn * RK + j];
+                qv[j] = Q[hn * RK + j];
+            }
+        }
+        if (n < npad) {
+            sl[tid] = lam;
+            sc[tid] = c;
+            sb[tid] = b;
+#pragma unroll
+            for (int j = 0; j < RK; ++j) {
+                sp[tid * RK + j] = pv[j];
+                sq[tid * RK + j] = qv[j];
+            }
+            hx[n] = -lam.x;
+            hx[npad + n] = n < N ? lam.x * lam.x : 1.0f;
+            hx[2 * npad + n] = lam.y;
+        }
+    };
+
+    // the scales (largest weight component per family, X^2, R^2) and the
+    // z = -1 sum (dt/2) C~^* B in float64
     double m1x = 0.0, m1y = 0.0;
     {
         float tl[F + 2];
 #pragma unroll
         for (int f = 0; f < F + 2; ++f) tl[f] = 0.0f;
+        if (one) {
+            stage(0);
+            __syncthreads();
+        }
         for (int n = tid; n < N; n += 256) {
-            const size_t hn = hbase + n;
-            const float2 lam = Lambda[hn];
+            float2 lam, uu[RK + 1], vv[RK + 1];
+            if (one) {
+                lam = sl[n];
+                uu[0] = sc[n];
+                vv[0] = sb[n];
+#pragma unroll
+                for (int j = 0; j < RK; ++j) {
+                    uu[1 + j] = sq[n * RK + j];
+                    vv[1 + j] = sp[n * RK + j];
+                }
+            } else {
+                const size_t hn = hbase + n;
+                lam = Lambda[hn];
+                uu[0] = Ct[hn];
+                vv[0] = Bv[hn];
+#pragma unroll
+                for (int j = 0; j < RK; ++j) {
+                    uu[1 + j] = Q[hn * RK + j];
+                    vv[1 + j] = P[hn * RK + j];
+                }
+            }
             tl[F] = fmaxf(tl[F], lam.x * lam.x);
             tl[F + 1] = fmaxf(tl[F + 1], lam.y * lam.y);
-            float2 uu[RK + 1], vv[RK + 1];
-            uu[0] = Ct[hn];
-            vv[0] = Bv[hn];
-            // z = -1 takes (dt/2) C~^* B
             m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
             m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
-#pragma unroll
-            for (int j = 0; j < RK; ++j) {
-                uu[1 + j] = Q[hn * RK + j];
-                vv[1 + j] = P[hn * RK + j];
-            }
 #pragma unroll
             for (int iu = 0; iu <= RK; ++iu)
 #pragma unroll
@@ -300,71 +354,74 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
                     tl[f] = fmaxf(tl[f], fmaxf(fabsf(w.x), fabsf(w.y)));
                 }
         }
-#pragma unroll
-        for (int f = 0; f < F + 2; ++f)
-            if (tl[f] > 0.0f) atomicMax(&mx_bits[f], __float_as_uint(tl[f]));
+        // wave reductions by shuffles, then one LDS atomic per wave and value
 #pragma unroll
         for (int o = 32; o >= 1; o >>= 1) {
+#pragma unroll
+            for (int f = 0; f < F + 2; ++f) tl[f] = fmaxf(tl[f], __shfl_xor(tl[f], o, 64));
             m1x += __shfl_xor(m1x, o, 64);
             m1y += __shfl_xor(m1y, o, 64);
         }
-        if ((tid & 63) == 0) red[tid >> 6] = make_double2(m1x, m1y);
+        if ((tid & 63) == 0) {
+#pragma unroll
+            for (int f = 0; f < F + 2; ++f)
+                if (tl[f] > 0.0f) atomicMax(&mx_bits[f], __float_as_uint(tl[f]));
+            red[tid >> 6] = make_double2(m1x, m1y);
+        }
     }
     __syncthreads();
-    if (tid == 0) {
-        float* const sc = reinterpret_cast<float*>(out + rec.scal);
-        for (int f = 0; f < 16; ++f) sc[f] = f < F ? __uint_as_float(mx_bits[f]) : 0.0f;
+    if (tid < 16) {
+        reinterpret_cast<float*>(out + rec.scal)[tid] = tid < F ? __uint_as_float(mx_bits[tid]) : 0.0f;
+    } else if (tid == 16) {
         double* const sd = reinterpret_cast<double*>(out + rec.scal + 64);
         sd[0] = (double)__uint_as_float(mx_bits[F]) + (double)__uint_as_float(mx_bits[F + 1]);
         sd[1] = red[0].x + red[1].x + red[2].x + red[3].x;
         sd[2] = red[0].y + red[1].y + red[2].y + red[3].y;
     }
-    // headers
-    float* const hx = reinterpret_cast<float*>(out + rec.hdr);
-    for (int n = tid; n < rec.npad; n += 256) {
-        float2 lam = make_float2(0.0f, 0.0f);
-        float x2 = 1.0f;
-        if (n < N) {
-            lam = Lambda[hbase + n];
-            x2 = lam.x * lam.x;
+    // the weight blocks, per chunk of 256 states: one 16-byte group (block,
+    // lane half, column) per item, hi and lo
+    for (int n0 = 0; n0 < npad; n0 += 256) {
+        const int nch = min(256, npad - n0);
+        if (!one) {
+            __syncthreads();  // the previous chunk's readers are done
+            stage(n0);
+            __syncthreads();
         }
-        hx[n] = -lam.x;
-        hx[rec.npad + n] = x2;
-        hx[2 * rec.npad + n] = lam.y;
-    }
-    // weight blocks: one 16-byte group (block, lane half, column) per item, hi and lo
-    const int items = (int)(rec.npad / 8) * 64;
-    for (int it = tid; it < items; it += 256) {
-        const int kb = it >> 6, lh = (it >> 5) & 1, col = it & 31, f = col >> 1;
-        float itau = 0.0f;
-        if (f < F) {
-            const float t = __uint_as_float(mx_bits[f]);
-            itau = t > 0.0f ? 1.0f / t : 0.0f;
-        }
-        h8 hi8, lo8;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int n = 8 * kb + 4 * lh + q;
-            float2 w = make_float2(0.0f, 0.0f);
-            if (n < N && f < F) {
-                const size_t hn = hbase + n;
-                const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
-                w = c_mul(c_conj(fam_u<RK>(Ct, Q, hn, iu)), fam_v<RK>(Bv, P, hn, iv));
+        const int items = nch / 8 * 64;
+        for (int it = tid; it < items; it += 256) {
+            const int kbl = it >> 6, lh = (it >> 5) & 1, col = it & 31, f = col >> 1;
+            const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
+            float itau = 0.0f;
+            if (f < F) {
+                const float t = __uint_as_float(mx_bits[f]);
+                itau = t > 0.0f ? 1.0f / t : 0.0f;
             }
-            const float wx = w.x * itau, wy = w.y * itau;
-            h2 hi, lo;
-            if (col & 1)
-                split_pair(wy, wx, hi, lo);  // column 2f + 1: (w.y, w.x)
-            else
-                split_pair(wx, -wy, hi, lo);  // column 2f: (w.x, -w.y)
-            hi8[2 * q] = hi[0];
-            hi8[2 * q + 1] = hi[1];
-            lo8[2 * q] = lo[0];
-            lo8[2 * q + 1] = lo[1];
+            h8 hi8, lo8;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int nl = 8 * kbl + 4 * lh + q;
+                float2 w = make_float2(0.0f, 0.0f);
+                if (f < F) {
+                    const float2 u = iu == 0 ? sc[nl] : sq[nl * RK + iu - 1];
+                    const float2 v = iv == 0 ? sb[nl] : sp[nl * RK + iv - 1];
+                    w = c_mul(c_conj(u), v);  // zero for padding states
+                }
+                const float wx = w.x * itau, wy = w.y * itau;
+                h2 hi, lo;
+                if (col & 1)
+                    split_pair(wy, wx, hi, lo);  // column 2f + 1: (w.y, w.x)
+                else
+                    split_pair(wx, -wy, hi, lo);  // column 2f: (w.x, -w.y)
+                hi8[2 * q] = hi[0];
+                hi8[2 * q + 1] = hi[1];
+                lo8[2 * q] = lo[0];
+                lo8[2 * q + 1] = lo[1];
+            }
+            h8* const dst =
+                reinterpret_cast<h8*>(out + (size_t)(n0 / 8 + kbl) * kHBlockBytes + lh * 1024 + col * 16);
+            dst[0] = hi8;
+            dst[32] = lo8;
         }
-        h8* const dst = reinterpret_cast<h8*>(out + (size_t)kb * kHBlockBytes + lh * 1024 + col * 16);
-        dst[0] = hi8;
-        dst[32] = lo8;
     }
 }
 
