@@ -32,11 +32,12 @@ UNIT = "channel-steps/s"
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 PEAK_FP32_TFLOPS = 157.3       # MI355X FP32: dense matrix (MFMA) and vector peaks are both 157.3
 PEAK_FP64_TFLOPS = 78.6        # MI355X FP64 vector
+PEAK_FP16_TFLOPS = 2500.0      # MI355X dense FP16 matrix (no sparsity)
 DEFAULT_WORKLOAD = "s4-h1k-l16k"   # the largest workload: most channel-steps and bytes
 
 KERNEL_SOURCES = {
     "filter": ["single_launch.hip", "roots.hpp", "fft.hpp", "common.hpp"],
-    "cauchy": ["cauchy.hip", "roots.hpp", "common.hpp"],
+    "cauchy": ["cauchy.hip", "roots.hpp", "wfft.hpp", "common.hpp"],
     "spectrum": ["wconv.hip", "wlarge.hip", "multipass.hip", "spectrum_conv.hip", "wfft.hpp", "fft.hpp",
                  "common.hpp"],
     "conv": ["wconv.hip", "wlarge.hip", "spectrum_conv.hip", "wfft.hpp", "fft.hpp", "common.hpp"],
@@ -58,8 +59,12 @@ def algorithmic(w, M, fused):
     H, N, r, L, B = w.H, w.N, w.r, w.L, w.Bsz
     roots = M - 1 if M >= 2 else M                      # z = -1 takes its finite formula
     out = {
-        "cauchy": dict(bound="mfma", unit="TFLOP/s", work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12,
-                       peak=PEAK_FP32_TFLOPS),
+        # ranks 2 and 3 run the split-precision kernel, bound by the vector ALU
+        # (forming and splitting the Cauchy entries); rank 1 and 4 the float32
+        # matrix-core kernel.  Both rated on the same algorithmic flops against
+        # 157.3 TFLOP/s (the FP32 vector and FP32 dense matrix peaks coincide).
+        "cauchy": dict(bound="alu" if r in (2, 3) else "mfma", unit="TFLOP/s",
+                       work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12, peak=PEAK_FP32_TFLOPS),
         # the root values read, one spectrum of M complex written per channel
         "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
         "conv": dict(bound="hbm", unit="GB/s", work=8 * B * H * L + 4 * H * L + 4 * H, scale=1e-9,
@@ -584,6 +589,13 @@ def main():
         phases["conv"]["transform_flops_per_launch"] = conv_flops
         phases["conv"]["transform_tflops"] = tf
         phases["conv"]["transform_frac_fp32"] = tf / PEAK_FP32_TFLOPS
+    if "cauchy" in phases and w.r in (2, 3):
+        # the split-precision kernel's matrix-core side: three float16 products
+        # of 32 x 32 x 16 per block of 8 states and 32 roots (32 columns, of
+        # which 2 (r+1)^2 are used), against the dense float16 peak
+        mf = 3 * 2 * 32 * 32 * 16 * w.H * M * ((w.N + 7) // 8) / 32
+        phases["cauchy"]["matrix_core_flops_per_launch"] = mf
+        phases["cauchy"]["matrix_core_frac_fp16"] = mf * 1e-12 / (phase_ms["cauchy"] * 1e-3) / PEAK_FP16_TFLOPS
     dom = max(names, key=lambda k: phase_ms[k])
     traffic = read_traffic(dom, w.name)
     roofline = {"bound": phases[dom]["bound"], "achieved": phases[dom]["achieved"], "peak": phases[dom]["peak"],
