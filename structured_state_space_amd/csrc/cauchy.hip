@@ -450,7 +450,8 @@ __device__ __forceinline__ void h_stage(char* smem, float* hx, const char* rp, i
 
 template <int RK, int RPT>
 __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(3))) void cauchy_h_kernel(
-    int M, int pos_m1, int N, int tiles, int tpw, const float2* __restrict__ Lambda, const float2* __restrict__ P,
+    int M, int pos_m1, int N, int tiles, int tpw, int xcd_remap, const float2* __restrict__ Lambda,
+    const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, const char* __restrict__ prep, const double* __restrict__ tant,
     float2* __restrict__ roots, int32_t* __restrict__ tile_status) {
@@ -469,8 +470,14 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 
     // this workgroup: tiles [t0, t1) of channel h (tpw tiles per workgroup)
     const int wpc = (tiles + tpw - 1) / tpw;
-    const int h = blockIdx.x / wpc;
-    const int t0 = (blockIdx.x - h * wpc) * tpw, t1 = min(t0 + tpw, tiles);
+    int blk = blockIdx.x;
+    if (xcd_remap) {  // the workgroups of one channel on one XCD (dispatch is round-robin over 8), so
+                      // its record is fetched into one L2
+        const int x = blk & 7, s = blk >> 3;
+        blk = ((s / wpc) * 8 + x) * wpc + s % wpc;
+    }
+    const int h = blk / wpc;
+    const int t0 = (blk - h * wpc) * tpw, t1 = min(t0 + tpw, tiles);
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int lh = lane >> 5, row = lane & 31;
     const size_t hbase = (size_t)h * N;
@@ -615,8 +622,10 @@ hipError_t launch_h(int64_t H, int64_t N, int64_t M, int scr_logm, const float2*
     while (tpw < 4 && tpw < tiles && H * ((tiles + 2 * tpw - 1) / (2 * tpw)) >= 8192) tpw *= 2;
     const int64_t blocks = H * ((tiles + tpw - 1) / tpw);
     const int pos_m1 = M < 2 ? -1 : scr_logm > 0 ? 512 : (int)(M / 2);  // where the root z = -1 is stored
+    // the XCD mapping is a bijection on the grid when it holds whole groups of 8 channels
+    const int xcd_remap = H % 8 == 0 ? 1 : 0;
     hipLaunchKernelGGL((cauchy_h_kernel<RK, RPT>), dim3((unsigned)blocks), dim3(kCauchyThreads), 0, stream, (int)M,
-                       pos_m1, (int)N, tiles, tpw, Lambda, P, Q, Bv, Ct, dt, prep, tant, roots, tstat);
+                       pos_m1, (int)N, tiles, tpw, xcd_remap, Lambda, P, Q, Bv, Ct, dt, prep, tant, roots, tstat);
     return hipGetLastError();
 }
 
