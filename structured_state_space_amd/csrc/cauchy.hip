@@ -23,7 +23,8 @@
 // Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
 // with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
 // flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
-// |re|+|im| order) is flagged resonant-correction.
+// |re|+|im| order; rank 2 in the split-precision kernel, which solves by
+// Cramer's rule: det W exactly zero) is flagged resonant-correction.
 #include <float.h>
 
 #include "common.hpp"
@@ -425,6 +426,35 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
     }
 }
 
+// Rank 2 finish by Cramer's rule: with W = I + rho_QP (2 x 2) and
+// v = adj(W) rho_QB, H = (1 + i t)(rho_C~B det W - rho_C~P v) / det W.  The
+// families are f = 3 iu + iv (iu: C~, Q_1, Q_2; iv: B, P_1, P_2).  A non-finite
+// sum takes the same exact re-check as the general finish; det W exactly zero
+// is resonant-correction.
+__device__ __forceinline__ float2 finish_root_r2(float2 (&acc)[9], float st, float tf, int N, size_t hbase,
+                                                 const float2* Lambda, const float2* P, const float2* Q,
+                                                 const float2* Bv, const float2* Ct, int& status) {
+    bool finite = true;
+#pragma unroll
+    for (int f = 0; f < 9; ++f) finite = finite && isfinite(acc[f].x) && isfinite(acc[f].y);
+    if (!finite && !root_recheck<2>(N, hbase, st, Lambda, P, Q, Bv, Ct, acc)) {
+        status = max(status, SSM_ST_RESONANT_DIAGONAL);
+        return c_nan();
+    }
+    const float2 w00 = make_float2(acc[4].x + 1.0f, acc[4].y), w01 = acc[5], w10 = acc[7];
+    const float2 w11 = make_float2(acc[8].x + 1.0f, acc[8].y);
+    const float2 det = c_sub(c_mul(w00, w11), c_mul(w01, w10));
+    if (det.x == 0.0f && det.y == 0.0f) {
+        status = max(status, SSM_ST_RESONANT_CORRECTION);
+        return c_nan();
+    }
+    const float2 r0 = acc[3], r1 = acc[6];
+    const float2 v0 = c_sub(c_mul(w11, r0), c_mul(w01, r1));
+    const float2 v1 = c_sub(c_mul(w00, r1), c_mul(w10, r0));
+    const float2 num = c_sub(c_mul(acc[0], det), c_add(c_mul(acc[1], v0), c_mul(acc[2], v1)));
+    return c_mul(make_float2(1.0f, tf), cdivf(num, det));
+}
+
 // Copy states [n0, n0 + 8 nkb) of a channel's record to LDS: the weight blocks
 // (all loads issued before the stores) and the three header rows.
 __device__ __forceinline__ void h_stage(char* smem, float* hx, const char* rp, int npad, int hdr, int n0, int nkb,
@@ -593,7 +623,10 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
                     const double* const m1 = reinterpret_cast<const double*>(rp + rec.scal + 72);
                     Hk = make_float2((float)(0.5 * dtv * m1[0]), (float)(0.5 * dtv * m1[1]));
                 } else {
-                    Hk = finish_root<RK>(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                    if constexpr (RK == 2)
+                        Hk = finish_root_r2(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                    else
+                        Hk = finish_root<RK>(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
                 }
                 roots[(size_t)h * M + pos] = Hk;
             }
