@@ -106,6 +106,8 @@ def test_root_values_multipass_lengths(L):
     (256, 203, 2, 4096, 4),   # rank 2, 2 roots per thread; 128 + 75 states (padded)
     (8, 301, 1, 3000, 2),     # small grid: 1 root per thread, unroll 8; 256 + 45 states (padded)
     (4, 71, 3, 2048, 2),      # rank 3: 64 + 7 states (padded)
+    (8, 300, 2, 2048, 2),     # rank 2 past one 256-state record chunk: 4 x 64 + 44 states in the sweep
+    (4, 270, 3, 1024, 2),     # rank 3 past one record chunk
     (4, 66, 4, 1500, 2),      # rank 4: 64 + 2 states
 ])
 def test_root_values_chunks_and_roots_per_thread(H, N, r, L, nsample):
