@@ -214,18 +214,19 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 // three v_mfma_f32_32x32x16_f16 per block of 8 states and 32 roots.  The
 // dropped a_l b_l and the roundings of the low parts leave about 2^-21 of each
 // product.
-// Layout of one instruction: A is 32 roots x 16 (k = 2 s + c for the 8 states s
-// of the block and the components c of g = gx + i gy), B is 16 x 32 columns
-// (column 2 f + p: the real and imaginary parts p of family f), C is 32 roots x
-// 32 columns.  Lane l holds row l % 32 and k = 8 (l / 32) + 0..7 of A (four
-// states, both components), column l % 32 and the same k of B, and column
-// l % 32 of rows 8 (v / 4) + 4 (l / 32) + v % 4 of C.  Re(w g) = w.x gx - w.y gy
-// and Im(w g) = w.y gx + w.x gy give the B entries (gx row, gy row): column 2f:
-// (w.x, -w.y), column 2f + 1: (w.y, w.x).
+// Layout of one instruction: A is the weights, 32 columns x 16 (column 2 f + p:
+// the real and imaginary parts p of family f; k = 2 s + c for the 8 states s of
+// the block and the components c of g = gx + i gy), B the Cauchy entries, 16 x
+// 32 roots, and C is 32 columns x 32 roots.  Lane l holds row l % 32 and k =
+// 8 (l / 32) + 0..7 of A (column l % 32's weights of four states), column l % 32
+// and the same k of B (root l % 32's entries of those states, both
+// components), and rows 8 (v / 4) + 4 (l / 32) + v % 4 of C's column l % 32.
+// Re(w g) = w.x gx - w.y gy and Im(w g) = w.y gx + w.x gy give the weight
+// entries (gx, gy): column 2f: (w.x, -w.y), column 2f + 1: (w.y, w.x).
 //
 // The per-channel part (the scales, the split weight blocks in the order the
 // sweep reads them, the state headers and the z = -1 sum) is formed once per
-// channel by a small kernel and copied to LDS by each root tile.
+// channel by a small kernel and copied to LDS by each root workgroup.
 // ---------------------------------------------------------------------------
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef _Float16 h8 __attribute__((ext_vector_type(8)));
@@ -234,17 +235,32 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 constexpr int kHChunk = 64;  // states staged in LDS at a time (8 blocks of 8)
 constexpr int kHBlockBytes = 2048;  // one block of 8 states: [lane half][hi, lo][32 columns] x 16 bytes
 
+// Far roots.  Around the centre c of the channel's poles (their mean) with
+// radius R = max |lambda_n - c|, a root with |s - c| >= 2 R has
+//   rho_f(s) = (1/R) sum_{j >= 0} Mt_{j,f} v^(j+1),  v = R/(s - c),  |v| <= 1/2,
+//   Mt_{j,f} = sum_n w_{f,n} ((lambda_n - c)/R)^j,
+// the expansion of each 1/(s - lambda_n) in powers of (lambda_n - c)/(s - c).
+// Its terms after j = kFarJ - 1 are below 2^-kFarJ of the first, so the sums
+// are the same product as over the states, with kFarJ pseudo-states: moments
+// in place of weights and the powers v^(j+1) in place of the Cauchy entries.
+constexpr int kFarJ = 24;              // terms kept (3 blocks of 8)
+constexpr float kFarRadius2 = 0.25f;   // |v|^2 at most: |s - c| >= 2 R
+
 // One channel's record: the weight blocks (npad / 8 x 2048 bytes), the
 // headers x = -Re lambda, x^2, Im lambda (npad floats each; padding states
-// x = 0, x^2 = 1), then 128 bytes of scales: tau_f (16 floats), X^2 + R^2,
-// and the z = -1 sum C~^* B (float64).
+// x = 0, x^2 = 1), the moment blocks of the far roots (kFarJ / 8 x 2048 bytes),
+// then 256 bytes of scales: tau_f (16 floats), X^2 + R^2 and the z = -1 sum
+// C~^* B (float64), and at 96 the moments' tau_f (16 floats), c (2 floats),
+// R and 1/R (floats); R = 0 (a single pole position, or non-finite poles)
+// turns the far form off.
 struct HRec {
-    int64_t npad, hdr, scal, bytes;
+    int64_t npad, hdr, far, scal, bytes;
     __host__ __device__ explicit HRec(int64_t N) {
         npad = (N + 7) & ~(int64_t)7;
         hdr = npad / 8 * kHBlockBytes;
-        scal = hdr + 3 * npad * 4;
-        bytes = scal + 128;
+        far = hdr + 3 * npad * 4;
+        scal = far + kFarJ / 8 * kHBlockBytes;
+        bytes = scal + 256;
     }
 };
 
@@ -311,7 +327,8 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
 
     // the scales (largest weight component per family, X^2, R^2) and the
     // z = -1 sum (dt/2) C~^* B in float64
-    double m1x = 0.0, m1y = 0.0;
+    double m1x = 0.0, m1y = 0.0, lsx = 0.0, lsy = 0.0;
+    __shared__ double2 lsum[4];
     {
         float tl[F + 2];
 #pragma unroll
@@ -344,6 +361,8 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
             }
             tl[F] = fmaxf(tl[F], lam.x * lam.x);
             tl[F + 1] = fmaxf(tl[F + 1], lam.y * lam.y);
+            lsx += lam.x;
+            lsy += lam.y;
             m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
             m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
 #pragma unroll
@@ -362,12 +381,15 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
             for (int f = 0; f < F + 2; ++f) tl[f] = fmaxf(tl[f], __shfl_xor(tl[f], o, 64));
             m1x += __shfl_xor(m1x, o, 64);
             m1y += __shfl_xor(m1y, o, 64);
+            lsx += __shfl_xor(lsx, o, 64);
+            lsy += __shfl_xor(lsy, o, 64);
         }
         if ((tid & 63) == 0) {
 #pragma unroll
             for (int f = 0; f < F + 2; ++f)
                 if (tl[f] > 0.0f) atomicMax(&mx_bits[f], __float_as_uint(tl[f]));
             red[tid >> 6] = make_double2(m1x, m1y);
+            lsum[tid >> 6] = make_double2(lsx, lsy);
         }
     }
     __syncthreads();
@@ -424,6 +446,129 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
             dst[32] = lo8;
         }
     }
+    // ---- far roots: the poles' centre c and radius R, the moments Mt_{j,f}
+    //      (float64), their scales, and the moment blocks ----
+    __shared__ double rmax[4];
+    __shared__ double2 qp[64][kFarJ];  // powers ((lambda_n - c)/R)^j of 64 states
+    __shared__ double2 mt[kFarJ * F];
+    __shared__ float tauf[F];
+    const double cx = (lsum[0].x + lsum[1].x + lsum[2].x + lsum[3].x) / (double)N;
+    const double cy = (lsum[0].y + lsum[1].y + lsum[2].y + lsum[3].y) / (double)N;
+    auto lam_at = [&](int n) -> float2 {  // state n of the staged chunk n0 (one) or from HBM
+        return one ? sl[n] : Lambda[hbase + n];
+    };
+    {
+        double r2 = 0.0;
+        for (int n = tid; n < N; n += 256) {
+            const float2 lam = lam_at(n);
+            const double dx = (double)lam.x - cx, dy = (double)lam.y - cy;
+            r2 = fmax(r2, dx * dx + dy * dy);
+        }
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) r2 = fmax(r2, __shfl_xor(r2, o, 64));
+        if ((tid & 63) == 0) rmax[tid >> 6] = r2;
+    }
+    __syncthreads();
+    const double R2 = fmax(fmax(rmax[0], rmax[1]), fmax(rmax[2], rmax[3]));
+    double R = sqrt(R2);
+    if (!(R >= 1e-30) || !(R <= 1e30)) R = 0.0;  // a single pole position or non-finite poles: no far form
+    const double iR = R > 0.0 ? 1.0 / R : 0.0;
+    constexpr int NM = kFarJ * F;  // moments, (j, f) = (i / F, i % F), two per thread at most
+    static_assert(NM <= 2 * 256, "two moments per thread");
+    double2 macc[2] = {make_double2(0.0, 0.0), make_double2(0.0, 0.0)};
+    for (int n0 = 0; n0 < N; n0 += 256) {
+        const int nch = min(256, N - n0);
+        if (!one) {
+            __syncthreads();  // the previous chunk's readers are done
+            stage(n0);
+        }
+        for (int sub = 0; sub < nch; sub += 64) {
+            __syncthreads();  // staged states visible; the previous sub-chunk's powers are read
+            if (tid < 64) {
+                const int m = sub + tid;
+                double2 q = make_double2(0.0, 0.0), pw = make_double2(0.0, 0.0);
+                if (m < nch) {
+                    const float2 lam = sl[m];
+                    q = make_double2(((double)lam.x - cx) * iR, ((double)lam.y - cy) * iR);
+                    pw = make_double2(1.0, 0.0);
+                }
+                for (int j = 0; j < kFarJ; ++j) {
+                    qp[tid][j] = pw;
+                    pw = make_double2(pw.x * q.x - pw.y * q.y, pw.x * q.y + pw.y * q.x);
+                }
+            }
+            __syncthreads();
+            const int nsub = min(64, nch - sub);
+#pragma unroll
+            for (int i2 = 0; i2 < 2; ++i2) {
+                const int idx = tid + 256 * i2;
+                if (idx >= NM) continue;
+                const int j = idx / F, f = idx - j * F;
+                const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
+                double2 a = macc[i2];
+                for (int m = 0; m < nsub; ++m) {
+                    const int ml = sub + m;
+                    const float2 uu = iu == 0 ? sc[ml] : sq[ml * RK + iu - 1];
+                    const float2 vv = iv == 0 ? sb[ml] : sp[ml * RK + iv - 1];
+                    const float2 w = c_mul(c_conj(uu), vv);
+                    const double2 q = qp[m][j];
+                    a.x += (double)w.x * q.x - (double)w.y * q.y;
+                    a.y += (double)w.x * q.y + (double)w.y * q.x;
+                }
+                macc[i2] = a;
+            }
+        }
+    }
+#pragma unroll
+    for (int i2 = 0; i2 < 2; ++i2)
+        if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = macc[i2];
+    __syncthreads();
+    if (tid < F) {
+        float tm = 0.0f;
+        for (int j = 0; j < kFarJ; ++j) {
+            const double2 m = mt[j * F + tid];
+            tm = fmaxf(tm, fmaxf(fabsf((float)m.x), fabsf((float)m.y)));
+        }
+        tauf[tid] = tm;
+    }
+    __syncthreads();
+    if (tid < 16) {
+        reinterpret_cast<float*>(out + rec.scal + 96)[tid] = tid < F ? tauf[tid] : 0.0f;
+    } else if (tid == 16) {
+        float* const sf = reinterpret_cast<float*>(out + rec.scal + 160);
+        sf[0] = (float)cx;
+        sf[1] = (float)cy;
+        sf[2] = (float)R;
+        sf[3] = (float)iR;
+    }
+    // moment blocks: the same layout as the weight blocks, pseudo-state j in place of the state
+    for (int it = tid; it < kFarJ / 8 * 64; it += 256) {
+        const int kb = it >> 6, lh = (it >> 5) & 1, col = it & 31, f = col >> 1;
+        float it_f = 0.0f;
+        if (f < F) it_f = tauf[f] > 0.0f ? 1.0f / tauf[f] : 0.0f;
+        h8 hi8, lo8;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = 8 * kb + 4 * lh + q;
+            float2 m = make_float2(0.0f, 0.0f);
+            if (f < F) {
+                const double2 md = mt[j * F + f];
+                m = make_float2((float)md.x * it_f, (float)md.y * it_f);
+            }
+            h2 hi, lo;
+            if (col & 1)
+                split_pair(m.y, m.x, hi, lo);  // column 2f + 1: (m.y, m.x)
+            else
+                split_pair(m.x, -m.y, hi, lo);  // column 2f: (m.x, -m.y)
+            hi8[2 * q] = hi[0];
+            hi8[2 * q + 1] = hi[1];
+            lo8[2 * q] = lo[0];
+            lo8[2 * q + 1] = lo[1];
+        }
+        h8* const dst = reinterpret_cast<h8*>(out + rec.far + (size_t)kb * kHBlockBytes + lh * 1024 + col * 16);
+        dst[0] = hi8;
+        dst[32] = lo8;
+    }
 }
 
 // Rank 2 finish by Cramer's rule: with W = I + rho_QP (2 x 2) and
@@ -453,6 +598,27 @@ __device__ __forceinline__ float2 finish_root_r2(float2 (&acc)[9], float st, flo
     const float2 v1 = c_sub(c_mul(w00, r1), c_mul(w10, r0));
     const float2 num = c_sub(c_mul(acc[0], det), c_add(c_mul(acc[1], v0), c_mul(acc[2], v1)));
     return c_mul(make_float2(1.0f, tf), cdivf(num, det));
+}
+
+// Whether the root s = i st is far from the poles' disc (|s - c| >= 2 R = rf2,
+// false when R = 0), with |s - c| = mx |e|: mx = max(|Re|, |Im|) of s - c and
+// e = conj(s - c)/mx, |e| = ne in [1, sqrt 2] (no overflow in the square).
+struct FarRoot {
+    float ex, ey, ne, mx;
+    bool far;
+};
+__device__ __forceinline__ FarRoot far_root(float st, float cx, float cy, float rf2) {
+    FarRoot r;
+    const float sy = st - cy;
+    r.mx = fmaxf(fabsf(cx), fabsf(sy));
+    const bool big = r.mx >= 0.5f * rf2 && r.mx <= FLT_MAX;
+    const float im = big ? __builtin_amdgcn_rcpf(r.mx) : 0.0f;
+    r.ex = -cx * im;
+    r.ey = -sy * im;
+    r.ne = sqrtf(fmaf(r.ex, r.ex, r.ey * r.ey));
+    const float d = r.mx * r.ne;
+    r.far = big && d >= rf2 && d <= FLT_MAX;
+    return r;
 }
 
 // Copy states [n0, n0 + 8 nkb) of a channel's record to LDS: the weight blocks
@@ -492,8 +658,9 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     // the staged chunk (weight blocks, then the headers), and each wave's C
     // block with a row per root
     __shared__ __align__(16) char smem[kHChunk / 8 * kHBlockBytes + 3 * kHChunk * 4];
-    __shared__ float ctr_s[(kCauchyThreads / 64) * 32 * 33];
+    __shared__ __align__(16) char fsm[kFarJ / 8 * kHBlockBytes];  // the moment blocks
     __shared__ int blk_status;
+    __shared__ int wnear[kCauchyThreads / 64];  // per wave: some root of this tile is near
     float* const hx = reinterpret_cast<float*>(smem + kHChunk / 8 * kHBlockBytes);  // x = -Re lambda
     float* const hx2 = hx + kHChunk;                                               // x^2
     float* const him = hx2 + kHChunk;                                              // Im lambda
@@ -524,11 +691,25 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     const double a = 2.0 / (double)dtv;
     const bool one_chunk = N <= kHChunk;
     if (one_chunk) h_stage(smem, hx, rp, (int)rec.npad, (int)rec.hdr, 0, (N + 7) >> 3, tid);
-    float* const ctr = ctr_s + wv * (32 * 33);
+    {
+        const float4* const src = reinterpret_cast<const float4*>(rp + rec.far);
+        for (int i = tid; i < kFarJ / 8 * kHBlockBytes / 16; i += kCauchyThreads)
+            reinterpret_cast<float4*>(fsm)[i] = src[i];
+    }
+    if (tid == 0) blk_status = 0;
+    __syncthreads();
     const float* const tau = reinterpret_cast<const float*>(rp + rec.scal);  // uniform loads at the finish
+    const float* const tau_far = reinterpret_cast<const float*>(rp + rec.scal + 96);
+    const float* const fc = reinterpret_cast<const float*>(rp + rec.scal + 160);
+    const float cx = fc[0], cy = fc[1], rf = fc[2];
+    const float rf2 = rf > 0.0f ? 2.0f * rf : FLT_MAX * 2.0f;  // far: |s - c| >= 2 R, |v| <= 1/2
 
+    // One chunk of states: staged once, and the waves then run their tiles
+    // without barriers (a wave of far roots goes on to its next tile while the
+    // others sweep the states).  Several chunks: the workgroup stages each in
+    // turn, and skips them when all its waves are far.
+    int my_status = 0;
     for (int tile = t0; tile < t1; ++tile) {
-        if (tid == 0) blk_status = 0;
         // this lane's roots: row l % 32 of the wave's NB blocks (vectors, not
         // arrays: the finish selects an element per lane half)
         typedef float fnb __attribute__((ext_vector_type(NB)));
@@ -541,6 +722,23 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
             tf[nb] = (float)t;
             sig[nb] = sqrtf(fmaf(st[nb], st[nb], xr2));
         }
+        // the far form for the wave when every root it stores is far (the
+        // roots past M and the z = -1 root, which has its own formula, do not vote)
+        bool lane_far = true;
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const int pos = tile * TILE + wv * (32 * NB) + nb * 32 + row;
+            lane_far = lane_far && (far_root(st[nb], cx, cy, rf2).far || pos >= M || pos == pos_m1);
+        }
+        const bool far = __builtin_amdgcn_ballot_w64(!lane_far) == 0;  // uniform over the wave
+        bool any_near = true;
+        if (!one_chunk) {
+            if (lane == 0) wnear[wv] = far ? 0 : 1;
+            __syncthreads();  // also: the previous tile's readers of the staged chunks are done
+            any_near = false;
+#pragma unroll
+            for (int w = 0; w < kCauchyThreads / 64; ++w) any_near = any_near || wnear[w] != 0;
+        }
 
         f16v acc[NB];
 #pragma unroll
@@ -548,13 +746,14 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[nb][v] = 0.0f;
 
-        for (int n0 = 0; n0 < N; n0 += kHChunk) {
+        for (int n0 = 0; any_near && n0 < N; n0 += kHChunk) {
             const int nkb = (min(kHChunk, N - n0) + 7) >> 3;
             if (!one_chunk) {
-                __syncthreads();  // the previous chunk's readers are done
+                if (n0 > 0) __syncthreads();  // the previous chunk's readers are done
                 h_stage(smem, hx, rp, (int)rec.npad, (int)rec.hdr, n0, nkb, tid);
+                __syncthreads();
             }
-            __syncthreads();
+            if (far) continue;
             const h8* const bsh = reinterpret_cast<const h8*>(smem) + lh * 64 + row;
             for (int kb = 0; kb < nkb; ++kb) {
                 const float4 x4 = *reinterpret_cast<const float4*>(&hx[8 * kb + 4 * lh]);
@@ -582,60 +781,126 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
                 // independent accumulators back to back
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[nb], bh, acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh, ah[nb], acc[nb], 0, 0, 0);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[nb], bl, acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bl, ah[nb], acc[nb], 0, 0, 0);
 #pragma unroll
                 for (int nb = 0; nb < NB; ++nb)
-                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[nb], bh, acc[nb], 0, 0, 0);
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh, al[nb], acc[nb], 0, 0, 0);
             }
         }
-
-        // C through LDS to one root per lane (lanes 0-31 and 32-63 take the
-        // rows of alternate blocks), unscaled, then the Woodbury finish
-        int my_status = 0;
+        if (far) {
+            // A entries u v^j, u = v/|v| = conj(s - c)/|s - c|, for j = 8 kb +
+            // 4 (l / 32) + 0..3: the sums are Mt-products times tau_f/|s - c|
+            f2v vv[NB], pw[NB];
 #pragma unroll
-        for (int nb2 = 0; nb2 < NB; nb2 += 2) {
-            float2 sums[F];
-#pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
-                if (row < NC) {
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) ctr[(8 * (v >> 2) + 4 * lh + (v & 3)) * 33 + row] = acc[nb2 + hb][v];
-                }
-                lds_sync<true>();
-                if (lh == hb) {
-                    const float us = rcp_safe(sig[nb2 + hb]);
-#pragma unroll
-                    for (int f = 0; f < F; ++f)
-                        sums[f] = make_float2(ctr[row * 33 + 2 * f] * (tau[f] * us),
-                                              ctr[row * 33 + 2 * f + 1] * (tau[f] * us));
-                }
-                lds_sync<true>();
+            for (int nb = 0; nb < NB; ++nb) {
+                // roots that are not far (past M, z = -1) take zero entries
+                const FarRoot fr = far_root(st[nb], cx, cy, rf2);
+                const bool ok = fr.far;
+                const float dst = fr.mx * fr.ne;
+                const float sc = ok ? __builtin_amdgcn_rcpf(fr.ne) : 0.0f;
+                const f2v u = {fr.ex * sc, fr.ey * sc};  // conj(s - c)/|s - c|
+                vv[nb] = u * (ok ? rf * __builtin_amdgcn_rcpf(dst) : 0.0f);
+                sig[nb] = ok ? dst : 1.0f;  // |s - c|
+                pw[nb] = u;
             }
-            const float stv = lh ? st[nb2 + 1] : st[nb2];
-            const float tfv = lh ? tf[nb2 + 1] : tf[nb2];
-            const int pos = tile * TILE + wv * (32 * NB) + (nb2 + lh) * 32 + row;
+            f2v v4[NB];
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) {
+                const f2v v2 = {vv[nb].x * vv[nb].x - vv[nb].y * vv[nb].y, 2.0f * vv[nb].x * vv[nb].y};
+                v4[nb] = (f2v){v2.x * v2.x - v2.y * v2.y, 2.0f * v2.x * v2.y};
+                if (lh) pw[nb] = (f2v){pw[nb].x * v4[nb].x - pw[nb].y * v4[nb].y,
+                                       pw[nb].x * v4[nb].y + pw[nb].y * v4[nb].x};
+            }
+            const h8* const fsh = reinterpret_cast<const h8*>(fsm) + lh * 64 + row;
+#pragma unroll
+            for (int kb = 0; kb < kFarJ / 8; ++kb) {
+                const h8 bh = fsh[kb * 128];
+                const h8 bl = fsh[kb * 128 + 32];
+                h8 ah[NB], al[NB];
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        h2 hi, lo;
+                        split_pair(pw[nb].x, pw[nb].y, hi, lo);
+                        ah[nb][2 * q] = hi[0];
+                        ah[nb][2 * q + 1] = hi[1];
+                        al[nb][2 * q] = lo[0];
+                        al[nb][2 * q + 1] = lo[1];
+                        pw[nb] = (f2v){pw[nb].x * vv[nb].x - pw[nb].y * vv[nb].y,
+                                       pw[nb].x * vv[nb].y + pw[nb].y * vv[nb].x};
+                    }
+                    // past the other lane half's four terms
+                    pw[nb] = (f2v){pw[nb].x * v4[nb].x - pw[nb].y * v4[nb].y,
+                                   pw[nb].x * v4[nb].y + pw[nb].y * v4[nb].x};
+                }
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh, ah[nb], acc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bl, ah[nb], acc[nb], 0, 0, 0);
+#pragma unroll
+                for (int nb = 0; nb < NB; ++nb)
+                    acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bh, al[nb], acc[nb], 0, 0, 0);
+            }
+        }
+        const float* const tsel = far ? tau_far : tau;
+
+        // C has a row per column 2f + p and a column per root (the weights are
+        // the instruction's A operand): lane l holds root l % 32 of its block in
+        // rows 8 (v/4) + 4 (l/32) + v % 4.  One swap of lane halves gives each
+        // lane all rows of one root, that of block l / 32: rows 8 (v/4) + v % 4
+        // in lo_rows, 8 (v/4) + 4 + v % 4 in hi_rows.
+        static_assert(NB == 2, "one root per lane at the finish");
+        f16v lo_rows, hi_rows;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(acc[0][v]), __float_as_uint(acc[1][v]),
+                                                             false, false);
+            lo_rows[v] = __uint_as_float(sw[0]);
+            hi_rows[v] = __uint_as_float(sw[1]);
+        }
+        {
+            float2 sums[F];
+            const float us = rcp_safe(lh ? sig[1] : sig[0]);
+#pragma unroll
+            for (int f = 0; f < F; ++f) {
+                const float ts = tsel[f] * us;
+                const int r0 = 2 * f, r1 = 2 * f + 1;
+                const float c0 = ((r0 >> 2) & 1) ? hi_rows[4 * (r0 >> 3) + (r0 & 3)] : lo_rows[4 * (r0 >> 3) + (r0 & 3)];
+                const float c1 = ((r1 >> 2) & 1) ? hi_rows[4 * (r1 >> 3) + (r1 & 3)] : lo_rows[4 * (r1 >> 3) + (r1 & 3)];
+                sums[f] = make_float2(c0 * ts, c1 * ts);
+            }
+            const float stv = lh ? st[1] : st[0];
+            const float tfv = lh ? tf[1] : tf[0];
+            const int pos = tile * TILE + wv * (32 * NB) + lh * 32 + row;
             if (pos < M) {
                 float2 Hk;
                 if (pos == pos_m1) {
                     const double* const m1 = reinterpret_cast<const double*>(rp + rec.scal + 72);
                     Hk = make_float2((float)(0.5 * dtv * m1[0]), (float)(0.5 * dtv * m1[1]));
                 } else {
+                    int st_root = 0;
                     if constexpr (RK == 2)
-                        Hk = finish_root_r2(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                        Hk = finish_root_r2(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, st_root);
                     else
-                        Hk = finish_root<RK>(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, my_status);
+                        Hk = finish_root<RK>(sums, stv, tfv, N, hbase, Lambda, P, Q, Bv, Ct, st_root);
+                    my_status = max(my_status, st_root);
                 }
                 roots[(size_t)h * M + pos] = Hk;
             }
         }
-        __syncthreads();  // blk_status reset is visible
-        if (my_status) atomicMax(&blk_status, my_status);
-        __syncthreads();
-        if (tid == 0) tile_status[(size_t)h * tiles + tile] = blk_status;
     }
+    // the workgroup's status in its first tile's entry (the readers take the
+    // largest over a channel's entries), zero in the others
+    __syncthreads();
+    if (my_status) atomicMax(&blk_status, my_status);
+    __syncthreads();
+    if (tid < t1 - t0) tile_status[(size_t)h * tiles + t0 + tid] = tid == 0 ? blk_status : 0;
 }
 
 template <int RK, int RPT>

@@ -74,11 +74,13 @@ def test_workspace_sizes():
     assert ws % 256 == 0
     assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
     # ranks 2 and 3 add one record per channel for the split-precision root
-    # values: N/8 weight blocks of 2048 bytes, 3 N floats of state headers and
-    # 128 bytes of scales (the tile count is the same as rank 1's here)
+    # values: N/8 weight blocks of 2048 bytes, 3 N floats of state headers, the
+    # far roots' 3 moment blocks of 2048 bytes and 256 bytes of scales (the tile
+    # count is the same as rank 1's here)
+    rec = 64 * 256 + 3 * 64 * 4 + 3 * 2048 + 256
     for r in (2, 3):
-        assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, r, 1024) - ws == H * (64 * 256 + 3 * 64 * 4 + 128)
-    assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 61, 2, 1024) - ws == H * (64 * 256 + 3 * 64 * 4 + 128)
+        assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, r, 1024) - ws == H * rec
+    assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 61, 2, 1024) - ws == H * rec
     assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, 4, 1024) == ws
     # fftconv for 1024 <= M <= 16384: spectra [H,2,M] c64, the table [M] c64 and the
     # wave-structured transforms' table [2M] c64 (sizes multiples of 256 here)
