@@ -240,11 +240,13 @@ constexpr int kHBlockBytes = 2048;  // one block of 8 states: [lane half][hi, lo
 //   rho_f(s) = (1/R) sum_{j >= 0} Mt_{j,f} v^(j+1),  v = R/(s - c),  |v| <= 1/2,
 //   Mt_{j,f} = sum_n w_{f,n} ((lambda_n - c)/R)^j,
 // the expansion of each 1/(s - lambda_n) in powers of (lambda_n - c)/(s - c).
-// Its terms after j = kFarJ - 1 are below 2^-kFarJ of the first, so the sums
-// are the same product as over the states, with kFarJ pseudo-states: moments
-// in place of weights and the powers v^(j+1) in place of the Cauchy entries.
-constexpr int kFarJ = 24;              // terms kept (3 blocks of 8)
-constexpr float kFarRadius2 = 0.25f;   // |v|^2 at most: |s - c| >= 2 R
+// The sums are then the same product as over the states, with pseudo-states j:
+// moments in place of weights and the powers v^(j+1) in place of the Cauchy
+// entries.  A wave keeps J = 8, 16 or 24 terms (1 to 3 blocks), the fewest with
+// |v|^J <= 2^-24 for all its roots (|v| <= 1/8, 2^-1.5, 1/2): the dropped tail
+// is below 2^-24 (1 + |v|)/(1 - |v|) <= 3 2^-24 of the sum of |terms|.
+constexpr int kFarJ = 24;                        // terms at most (3 blocks of 8)
+constexpr float kFarTwoBlockRatio = 2.8284271f;  // |s - c|/R at least for 16 terms
 
 // One channel's record: the weight blocks (npad / 8 x 2048 bytes), the
 // headers x = -Re lambda, x^2, Im lambda (npad floats each; padding states
@@ -724,13 +726,22 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
         }
         // the far form for the wave when every root it stores is far (the
         // roots past M and the z = -1 root, which has its own formula, do not vote)
-        bool lane_far = true;
+        // and the terms it keeps: 8 nfb with |v|^(8 nfb) <= 2^-24 for all its roots
+        bool lane_far = true, lane_v2 = false, lane_v3 = false;
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int pos = tile * TILE + wv * (32 * NB) + nb * 32 + row;
-            lane_far = lane_far && (far_root(st[nb], cx, cy, rf2).far || pos >= M || pos == pos_m1);
+            const FarRoot fr = far_root(st[nb], cx, cy, rf2);
+            const bool skip = pos >= M || pos == pos_m1;
+            lane_far = lane_far && (fr.far || skip);
+            const float d = fr.mx * fr.ne;  // |s - c|
+            lane_v2 = lane_v2 || (!skip && !(d >= 8.0f * rf));                // |v| > 1/8
+            lane_v3 = lane_v3 || (!skip && !(d >= kFarTwoBlockRatio * rf));  // |v| > 2^-1.5
         }
         const bool far = __builtin_amdgcn_ballot_w64(!lane_far) == 0;  // uniform over the wave
+        const int nfb = __builtin_amdgcn_ballot_w64(lane_v3) != 0   ? 3
+                        : __builtin_amdgcn_ballot_w64(lane_v2) != 0 ? 2
+                                                                    : 1;
         bool any_near = true;
         if (!one_chunk) {
             if (lane == 0) wnear[wv] = far ? 0 : 1;
@@ -816,7 +827,7 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
             }
             const h8* const fsh = reinterpret_cast<const h8*>(fsm) + lh * 64 + row;
 #pragma unroll
-            for (int kb = 0; kb < kFarJ / 8; ++kb) {
+            for (int kb = 0; kb < nfb; ++kb) {
                 const h8 bh = fsh[kb * 128];
                 const h8 bl = fsh[kb * 128 + 32];
                 h8 ah[NB], al[NB];
