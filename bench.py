@@ -24,6 +24,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -74,6 +76,54 @@ def algorithmic(w, M, fused):
         del out["spectrum"]
         out["conv"]["work"] = 8 * B * H * L + 8 * H * M + 4 * H
     return out
+
+
+def wave_freq(logm, pos):
+    """Frequency index held at each output position of the wave-structured
+    transforms' scrambled order (M = 2^logm >= 1024; M = P 16384 in slices)."""
+    lq = min(logm, 14)
+    q = pos & ((1 << lq) - 1)
+    logw = lq - 10
+    sb = 4 - logw
+    wave, e, lane = q >> 10, (q >> 6) & 15, q & 63
+    rb = ((lane >> 4) & 3) | (((lane >> 2) & 3) << 2)
+    k = ((rb & ((1 << sb) - 1)) | (wave << sb)) + 16 * ((rb >> sb) + (1 << logw) * ((lane & 3) + 4 * e))
+    return k if logm <= 14 else (k << (logm - 14)) + (pos >> 14)
+
+
+def root_value_terms(p, M, scrambled):
+    """Terms the rank-2/3 root-value kernel sums per launch, by its own rule: a
+    wave of 64 consecutive output positions whose roots s = i a tan(pi k/M) all
+    lie at |s - c| >= 2 R from the channel's pole centre c (R the pole radius)
+    sums J = 8, 16 or 24 moment terms per root (the fewest with |v|^J <= 2^-24,
+    v = R/(s - c)); any other wave sums the N states.  Returns (terms over the
+    M - 1 roots != -1, fraction of those roots in far waves)."""
+    pos = np.arange(M)
+    k = wave_freq(int(math.log2(M)), pos) if scrambled else pos
+    t = np.tan(np.pi * k / M)
+    t[2 * k == M] = 0.0
+    pos_m1 = 512 if scrambled else M // 2
+    counted = np.ones(M, dtype=bool)
+    counted[pos_m1] = False
+    pad = (-M) % 64
+    terms, far_roots = 0, 0
+    for h in range(p.H):
+        lam = p.Lambda[h].astype(np.complex128)
+        c = lam.mean()
+        R = float(np.sqrt(np.max((lam.real - c.real) ** 2 + (lam.imag - c.imag) ** 2)))
+        if not (1e-30 <= R <= 1e30):
+            R = 0.0
+        cx, cy, rf = np.float32(c.real), np.float32(c.imag), np.float32(R)
+        st = (2.0 / float(np.float32(p.dt[h])) * t).astype(np.float32)
+        d = np.hypot(cx, (st - cy).astype(np.float32)).astype(np.float32)
+        far = (rf > 0) & (d >= 2 * rf)
+        lv = np.where(d >= 8 * rf, 1, np.where(d >= np.float32(2.8284271) * rf, 2, 3))
+        far = np.concatenate([far | ~counted, np.ones(pad, bool)]).reshape(-1, 64).all(1)
+        lv = np.concatenate([np.where(counted, lv, 0), np.zeros(pad, int)]).reshape(-1, 64).max(1)
+        cnt = np.concatenate([counted, np.zeros(pad, bool)]).reshape(-1, 64).sum(1)
+        terms += int(np.sum(np.where(far, 8 * lv, p.N) * cnt))
+        far_roots += int(np.sum(cnt[far]))
+    return terms, far_roots / (p.H * (M - 1))
 
 
 def read_traffic(kernel, workload):
@@ -569,6 +619,16 @@ def main():
         phase_ms["spectrum"] -= phase_ms["cauchy"] * (reps - 1) / reps
 
     alg = algorithmic(w, M, fused)
+    far_info = None
+    if form != 1 and w.r in (2, 3):
+        # the rank-2/3 kernel sums moment expansions for far waves: its
+        # algorithmic flops are the same per-term figure over the terms it sums
+        scrambled = M > 16384 or (not fused and M >= 1024)
+        terms, far_frac = root_value_terms(p, M, scrambled)
+        direct = alg["cauchy"]["work"]
+        alg["cauchy"]["work"] = terms * (8 * (w.r + 1) ** 2 + 7)
+        far_info = {"work_direct_sum": direct, "terms_per_root": terms / (w.H * (M - 1)),
+                    "far_root_fraction": far_frac}
     if form == 1:
         # the single launch is compute-bound (root-value sums on the matrix cores,
         # transforms on the vector ALU): rated on the root values' flops plus the
@@ -589,11 +649,16 @@ def main():
         phases["conv"]["transform_flops_per_launch"] = conv_flops
         phases["conv"]["transform_tflops"] = tf
         phases["conv"]["transform_frac_fp32"] = tf / PEAK_FP32_TFLOPS
+    if far_info is not None and "cauchy" in phases:
+        phases["cauchy"].update(far_info)
+        phases["cauchy"]["direct_sum_equivalent_tflops"] = far_info["work_direct_sum"] * 1e-12 / (
+            phase_ms["cauchy"] * 1e-3)
     if "cauchy" in phases and w.r in (2, 3):
         # the split-precision kernel's matrix-core side: three float16 products
-        # of 32 x 32 x 16 per block of 8 states and 32 roots (32 columns, of
-        # which 2 (r+1)^2 are used), against the dense float16 peak
-        mf = 3 * 2 * 32 * 32 * 16 * w.H * M * ((w.N + 7) // 8) / 32
+        # of 32 x 32 x 16 per block of 8 states (or moment terms) and 32 roots
+        # (32 columns, of which 2 (r+1)^2 are used), against the dense float16 peak
+        blocks = far_info["terms_per_root"] / 8 if far_info is not None else (w.N + 7) // 8
+        mf = 3 * 2 * 32 * 32 * 16 * w.H * M * blocks / 32
         phases["cauchy"]["matrix_core_flops_per_launch"] = mf
         phases["cauchy"]["matrix_core_frac_fp16"] = mf * 1e-12 / (phase_ms["cauchy"] * 1e-3) / PEAK_FP16_TFLOPS
     dom = max(names, key=lambda k: phase_ms[k])
