@@ -431,6 +431,50 @@ def test_split_precision_root_values_hard_cases(r, L):
         assert_rows_close(y[:, h, :], r_["y"], what=f"y h{h}")
 
 
+@pytest.mark.parametrize("order,r,kind,N", [
+    ("reversed", 2, "s4", 64), ("shuffled", 2, "s4", 64), ("shuffled", 3, "random", 64),
+    ("shuffled", 2, "s4", 40), ("asis", 3, "s4", 57),
+])
+def test_far_field_root_values(order, r, kind, N):
+    """Ranks 2 and 3 where many waves of roots take the far-field moment form
+    (the sum over the states replaced by 8 to 24 moment terms).  Poles given in
+    reversed or shuffled order, steps across [1e-3, 1e-1], N with a ragged last
+    block.  Root values
+    (natural order) and the forward path's kernel (the transforms' order)
+    against the oracle.  With the S4 poles at a tenth of the path tolerance:
+    the expansions' tails are below 3 2^-24 of the sums of |terms|, so an error
+    in a moment, a power or a scale shows here.  The random poles (Re down to
+    -0.1) have resonance peaks where rounding s = i a t to float32 alone moves
+    the value by ~4e-5 of the row's largest (with or without the far forms):
+    those take the path tolerance."""
+    ssm = _ssm()
+    H, L, Bsz = 8, 16384, 2
+    p = I.random_params(7000 + 10 * r + N, H, N, r, L, lambda_kind=kind)
+    if order != "asis":
+        perm = np.arange(N)[::-1] if order == "reversed" else np.random.default_rng(r + N).permutation(N)
+        p.Lambda, p.P, p.Q = p.Lambda[:, perm].copy(), p.P[:, perm].copy(), p.Q[:, perm].copy()
+        p.B, p.C = p.B[:, perm].copy(), p.C[:, perm].copy()
+    d = _dev(p)
+    out = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_kernel=True,
+                         want_roots=True)
+    assert np.all(_np(out["status"]) == 0)
+    roots = _np(out["roots"])
+    ref = []
+    for h in range(H):
+        c = p.channel(h)
+        Hk, st = O.root_values(c["Lambda"], c["P"], c["Q"], c["B"], c["C"], c["dt"], L)
+        assert st == O.OK
+        ref.append(Hk)
+    ref = np.array(ref)
+    tol = TOL / 10 if kind == "s4" else TOL
+    assert_rows_close(roots, ref, tol=tol, what="root values")
+    u = I.random_input(L + N, Bsz, H, L)
+    fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"],
+                     torch.from_numpy(u).to(DEV), want_kernel=True)
+    assert np.all(_np(fw["status"]) == 0)
+    assert_rows_close(_np(fw["K"]), np.fft.ifft(ref, axis=1)[:, :L], tol=tol, what="forward kernel")
+
+
 # ---------------------------------------------------------------------------
 # edge cases: ragged and tiny lengths, odd batch, any N and r, unordered poles
 # ---------------------------------------------------------------------------
