@@ -453,6 +453,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
     __shared__ double rmax[4];
     __shared__ double2 qp[64][kFarJ];  // powers ((lambda_n - c)/R)^j of 64 states
     __shared__ double2 mt[kFarJ * F];
+    __shared__ float2 wsub[64 * F];    // the weights of 64 states
     __shared__ float tauf[F];
     const double cx = (lsum[0].x + lsum[1].x + lsum[2].x + lsum[3].x) / (double)N;
     const double cy = (lsum[0].y + lsum[1].y + lsum[2].y + lsum[3].y) / (double)N;
@@ -485,12 +486,12 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
             stage(n0);
         }
         for (int sub = 0; sub < nch; sub += 64) {
-            __syncthreads();  // staged states visible; the previous sub-chunk's powers are read
+            __syncthreads();  // staged states visible; the previous sub-chunk's powers and weights are read
+            const int nsub = min(64, nch - sub);
             if (tid < 64) {
-                const int m = sub + tid;
                 double2 q = make_double2(0.0, 0.0), pw = make_double2(0.0, 0.0);
-                if (m < nch) {
-                    const float2 lam = sl[m];
+                if (tid < nsub) {
+                    const float2 lam = sl[sub + tid];
                     q = make_double2(((double)lam.x - cx) * iR, ((double)lam.y - cy) * iR);
                     pw = make_double2(1.0, 0.0);
                 }
@@ -499,25 +500,37 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
                     pw = make_double2(pw.x * q.x - pw.y * q.y, pw.x * q.y + pw.y * q.x);
                 }
             }
+            // the weights of the sub-chunk's states (zero past it)
+            for (int i = tid; i < 64 * F; i += 256) {
+                const int m = i / F, f = i - m * F;
+                const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
+                float2 w = make_float2(0.0f, 0.0f);
+                if (m < nsub) {
+                    const int ml = sub + m;
+                    const float2 uu = iu == 0 ? sc[ml] : sq[ml * RK + iu - 1];
+                    const float2 vv = iv == 0 ? sb[ml] : sp[ml * RK + iv - 1];
+                    w = c_mul(c_conj(uu), vv);
+                }
+                wsub[i] = w;
+            }
             __syncthreads();
-            const int nsub = min(64, nch - sub);
 #pragma unroll
             for (int i2 = 0; i2 < 2; ++i2) {
                 const int idx = tid + 256 * i2;
                 if (idx >= NM) continue;
                 const int j = idx / F, f = idx - j * F;
-                const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
-                double2 a = macc[i2];
-                for (int m = 0; m < nsub; ++m) {
-                    const int ml = sub + m;
-                    const float2 uu = iu == 0 ? sc[ml] : sq[ml * RK + iu - 1];
-                    const float2 vv = iv == 0 ? sb[ml] : sp[ml * RK + iv - 1];
-                    const float2 w = c_mul(c_conj(uu), vv);
-                    const double2 q = qp[m][j];
-                    a.x += (double)w.x * q.x - (double)w.y * q.y;
-                    a.y += (double)w.x * q.y + (double)w.y * q.x;
+                // two partial sums (even and odd states) to halve the FMA chain
+                double2 a = macc[i2], b = make_double2(0.0, 0.0);
+#pragma unroll 16
+                for (int m = 0; m < 64; m += 2) {
+                    const float2 w0 = wsub[m * F + f], w1 = wsub[(m + 1) * F + f];
+                    const double2 q0 = qp[m][j], q1 = qp[m + 1][j];
+                    a.x += (double)w0.x * q0.x - (double)w0.y * q0.y;
+                    a.y += (double)w0.x * q0.y + (double)w0.y * q0.x;
+                    b.x += (double)w1.x * q1.x - (double)w1.y * q1.y;
+                    b.y += (double)w1.x * q1.y + (double)w1.y * q1.x;
                 }
-                macc[i2] = a;
+                macc[i2] = make_double2(a.x + b.x, a.y + b.y);
             }
         }
     }
@@ -617,7 +630,7 @@ __device__ __forceinline__ FarRoot far_root(float st, float cx, float cy, float 
     const float im = big ? __builtin_amdgcn_rcpf(r.mx) : 0.0f;
     r.ex = -cx * im;
     r.ey = -sy * im;
-    r.ne = sqrtf(fmaf(r.ex, r.ex, r.ey * r.ey));
+    r.ne = __builtin_amdgcn_sqrtf(fmaf(r.ex, r.ex, r.ey * r.ey));  // in [1, 2]: the hardware square root
     const float d = r.mx * r.ne;
     r.far = big && d >= rf2 && d <= FLT_MAX;
     return r;
@@ -722,7 +735,9 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
             const double t = pos < M ? tant[pos] : 0.0;
             st[nb] = (float)(a * t);
             tf[nb] = (float)t;
-            sig[nb] = sqrtf(fmaf(st[nb], st[nb], xr2));
+            // any sigma of the right size serves (the same value scales and
+            // unscales); the floor keeps the hardware square root off subnormals
+            sig[nb] = __builtin_amdgcn_sqrtf(fmaxf(fmaf(st[nb], st[nb], xr2), 1e-30f));
         }
         // the far form for the wave when every root it stores is far (the
         // roots past M and the z = -1 root, which has its own formula, do not vote)
