@@ -448,10 +448,10 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
             dst[32] = lo8;
         }
     }
-    // ---- far roots: the poles' centre c and radius R, the moments Mt_{j,f}
-    //      (float64), their scales, and the moment blocks ----
+    // ---- far roots: the poles' centre c and radius R (float64), the moments
+    //      Mt_{j,f}, their scales, and the moment blocks ----
     __shared__ double rmax[4];
-    __shared__ double2 qp[64][kFarJ];  // powers ((lambda_n - c)/R)^j of 64 states
+    __shared__ float2 qp[64][kFarJ];   // powers ((lambda_n - c)/R)^j of 64 states (formed in float64)
     __shared__ double2 mt[kFarJ * F];
     __shared__ float2 wsub[64 * F];    // the weights of 64 states
     __shared__ float tauf[F];
@@ -478,7 +478,9 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
     const double iR = R > 0.0 ? 1.0 / R : 0.0;
     constexpr int NM = kFarJ * F;  // moments, (j, f) = (i / F, i % F), two per thread at most
     static_assert(NM <= 2 * 256, "two moments per thread");
-    double2 macc[2] = {make_double2(0.0, 0.0), make_double2(0.0, 0.0)};
+    // The sums in float32: the moment blocks keep about 22 bits (float16 high
+    // and low parts), which a 64-term float32 sum of these products matches.
+    float2 macc[2] = {make_float2(0.0f, 0.0f), make_float2(0.0f, 0.0f)};
     for (int n0 = 0; n0 < N; n0 += 256) {
         const int nch = min(256, N - n0);
         if (!one) {
@@ -496,7 +498,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
                     pw = make_double2(1.0, 0.0);
                 }
                 for (int j = 0; j < kFarJ; ++j) {
-                    qp[tid][j] = pw;
+                    qp[tid][j] = make_float2((float)pw.x, (float)pw.y);
                     pw = make_double2(pw.x * q.x - pw.y * q.y, pw.x * q.y + pw.y * q.x);
                 }
             }
@@ -520,23 +522,23 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2*
                 if (idx >= NM) continue;
                 const int j = idx / F, f = idx - j * F;
                 // two partial sums (even and odd states) to halve the FMA chain
-                double2 a = macc[i2], b = make_double2(0.0, 0.0);
+                float2 a = macc[i2], b = make_float2(0.0f, 0.0f);
 #pragma unroll 16
                 for (int m = 0; m < 64; m += 2) {
                     const float2 w0 = wsub[m * F + f], w1 = wsub[(m + 1) * F + f];
-                    const double2 q0 = qp[m][j], q1 = qp[m + 1][j];
-                    a.x += (double)w0.x * q0.x - (double)w0.y * q0.y;
-                    a.y += (double)w0.x * q0.y + (double)w0.y * q0.x;
-                    b.x += (double)w1.x * q1.x - (double)w1.y * q1.y;
-                    b.y += (double)w1.x * q1.y + (double)w1.y * q1.x;
+                    const float2 q0 = qp[m][j], q1 = qp[m + 1][j];
+                    a.x = fmaf(w0.x, q0.x, fmaf(-w0.y, q0.y, a.x));
+                    a.y = fmaf(w0.x, q0.y, fmaf(w0.y, q0.x, a.y));
+                    b.x = fmaf(w1.x, q1.x, fmaf(-w1.y, q1.y, b.x));
+                    b.y = fmaf(w1.x, q1.y, fmaf(w1.y, q1.x, b.y));
                 }
-                macc[i2] = make_double2(a.x + b.x, a.y + b.y);
+                macc[i2] = make_float2(a.x + b.x, a.y + b.y);
             }
         }
     }
 #pragma unroll
     for (int i2 = 0; i2 < 2; ++i2)
-        if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = macc[i2];
+        if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = make_double2(macc[i2].x, macc[i2].y);
     __syncthreads();
     if (tid < F) {
         float tm = 0.0f;
