@@ -103,6 +103,8 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
 // One workgroup (T = M/16 threads) per pair of batch rows (b, b+1) of one
 // channel.  The input pair is read once and kept in registers for both halves;
 // the cyclic half's result is kept in registers while the twisted half runs.
+// At its register limit: the transforms load each stage's table entries right
+// before the stage.
 template <int LOGM>
 __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4))) void wconv_kernel(
     int Bsz, int H, int L, int npb, int64_t npairs, int remap_bpc, const float* __restrict__ u,
@@ -149,19 +151,19 @@ __global__ __launch_bounds__(WGeo<LOGM>::T) __attribute__((amdgpu_waves_per_eu(4
     // half A: twist psi
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = z[e];
-    wf_forward<LOGM, 1>(v, lds, tw4, t);
+    wf_forward<LOGM, 1, false>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], buf_ld_c64(rk, vk, e * 64 * sizeof(float2)));
-    wf_inverse<LOGM, 1>(v, lds, tw4, t);
+    wf_inverse<LOGM, 1, false>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) out[e] = v[e];
     // half B: twist psi^3, spectrum S_B = conj(S_A) at the complemented position
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = z[e];
-    wf_forward<LOGM, 3>(v, lds, tw4, t);
+    wf_forward<LOGM, 3, false>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], c_conj(buf_ld_c64(rk, vkm, (15 - e) * 64 * sizeof(float2))));
-    wf_inverse<LOGM, 3>(v, lds, tw4, t);
+    wf_inverse<LOGM, 3, false>(v, lds, tw4, t);
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
         if (t + T * e < L) {

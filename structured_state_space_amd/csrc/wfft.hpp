@@ -119,14 +119,38 @@ __device__ __forceinline__ void power_after(float2& p, const float2& used) {
 
 // ---- stage A: DFT_16 over the register index, twiddle exp(-2 pi i t k/M)
 //      (TW: exp(-2 pi i t (TW + 4k)/(4M)), the per-register constant first) ----
+// The four table entries a transform's stage twiddles start from.  PRE
+// transforms load them together when they start, so that only the first
+// stage's wait is exposed; the others load each right before its stage (fewer
+// registers held, for kernels at their register limit).
+struct WTw {
+    float2 a;   // exp(-2 pi i t/M)
+    float2 u;   // exp(-2 pi i t/(4M)) (twisted transforms)
+    float2 b;   // exp(-2 pi i lane/T), T = 64 W = 4M/64
+    float2 c1;  // exp(-2 pi i (lane mod 16)/64), 4M/64 = 64 W
+};
+template <int LOGM, int TW>
+__device__ __forceinline__ void wf_tw_load_a(WTw& w, const float2* __restrict__ tab, int t) {
+    w.a = tab[4 * t];
+    w.u = TW != 0 ? tab[t] : make_float2(1.0f, 0.0f);
+}
+template <int LOGM>
+__device__ __forceinline__ void wf_tw_load_b(WTw& w, const float2* __restrict__ tab, int lane) {
+    w.b = WGeo<LOGM>::W > 1 ? tab[lane * 64] : make_float2(1.0f, 0.0f);
+}
+template <int LOGM>
+__device__ __forceinline__ void wf_tw_load_c1(WTw& w, const float2* __restrict__ tab, int lane) {
+    w.c1 = tab[(lane & 15) * 64 * WGeo<LOGM>::W];
+}
+
 template <int LOGM, int TW, bool INV>
-__device__ __forceinline__ void wf_twiddle_a(float2 (&v)[16], const float2* __restrict__ tab, int t) {
-    float2 step = tab[4 * t];  // exp(-2 pi i t/M)
+__device__ __forceinline__ void wf_twiddle_a(float2 (&v)[16], const WTw& tw) {
+    float2 step = tw.a;
     if (INV) step.y = -step.y;
     // keep the powers per call (not hoisted and kept live across stages)
     asm volatile("" : "+v"(step.x), "+v"(step.y));
     if constexpr (TW != 0) {
-        float2 u = tab[t];  // exp(-2 pi i t/(4M))
+        float2 u = tw.u;
         if (INV) u.y = -u.y;
         float2 p = TW == 1 ? u : c_mul(c_mul(u, u), u);
 #pragma unroll
@@ -166,9 +190,9 @@ __device__ __forceinline__ void wf_dft_waves(float2 (&v)[16]) {
 }
 
 template <int LOGM, bool INV>
-__device__ __forceinline__ void wf_twiddle_b(float2 (&v)[16], const float2* __restrict__ tab, int lane) {
+__device__ __forceinline__ void wf_twiddle_b(float2 (&v)[16], const WTw& tw) {
     using G = WGeo<LOGM>;
-    float2 base = tab[lane * 64];  // exp(-2 pi i lane/T), T = 64 W = 4M/64
+    float2 base = tw.b;
     if (INV) base.y = -base.y;
     asm volatile("" : "+v"(base.x), "+v"(base.y));
     float2 p = base;
@@ -220,9 +244,8 @@ __device__ __forceinline__ void wf_dft4_groups(float2 (&v)[16]) {
 }
 
 template <int LOGM, bool INV>
-__device__ __forceinline__ void wf_twiddle_c1(float2 (&v)[16], const float2* __restrict__ tab, int lane) {
-    using G = WGeo<LOGM>;
-    float2 base = tab[(lane & 15) * 64 * G::W];  // exp(-2 pi i (lane mod 16)/64), 4M/64 = 64 W
+__device__ __forceinline__ void wf_twiddle_c1(float2 (&v)[16], const WTw& tw) {
+    float2 base = tw.c1;
     if (INV) base.y = -base.y;
     asm volatile("" : "+v"(base.x), "+v"(base.y));
     const float2 b2 = c_mul(base, base), b3 = c_mul(b2, base);
@@ -288,44 +311,62 @@ __device__ __forceinline__ void exchange_waves(float2 (&v)[16], float2* __restri
 // Forward transform (see the header comment).  lds: WGeo::LDS complex, shared by the
 // T = 64 W threads of the transform (threadIdx.x < T), every one of which
 // must call it.  t = threadIdx.x.
-template <int LOGM, int TW>
+template <int LOGM, int TW, bool PRE = true>
 __device__ __forceinline__ void wf_forward(float2 (&v)[16], float2* __restrict__ lds, const float2* __restrict__ tab,
                                            int t) {
     using G = WGeo<LOGM>;
     const int lane = t & 63, wv = t >> 6;
+    WTw tw;
+    if constexpr (PRE) {
+        wf_tw_load_a<LOGM, TW>(tw, tab, t);
+        wf_tw_load_b<LOGM>(tw, tab, lane);
+        wf_tw_load_c1<LOGM>(tw, tab, lane);
+    }
     if constexpr (TW != 0) pretwist64<TW, false>(v);
     dft_reg<16, false>(v);
-    wf_twiddle_a<LOGM, TW, false>(v, tab, t);
+    if constexpr (!PRE) wf_tw_load_a<LOGM, TW>(tw, tab, t);
+    wf_twiddle_a<LOGM, TW, false>(v, tw);
     if constexpr (G::W > 1) {
         exchange_waves<LOGM, false>(v, lds, lane, wv);
         wf_dft_waves<LOGM, false>(v);
-        wf_twiddle_b<LOGM, false>(v, tab, lane);
+        if constexpr (!PRE) wf_tw_load_b<LOGM>(tw, tab, lane);
+        wf_twiddle_b<LOGM, false>(v, tw);
     }
     swap_bits_lane45(v);
     wf_dft4_groups<false>(v);
-    wf_twiddle_c1<LOGM, false>(v, tab, lane);
+    if constexpr (!PRE) wf_tw_load_c1<LOGM>(tw, tab, lane);
+    wf_twiddle_c1<LOGM, false>(v, tw);
     swap_bits_lane0123<false>(v, lds + kSlice * wv, lane);
     dft_reg<16, false>(v);
 }
 
 // The exact mirror of wf_forward with conjugate constants: from the scrambled
 // order back to natural order, unscaled (M x the inverse transform).
-template <int LOGM, int TW>
+template <int LOGM, int TW, bool PRE = true>
 __device__ __forceinline__ void wf_inverse(float2 (&v)[16], float2* __restrict__ lds, const float2* __restrict__ tab,
                                            int t) {
     using G = WGeo<LOGM>;
     const int lane = t & 63, wv = t >> 6;
+    WTw tw;
+    if constexpr (PRE) {
+        wf_tw_load_c1<LOGM>(tw, tab, lane);
+        wf_tw_load_b<LOGM>(tw, tab, lane);
+        wf_tw_load_a<LOGM, TW>(tw, tab, t);
+    }
     dft_reg<16, true>(v);
     swap_bits_lane0123<true>(v, lds + kSlice * wv, lane);
-    wf_twiddle_c1<LOGM, true>(v, tab, lane);
+    if constexpr (!PRE) wf_tw_load_c1<LOGM>(tw, tab, lane);
+    wf_twiddle_c1<LOGM, true>(v, tw);
     wf_dft4_groups<true>(v);
     swap_bits_lane45(v);
     if constexpr (G::W > 1) {
-        wf_twiddle_b<LOGM, true>(v, tab, lane);
+        if constexpr (!PRE) wf_tw_load_b<LOGM>(tw, tab, lane);
+        wf_twiddle_b<LOGM, true>(v, tw);
         wf_dft_waves<LOGM, true>(v);
         exchange_waves<LOGM, true>(v, lds, lane, wv);
     }
-    wf_twiddle_a<LOGM, TW, true>(v, tab, t);
+    if constexpr (!PRE) wf_tw_load_a<LOGM, TW>(tw, tab, t);
+    wf_twiddle_a<LOGM, TW, true>(v, tw);
     dft_reg<16, true>(v);
     if constexpr (TW != 0) pretwist64<TW, true>(v);
 }
