@@ -54,6 +54,12 @@ def source_hash(kernel):
     return h.hexdigest()[:16]
 
 
+def split_kernel(N, r, M):
+    """Whether the root values run the split-precision kernel with its far form
+    (the library's own rule: ranks 2 and 3; rank 1 from 128 states and 4096 roots)."""
+    return r in (2, 3) or (r == 1 and N >= 128 and M >= 4096)
+
+
 def algorithmic(w, M, fused):
     """Per-launch algorithmic work of each kernel (definitions in the design notes).
     fused: the kernel transform runs inside the convolution, which then reads
@@ -61,11 +67,12 @@ def algorithmic(w, M, fused):
     H, N, r, L, B = w.H, w.N, w.r, w.L, w.Bsz
     roots = M - 1 if M >= 2 else M                      # z = -1 takes its finite formula
     out = {
-        # ranks 2 and 3 run the split-precision kernel, bound by the vector ALU
-        # (forming and splitting the Cauchy entries); rank 1 and 4 the float32
-        # matrix-core kernel.  Both rated on the same algorithmic flops against
-        # 157.3 TFLOP/s (the FP32 vector and FP32 dense matrix peaks coincide).
-        "cauchy": dict(bound="alu" if r in (2, 3) else "mfma", unit="TFLOP/s",
+        # the split-precision kernel (split_kernel) is bound by the vector ALU
+        # (forming and splitting the Cauchy entries); the other rank-1 and the
+        # rank-4 shapes run the float32 matrix-core kernel.  Both rated on the
+        # same per-term flops against 157.3 TFLOP/s (the FP32 vector and FP32
+        # dense matrix peaks coincide).
+        "cauchy": dict(bound="alu" if split_kernel(N, r, M) else "mfma", unit="TFLOP/s",
                        work=H * roots * N * (8 * (r + 1) ** 2 + 7), scale=1e-12, peak=PEAK_FP32_TFLOPS),
         # the root values read, one spectrum of M complex written per channel
         "spectrum": dict(bound="hbm", unit="GB/s", work=H * M * 8 + H * M * 8, scale=1e-9, peak=PEAK_HBM_GBS),
@@ -620,7 +627,7 @@ def main():
 
     alg = algorithmic(w, M, fused)
     far_info = None
-    if form != 1 and w.r in (2, 3):
+    if form != 1 and split_kernel(w.N, w.r, M):
         # the rank-2/3 kernel sums moment expansions for far waves: its
         # algorithmic flops are the same per-term figure over the terms it sums
         scrambled = M > 16384 or (not fused and M >= 1024)
@@ -653,7 +660,7 @@ def main():
         phases["cauchy"].update(far_info)
         phases["cauchy"]["direct_sum_equivalent_tflops"] = far_info["work_direct_sum"] * 1e-12 / (
             phase_ms["cauchy"] * 1e-3)
-    if "cauchy" in phases and w.r in (2, 3):
+    if "cauchy" in phases and split_kernel(w.N, w.r, M):
         # the split-precision kernel's matrix-core side: three float16 products
         # of 32 x 32 x 16 per block of 8 states (or moment terms) and 32 roots
         # (32 columns, of which 2 (r+1)^2 are used), against the dense float16 peak

@@ -9,8 +9,8 @@
 #include "common.hpp"
 
 namespace ssm {
-int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M);
-int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r);
+int64_t cauchy_tiles(int64_t H, int64_t N, int64_t r, int64_t M);
+int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
@@ -112,13 +112,13 @@ WsLayout layout(int op, int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L)
         w.roots_bytes = (size_t)H * M * sizeof(float2);
         off = align256(off + w.roots_bytes);
         w.tstat = off;
-        w.tstat_bytes = (size_t)H * cauchy_tiles(H, r, M) * sizeof(int32_t);
+        w.tstat_bytes = (size_t)H * cauchy_tiles(H, N, r, M) * sizeof(int32_t);
         off = align256(off + w.tstat_bytes);
         w.tant = off;
         w.tant_bytes = (size_t)M * sizeof(double);
         off = align256(off + w.tant_bytes);
         w.cprep = off;
-        w.cprep_bytes = (size_t)cauchy_prep_bytes(H, N, r);
+        w.cprep_bytes = (size_t)cauchy_prep_bytes(H, N, r, M);
         off = align256(off + w.cprep_bytes);
     }
     if (op == SSM_OP_FFTCONV || fwd) {
@@ -289,10 +289,10 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     if (e != hipSuccess) return SSM_ERR_DEVICE;
     if (K || status) {  // kernel transform only: no spectra
         if (M > ((int64_t)1 << kMaxLdsLogM))
-            e = launch_spectrum_large(true, H, L, M, cauchy_tiles(H, r, M), roots, (float2*)(base + w.big), tstat,
+            e = launch_spectrum_large(true, H, L, M, cauchy_tiles(H, N, r, M), roots, (float2*)(base + w.big), tstat,
                                       nullptr, 1, nullptr, (float2*)K, status, nullptr, twtab, s);
         else
-            e = launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
+            e = launch_spectrum(true, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, nullptr, 1, nullptr, (float2*)K,
                                 status, nullptr, twtab, s);
         if (e != hipSuccess) return SSM_ERR_DEVICE;
     }
@@ -406,18 +406,18 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
                               (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s,
                               scrambled);
         if (e != hipSuccess) break;
-        e = large  ? launch_spectrum_wl(H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out, status,
+        e = large  ? launch_spectrum_wl(H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, D, (float2*)K_out, status,
                                         khat, (float2*)(base + w.tw4), s)
-            : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
+            : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, nullptr, 1, D,
                                       (float2*)K_out, status, khat, (float2*)(base + w.tw4), s)
-                   : launch_spectrum(true, H, L, M, cauchy_tiles(H, r, M), roots, tstat, nullptr, 1, D,
+                   : launch_spectrum(true, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, nullptr, 1, D,
                                      (float2*)K_out, status, khat, twtab, s);
     }
     if (e != hipSuccess || mark(2) != hipSuccess) return SSM_ERR_DEVICE;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = large   ? launch_wl_conv(Bsz, H, L, M, u, y, khat, (float2*)(base + w.big), (const float2*)(base + w.tw4),
                                      (const float2*)(base + w.tw4) + 2 * ((int64_t)1 << kMaxLdsLogM), s)
-            : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, r, M), roots, tstat, D, (float2*)K_out,
+            : fused ? launch_conv_fused(Bsz, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, D, (float2*)K_out,
                                         status, u, y, twtab, s)
             : wave  ? launch_wconv(Bsz, H, L, M, u, y, khat, (const float2*)(base + w.tw4), s)
                     : launch_conv(Bsz, H, L, M, u, y, khat, twtab, s);
@@ -470,7 +470,7 @@ int ssm_forward_complex(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L,
     float2* twtab = (float2*)(base + w.tw);
     float2* K = K_out ? (float2*)K_out : (float2*)(base + w.kbuf);
     const bool large = M > ((int64_t)1 << kMaxLdsLogM);
-    const int64_t tiles = cauchy_tiles(H, r, M);
+    const int64_t tiles = cauchy_tiles(H, N, r, M);
     hipError_t e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q,
                                  (const float2*)B, (const float2*)Ctilde, dt, roots, tstat, twtab,
                                  (double*)(base + w.tant), base + w.cprep, s, false);

@@ -39,9 +39,8 @@ namespace {
 // each output position (0 at k = M/2, which takes the finite z = -1 formula;
 // scr_logm > 0: positions in the wave-structured transforms' order, else
 // natural order) and exp(-i pi j/M) for the later transforms.
-__global__ __launch_bounds__(256) void root_tables_kernel(int M, int scr_logm, double* __restrict__ tant,
-                                                          float2* __restrict__ twtab) {
-    const int j = blockIdx.x * 256 + threadIdx.x;
+__device__ __forceinline__ void root_tables_at(int j, int M, int scr_logm, double* __restrict__ tant,
+                                               float2* __restrict__ twtab) {
     if (j >= M) return;
     double sn, cs;
     sincospi((double)j / (double)M, &sn, &cs);
@@ -49,6 +48,10 @@ __global__ __launch_bounds__(256) void root_tables_kernel(int M, int scr_logm, d
     const int k = scr_logm > 0 ? wf_freq_rt(scr_logm, j) : j;
     if (k != j) sincospi((double)k / (double)M, &sn, &cs);
     tant[j] = (2 * k == M) ? 0.0 : sn / cs;
+}
+__global__ __launch_bounds__(256) void root_tables_kernel(int M, int scr_logm, double* __restrict__ tant,
+                                                          float2* __restrict__ twtab) {
+    root_tables_at(blockIdx.x * 256 + threadIdx.x, M, scr_logm, tant, twtab);
 }
 
 template <int RK, int RPT>
@@ -276,10 +279,17 @@ __device__ __forceinline__ void split_pair(float a, float b, h2& hi, h2& lo) {
 }
 
 template <int RK>
-__global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int N, const float2* __restrict__ Lambda,
+// Workgroups H.. of the same grid write the per-call root tables.
+__global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const float2* __restrict__ Lambda,
                                                             const float2* __restrict__ P, const float2* __restrict__ Q,
                                                             const float2* __restrict__ Bv,
-                                                            const float2* __restrict__ Ct, char* __restrict__ prep) {
+                                                            const float2* __restrict__ Ct, char* __restrict__ prep,
+                                                            int M, int scr_logm, double* __restrict__ tant,
+                                                            float2* __restrict__ twtab) {
+    if ((int)blockIdx.x >= H) {  // uniform over the workgroup
+        root_tables_at(((int)blockIdx.x - H) * 256 + (int)threadIdx.x, M, scr_logm, tant, twtab);
+        return;
+    }
     constexpr int F = Fam<RK>::F;
     const HRec rec(N);
     const int h = blockIdx.x, tid = threadIdx.x;
@@ -935,11 +945,9 @@ template <int RK, int RPT>
 hipError_t launch_h(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
                     const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                     int32_t* tstat, float2* twtab, double* tant, char* prep, hipStream_t stream) {
-    hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M, scr_logm,
-                       tant, twtab);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL((cauchy_h_prep_kernel<RK>), dim3((unsigned)H), dim3(256), 0, stream, (int)N, Lambda, P, Q, Bv,
-                       Ct, prep);
+    // the per-channel records and (workgroups H..) the root tables in one launch
+    hipLaunchKernelGGL((cauchy_h_prep_kernel<RK>), dim3((unsigned)(H + (M + 255) / 256)), dim3(256), 0, stream,
+                       (int)H, (int)N, Lambda, P, Q, Bv, Ct, prep, (int)M, scr_logm, tant, twtab);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
     // tiles per workgroup: up to 4 while the grid keeps 8192 workgroups (the
@@ -977,22 +985,29 @@ hipError_t launch_rk(int64_t H, int64_t N, int64_t M, int scr_logm, const float2
 // measured fastest, the accumulators of more roots crowd out waves), one for
 // the split-precision kernel of ranks 2 and 3 (64 roots per wave, four waves
 // per SIMD), while the grid keeps at least 1024 workgroups
-int cauchy_rpt(int64_t H, int64_t r, int64_t M) {
-    const int max_rpt = r == 1 ? 4 : 1;
+// The split-precision kernel (matrix cores in float16 parts, with the far
+// form for roots far from the poles) takes ranks 2 and 3, and rank 1 from 128
+// states and 4096 roots: with 64 states the float32 kernel's sweep is cheaper
+// (measured at 512 channels x 4096 roots: 67 against 78 us), with 256 the far
+// form's savings win (256 channels x 65536 roots: 948 against 1478 us).
+bool cauchy_split(int64_t N, int64_t r, int64_t M) { return r == 2 || r == 3 || (r == 1 && N >= 128 && M >= 4096); }
+
+int cauchy_rpt(int64_t H, int64_t N, int64_t r, int64_t M) {
+    const int max_rpt = r == 1 && !cauchy_split(N, r, M) ? 4 : 1;
     int rpt = max_rpt;
     while (rpt > 1 && H * ((M + (int64_t)kCauchyThreads * rpt - 1) / ((int64_t)kCauchyThreads * rpt)) < 1024)
         rpt >>= 1;
     return rpt;
 }
 
-int64_t cauchy_tiles(int64_t H, int64_t r, int64_t M) {
-    const int64_t per = (int64_t)kCauchyThreads * cauchy_rpt(H, r, M);
+int64_t cauchy_tiles(int64_t H, int64_t N, int64_t r, int64_t M) {
+    const int64_t per = (int64_t)kCauchyThreads * cauchy_rpt(H, N, r, M);
     return (M + per - 1) / per;
 }
 
-// per-channel records of the split-precision path (ranks 2 and 3), else none
-int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r) {
-    return (r == 2 || r == 3) ? H * HRec(N).bytes : 0;
+// per-channel records of the split-precision path, else none
+int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r, int64_t M) {
+    return cauchy_split(N, r, M) ? H * HRec(N).bytes : 0;
 }
 
 // scrambled: store the root values in the order the wave-structured
@@ -1001,19 +1016,20 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
                          bool scrambled) {
-    const int rpt = cauchy_rpt(H, r, M);
+    const int rpt = cauchy_rpt(H, N, r, M);
+    const bool split = cauchy_split(N, r, M);
     const int scr_logm = scrambled ? ilog2_exact(M) : 0;
     if (scrambled && M < 1024) return hipErrorInvalidValue;
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
-    if (r == RK && rpt == RPT)                                                                                \
+    if (!split && r == RK && rpt == RPT)                                                                      \
         return launch_rk<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, \
                                   stream);
 #define SSM_CAUCHY_H(RK, RPT)                                                                                  \
-    if (r == RK && rpt == RPT)                                                                                 \
+    if (split && r == RK && rpt == RPT)                                                                        \
         return launch_h<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant,  \
                                  (char*)prep, stream);
     SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1)
-    SSM_CAUCHY_H(2, 1) SSM_CAUCHY_H(3, 1)
+    SSM_CAUCHY_H(1, 1) SSM_CAUCHY_H(2, 1) SSM_CAUCHY_H(3, 1)
     SSM_CAUCHY(4, 1)
 #undef SSM_CAUCHY
 #undef SSM_CAUCHY_H
