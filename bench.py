@@ -101,10 +101,10 @@ def wave_freq(logm, pos):
 def root_value_terms(p, M, scrambled):
     """Terms the rank-2/3 root-value kernel sums per launch, by its own rule: a
     wave of 64 consecutive output positions whose roots s = i a tan(pi k/M) all
-    lie at |s - c| >= 2 R from the channel's pole centre c (R the pole radius)
-    sums J = 8, 16 or 24 moment terms per root (the fewest with |v|^J <= 2^-24,
-    v = R/(s - c)); any other wave sums the N states.  Returns (terms over the
-    M - 1 roots != -1, fraction of those roots in far waves)."""
+    lie at |s - c| >= 2^0.6 R from the channel's pole centre c (R the pole radius)
+    sums J = 8 nfb moment terms per root, nfb = 1..5 (the fewest with
+    |v|^J <= 2^-24, v = R/(s - c)); any other wave sums the N states.  Returns
+    (terms over the M - 1 roots != -1, fraction of those roots in far waves)."""
     pos = np.arange(M)
     k = wave_freq(int(math.log2(M)), pos) if scrambled else pos
     t = np.tan(np.pi * k / M)
@@ -123,8 +123,9 @@ def root_value_terms(p, M, scrambled):
         cx, cy, rf = np.float32(c.real), np.float32(c.imag), np.float32(R)
         st = (2.0 / float(np.float32(p.dt[h])) * t).astype(np.float32)
         d = np.hypot(cx, (st - cy).astype(np.float32)).astype(np.float32)
-        far = (rf > 0) & (d >= 2 * rf)
-        lv = np.where(d >= 8 * rf, 1, np.where(d >= np.float32(2.8284271) * rf, 2, 3))
+        ratios = np.float32([8.0, 2.8284271, 2.0, 1.6817928, 1.5157166])  # 2^(3/nfb)
+        far = (rf > 0) & (d >= ratios[-1] * rf)
+        lv = 1 + sum((~(d >= q * rf)).astype(int) for q in ratios[:-1])
         far = np.concatenate([far | ~counted, np.ones(pad, bool)]).reshape(-1, 64).all(1)
         lv = np.concatenate([np.where(counted, lv, 0), np.zeros(pad, int)]).reshape(-1, 64).max(1)
         cnt = np.concatenate([counted, np.zeros(pad, bool)]).reshape(-1, 64).sum(1)

@@ -239,17 +239,18 @@ constexpr int kHChunk = 64;  // states staged in LDS at a time (8 blocks of 8)
 constexpr int kHBlockBytes = 2048;  // one block of 8 states: [lane half][hi, lo][32 columns] x 16 bytes
 
 // Far roots.  Around the centre c of the channel's poles (their mean) with
-// radius R = max |lambda_n - c|, a root with |s - c| >= 2 R has
-//   rho_f(s) = (1/R) sum_{j >= 0} Mt_{j,f} v^(j+1),  v = R/(s - c),  |v| <= 1/2,
+// radius R = max |lambda_n - c|, a root with |s - c| > R has
+//   rho_f(s) = (1/R) sum_{j >= 0} Mt_{j,f} v^(j+1),  v = R/(s - c),  |v| < 1,
 //   Mt_{j,f} = sum_n w_{f,n} ((lambda_n - c)/R)^j,
 // the expansion of each 1/(s - lambda_n) in powers of (lambda_n - c)/(s - c).
 // The sums are then the same product as over the states, with pseudo-states j:
 // moments in place of weights and the powers v^(j+1) in place of the Cauchy
-// entries.  A wave keeps J = 8, 16 or 24 terms (1 to 3 blocks), the fewest with
-// |v|^J <= 2^-24 for all its roots (|v| <= 1/8, 2^-1.5, 1/2): the dropped tail
-// is below 2^-24 (1 + |v|)/(1 - |v|) <= 3 2^-24 of the sum of |terms|.
-constexpr int kFarJ = 24;                        // terms at most (3 blocks of 8)
-constexpr float kFarTwoBlockRatio = 2.8284271f;  // |s - c|/R at least for 16 terms
+// entries.  A wave keeps J = 8 nfb terms (nfb = 1..5 blocks), the fewest with
+// |v|^J <= 2^-24 for all its roots (|v| <= 2^(-3/nfb): 1/8 to 0.66, i.e.
+// |s - c| >= kFarRatio[nfb - 1] R): the dropped tail is below
+// 2^-24 (1 + |v|)/(1 - |v|) <= 5 2^-24 of the sum of |terms|.
+constexpr int kFarJ = 40;  // terms at most (5 blocks of 8)
+constexpr float kFarRatio[kFarJ / 8] = {8.0f, 2.8284271f, 2.0f, 1.6817928f, 1.5157166f};  // 2^(3/nfb)
 
 // One channel's record: the weight blocks (npad / 8 x 2048 bytes), the
 // headers x = -Re lambda, x^2, Im lambda (npad floats each; padding states
@@ -486,11 +487,14 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
     double R = sqrt(R2);
     if (!(R >= 1e-30) || !(R <= 1e30)) R = 0.0;  // a single pole position or non-finite poles: no far form
     const double iR = R > 0.0 ? 1.0 / R : 0.0;
-    constexpr int NM = kFarJ * F;  // moments, (j, f) = (i / F, i % F), two per thread at most
-    static_assert(NM <= 2 * 256, "two moments per thread");
+    constexpr int NM = kFarJ * F;  // moments, (j, f) = (i / F, i % F), three per thread at most
+    constexpr int NMT = (NM + 255) / 256;
+    static_assert(NMT <= 3, "three moments per thread");
     // The sums in float32: the moment blocks keep about 22 bits (float16 high
     // and low parts), which a 64-term float32 sum of these products matches.
-    float2 macc[2] = {make_float2(0.0f, 0.0f), make_float2(0.0f, 0.0f)};
+    float2 macc[NMT];
+#pragma unroll
+    for (int i2 = 0; i2 < NMT; ++i2) macc[i2] = make_float2(0.0f, 0.0f);
     for (int n0 = 0; n0 < N; n0 += 256) {
         const int nch = min(256, N - n0);
         if (!one) {
@@ -527,13 +531,13 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
             }
             __syncthreads();
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2) {
+            for (int i2 = 0; i2 < NMT; ++i2) {
                 const int idx = tid + 256 * i2;
                 if (idx >= NM) continue;
                 const int j = idx / F, f = idx - j * F;
                 // two partial sums (even and odd states) to halve the FMA chain
                 float2 a = macc[i2], b = make_float2(0.0f, 0.0f);
-#pragma unroll 16
+#pragma unroll 4
                 for (int m = 0; m < 64; m += 2) {
                     const float2 w0 = wsub[m * F + f], w1 = wsub[(m + 1) * F + f];
                     const float2 q0 = qp[m][j], q1 = qp[m + 1][j];
@@ -547,7 +551,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
         }
     }
 #pragma unroll
-    for (int i2 = 0; i2 < 2; ++i2)
+    for (int i2 = 0; i2 < NMT; ++i2)
         if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = make_double2(macc[i2].x, macc[i2].y);
     __syncthreads();
     if (tid < F) {
@@ -627,7 +631,7 @@ __device__ __forceinline__ float2 finish_root_r2(float2 (&acc)[9], float st, flo
     return c_mul(make_float2(1.0f, tf), cdivf(num, det));
 }
 
-// Whether the root s = i st is far from the poles' disc (|s - c| >= 2 R = rf2,
+// Whether the root s = i st is far from the poles' disc (|s - c| >= rf2 > 0,
 // false when R = 0), with |s - c| = mx |e|: mx = max(|Re|, |Im|) of s - c and
 // e = conj(s - c)/mx, |e| = ne in [1, sqrt 2] (no overflow in the square).
 struct FarRoot {
@@ -729,7 +733,7 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     const float* const tau_far = reinterpret_cast<const float*>(rp + rec.scal + 96);
     const float* const fc = reinterpret_cast<const float*>(rp + rec.scal + 160);
     const float cx = fc[0], cy = fc[1], rf = fc[2];
-    const float rf2 = rf > 0.0f ? 2.0f * rf : FLT_MAX * 2.0f;  // far: |s - c| >= 2 R, |v| <= 1/2
+    const float rf2 = rf > 0.0f ? kFarRatio[kFarJ / 8 - 1] * rf : FLT_MAX * 2.0f;  // far: |v| <= 2^(-3/5)
 
     // One chunk of states: staged once, and the waves then run their tiles
     // without barriers (a wave of far roots goes on to its next tile while the
@@ -754,7 +758,8 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
         // the far form for the wave when every root it stores is far (the
         // roots past M and the z = -1 root, which has its own formula, do not vote)
         // and the terms it keeps: 8 nfb with |v|^(8 nfb) <= 2^-24 for all its roots
-        bool lane_far = true, lane_v2 = false, lane_v3 = false;
+        bool lane_far = true;
+        bool lane_more[kFarJ / 8 - 1] = {};  // some root needs more than 8 (j + 1) terms
 #pragma unroll
         for (int nb = 0; nb < NB; ++nb) {
             const int pos = tile * TILE + wv * (32 * NB) + nb * 32 + row;
@@ -762,13 +767,13 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
             const bool skip = pos >= M || pos == pos_m1;
             lane_far = lane_far && (fr.far || skip);
             const float d = fr.mx * fr.ne;  // |s - c|
-            lane_v2 = lane_v2 || (!skip && !(d >= 8.0f * rf));                // |v| > 1/8
-            lane_v3 = lane_v3 || (!skip && !(d >= kFarTwoBlockRatio * rf));  // |v| > 2^-1.5
+#pragma unroll
+            for (int j = 0; j < kFarJ / 8 - 1; ++j) lane_more[j] = lane_more[j] || (!skip && !(d >= kFarRatio[j] * rf));
         }
         const bool far = __builtin_amdgcn_ballot_w64(!lane_far) == 0;  // uniform over the wave
-        const int nfb = __builtin_amdgcn_ballot_w64(lane_v3) != 0   ? 3
-                        : __builtin_amdgcn_ballot_w64(lane_v2) != 0 ? 2
-                                                                    : 1;
+        int nfb = 1;
+#pragma unroll
+        for (int j = 0; j < kFarJ / 8 - 1; ++j) nfb += __builtin_amdgcn_ballot_w64(lane_more[j]) != 0 ? 1 : 0;
         bool any_near = true;
         if (!one_chunk) {
             if (lane == 0) wnear[wv] = far ? 0 : 1;

@@ -75,9 +75,9 @@ def test_workspace_sizes():
     assert ssm.workspace_bytes(ssm.OP_DISCRETIZE, 1, H, 64, 1, 1024) == 0
     # ranks 2 and 3 add one record per channel for the split-precision root
     # values: N/8 weight blocks of 2048 bytes, 3 N floats of state headers, the
-    # far roots' 3 moment blocks of 2048 bytes and 256 bytes of scales (the tile
+    # far roots' 5 moment blocks of 2048 bytes and 256 bytes of scales (the tile
     # count is the same as rank 1's here)
-    rec = 64 * 256 + 3 * 64 * 4 + 3 * 2048 + 256
+    rec = 64 * 256 + 3 * 64 * 4 + 5 * 2048 + 256
     for r in (2, 3):
         assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 64, r, 1024) - ws == H * rec
     assert ssm.workspace_bytes(ssm.OP_FORWARD, 8, H, 61, 2, 1024) - ws == H * rec
