@@ -14,7 +14,7 @@ int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r, int64_t M);
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
-                         bool scrambled);
+                         bool scrambled, float2* tw4 = nullptr, bool* tw4_done = nullptr);
 hipError_t launch_spectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                            const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
                            float2* K_out, int32_t* status, float2* khat, float2* twtab, hipStream_t stream);
@@ -39,7 +39,8 @@ hipError_t launch_spectrum_large(bool from_roots, int64_t H, int64_t L, int64_t 
 bool wave_path_fits(int64_t M);
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream);
+                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream,
+                            bool tw4_ready = false);
 hipError_t launch_wconv(int64_t Bsz, int64_t H, int64_t L, int64_t M, const float* u, float* y, const float2* khat,
                         const float2* tw4, hipStream_t stream);
 hipError_t launch_wl_spectrum(int64_t H, int64_t L, int64_t M, int64_t tiles, float2* roots, const int32_t* tstat,
@@ -394,9 +395,13 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
     const bool wave = !large && !fused && wave_path_fits(M);
     // the wave-structured transforms take the root values in their own order
     const bool scrambled = large || wave;
+    // on the wave-structured path the root-value launch also writes the
+    // transforms' table when it can (one launch fewer)
+    bool tw4_done = false;
     for (int i = 0; i < repeat && e == hipSuccess; ++i)
         e = launch_cauchy(H, N, r, M, (const float2*)Lambda, (const float2*)P, (const float2*)Q, (const float2*)B,
-                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s, scrambled);
+                          (const float2*)Ctilde, dt, roots, tstat, twtab, (double*)(base + w.tant), base + w.cprep, s,
+                          scrambled, wave ? (float2*)(base + w.tw4) : nullptr, &tw4_done);
     if (e != hipSuccess || mark(1) != hipSuccess) return SSM_ERR_DEVICE;
     // the multi-pass kernel transform works in place on the root values, so a
     // repeated stage first regenerates them (the repeat count is a timing aid)
@@ -409,7 +414,7 @@ int forward_impl(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const 
         e = large  ? launch_spectrum_wl(H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, D, (float2*)K_out, status,
                                         khat, (float2*)(base + w.tw4), s)
             : wave ? launch_wspectrum(true, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, nullptr, 1, D,
-                                      (float2*)K_out, status, khat, (float2*)(base + w.tw4), s)
+                                      (float2*)K_out, status, khat, (float2*)(base + w.tw4), s, tw4_done)
                    : launch_spectrum(true, H, L, M, cauchy_tiles(H, N, r, M), roots, tstat, nullptr, 1, D,
                                      (float2*)K_out, status, khat, twtab, s);
     }

@@ -280,15 +280,27 @@ __device__ __forceinline__ void split_pair(float a, float b, h2& hi, h2& lo) {
 }
 
 template <int RK>
-// Workgroups H.. of the same grid write the per-call root tables.
+// Workgroups H.. of the same grid write the per-call root tables, and after
+// them (tw4 given) the wave-structured transforms' table
+// tw4[j] = exp(-i pi j/(2M)), j < 2M.
 __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const float2* __restrict__ Lambda,
                                                             const float2* __restrict__ P, const float2* __restrict__ Q,
                                                             const float2* __restrict__ Bv,
                                                             const float2* __restrict__ Ct, char* __restrict__ prep,
                                                             int M, int scr_logm, double* __restrict__ tant,
-                                                            float2* __restrict__ twtab) {
+                                                            float2* __restrict__ twtab, float2* __restrict__ tw4) {
     if ((int)blockIdx.x >= H) {  // uniform over the workgroup
-        root_tables_at(((int)blockIdx.x - H) * 256 + (int)threadIdx.x, M, scr_logm, tant, twtab);
+        const int b = (int)blockIdx.x - H, ntab = (M + 255) / 256;
+        if (b < ntab) {
+            root_tables_at(b * 256 + (int)threadIdx.x, M, scr_logm, tant, twtab);
+        } else {
+            const int j = (b - ntab) * 256 + (int)threadIdx.x;
+            if (j < 2 * M) {
+                double sn, cs;
+                sincospi((double)j / (double)(2 * M), &sn, &cs);
+                tw4[j] = make_float2((float)cs, (float)-sn);
+            }
+        }
         return;
     }
     constexpr int F = Fam<RK>::F;
@@ -949,10 +961,12 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
 template <int RK, int RPT>
 hipError_t launch_h(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
                     const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                    int32_t* tstat, float2* twtab, double* tant, char* prep, hipStream_t stream) {
-    // the per-channel records and (workgroups H..) the root tables in one launch
-    hipLaunchKernelGGL((cauchy_h_prep_kernel<RK>), dim3((unsigned)(H + (M + 255) / 256)), dim3(256), 0, stream,
-                       (int)H, (int)N, Lambda, P, Q, Bv, Ct, prep, (int)M, scr_logm, tant, twtab);
+                    int32_t* tstat, float2* twtab, double* tant, char* prep, float2* tw4, hipStream_t stream) {
+    // the per-channel records, the root tables and (tw4 given) the transforms'
+    // table in one launch
+    const int64_t blocks0 = H + (M + 255) / 256 + (tw4 ? (2 * M + 255) / 256 : 0);
+    hipLaunchKernelGGL((cauchy_h_prep_kernel<RK>), dim3((unsigned)blocks0), dim3(256), 0, stream, (int)H, (int)N,
+                       Lambda, P, Q, Bv, Ct, prep, (int)M, scr_logm, tant, twtab, tw4);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
     // tiles per workgroup: up to 4 while the grid keeps 8192 workgroups (the
@@ -1016,11 +1030,14 @@ int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r, int64_t M) {
 }
 
 // scrambled: store the root values in the order the wave-structured
-// transforms take them (M >= 1024), not in natural order
+// transforms take them (M >= 1024), not in natural order.  tw4 (nullable): the
+// wave-structured transforms' table of 2M entries, written here when the
+// split-precision kernel runs (*tw4_done tells whether it was).
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
-                         bool scrambled) {
+                         bool scrambled, float2* tw4, bool* tw4_done) {
+    if (tw4_done) *tw4_done = false;
     const int rpt = cauchy_rpt(H, N, r, M);
     const bool split = cauchy_split(N, r, M);
     const int scr_logm = scrambled ? ilog2_exact(M) : 0;
@@ -1031,8 +1048,11 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
                                   stream);
 #define SSM_CAUCHY_H(RK, RPT)                                                                                  \
     if (split && r == RK && rpt == RPT)                                                                        \
+    {                                                                                                          \
+        if (tw4_done) *tw4_done = tw4 != nullptr;                                                              \
         return launch_h<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant,  \
-                                 (char*)prep, stream);
+                                 (char*)prep, tw4, stream);                                                    \
+    }
     SSM_CAUCHY(1, 4) SSM_CAUCHY(1, 2) SSM_CAUCHY(1, 1)
     SSM_CAUCHY_H(1, 1) SSM_CAUCHY_H(2, 1) SSM_CAUCHY_H(3, 1)
     SSM_CAUCHY(4, 1)

@@ -186,10 +186,13 @@ __global__ __launch_bounds__(256) void wtwiddle4_kernel(int M, float2* __restric
 template <int LOGM>
 hipError_t wspec_launch(bool from_roots, int64_t H, int64_t L, int64_t tiles, const float2* roots,
                         const int32_t* tstat, const float* Kin, int64_t kstride, const float* D, float2* K_out,
-                        int32_t* status, float2* khat, float2* tw4, hipStream_t stream) {
+                        int32_t* status, float2* khat, float2* tw4, hipStream_t stream, bool tw4_ready) {
     using G = WGeo<LOGM>;
-    hipLaunchKernelGGL(wtwiddle4_kernel, dim3((unsigned)((2 * G::M + 255) / 256)), dim3(256), 0, stream, G::M, tw4);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    if (!tw4_ready) {
+        hipLaunchKernelGGL(wtwiddle4_kernel, dim3((unsigned)((2 * G::M + 255) / 256)), dim3(256), 0, stream, G::M,
+                           tw4);
+        if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
     if (from_roots)
         hipLaunchKernelGGL((wspec_kernel<LOGM, true>), dim3((unsigned)H), dim3(G::T), 0, stream, (int)L, (int)tiles,
                            roots, tstat, Kin, kstride, D, K_out, status, khat, (const float2*)tw4);
@@ -217,14 +220,16 @@ hipError_t wconv_launch(int64_t Bsz, int64_t H, int64_t L, const float* u, float
 // the wave-structured path covers these transform lengths
 bool wave_path_fits(int64_t M) { return M >= 1024 && M <= 16384; }
 
+// tw4_ready: the table was written earlier on this stream (by the root-value launch)
 hipError_t launch_wspectrum(bool from_roots, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                             const int32_t* tstat, const float* Kin, int64_t kstride, const float* D,
-                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream) {
+                            float2* K_out, int32_t* status, float2* khat, float2* tw4, hipStream_t stream,
+                            bool tw4_ready) {
     switch (ilog2_exact(M)) {
 #define SSM_WSPEC_CASE(LG)                                                                                       \
     case LG:                                                                                                     \
         return wspec_launch<LG>(from_roots, H, L, tiles, roots, tstat, Kin, kstride, D, K_out, status, khat,    \
-                                tw4, stream);
+                                tw4, stream, tw4_ready);
         SSM_WSPEC_CASE(10) SSM_WSPEC_CASE(11) SSM_WSPEC_CASE(12) SSM_WSPEC_CASE(13) SSM_WSPEC_CASE(14)
 #undef SSM_WSPEC_CASE
         default: return hipErrorInvalidValue;
