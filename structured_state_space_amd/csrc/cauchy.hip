@@ -279,6 +279,10 @@ __device__ __forceinline__ void split_pair(float a, float b, h2& hi, h2& lo) {
     lo = __builtin_convertvector(r, h2);
 }
 
+__device__ __forceinline__ double2 c_mul_d(double2 a, double2 b) {
+    return make_double2(a.x * b.x - a.y * b.y, a.x * b.y + a.y * b.x);
+}
+
 template <int RK>
 // Workgroups H.. of the same grid write the per-call root tables, and after
 // them (tw4 given) the wave-structured transforms' table
@@ -516,16 +520,22 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
         for (int sub = 0; sub < nch; sub += 64) {
             __syncthreads();  // staged states visible; the previous sub-chunk's powers and weights are read
             const int nsub = min(64, nch - sub);
-            if (tid < 64) {
+            {   // 4 threads per state, each 10 consecutive powers from q^(10 k)
+                static_assert(kFarJ == 40, "4 x 10 powers");
+                const int m = tid >> 2, k = tid & 3;
                 double2 q = make_double2(0.0, 0.0), pw = make_double2(0.0, 0.0);
-                if (tid < nsub) {
-                    const float2 lam = sl[sub + tid];
+                if (m < nsub) {
+                    const float2 lam = sl[sub + m];
                     q = make_double2(((double)lam.x - cx) * iR, ((double)lam.y - cy) * iR);
                     pw = make_double2(1.0, 0.0);
+                    // q^(10 k) = (q^10)^k, q^10 = ((q^2)^2 q)^2
+                    const double2 q2 = c_mul_d(q, q), q5 = c_mul_d(c_mul_d(q2, q2), q), q10 = c_mul_d(q5, q5);
+                    for (int i = 0; i < k; ++i) pw = c_mul_d(pw, q10);
                 }
-                for (int j = 0; j < kFarJ; ++j) {
-                    qp[tid][j] = make_float2((float)pw.x, (float)pw.y);
-                    pw = make_double2(pw.x * q.x - pw.y * q.y, pw.x * q.y + pw.y * q.x);
+#pragma unroll
+                for (int j = 0; j < 10; ++j) {
+                    qp[m][10 * k + j] = make_float2((float)pw.x, (float)pw.y);
+                    pw = c_mul_d(pw, q);
                 }
             }
             // the weights of the sub-chunk's states (zero past it)
@@ -566,13 +576,20 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
     for (int i2 = 0; i2 < NMT; ++i2)
         if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = make_double2(macc[i2].x, macc[i2].y);
     __syncthreads();
-    if (tid < F) {
+    // tau'_f: 8 threads per family (consecutive lanes) take every 8th moment,
+    // then a shuffle maximum over the 8
+    static_assert(8 * F <= 256 && kFarJ % 8 == 0, "8 threads per family");
+    if (tid < 8 * F) {
+        const int f = tid >> 3, g = tid & 7;
         float tm = 0.0f;
-        for (int j = 0; j < kFarJ; ++j) {
-            const double2 m = mt[j * F + tid];
+#pragma unroll
+        for (int j = g; j < kFarJ; j += 8) {
+            const double2 m = mt[j * F + f];
             tm = fmaxf(tm, fmaxf(fabsf((float)m.x), fabsf((float)m.y)));
         }
-        tauf[tid] = tm;
+#pragma unroll
+        for (int o = 1; o < 8; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
+        if (g == 0) tauf[f] = tm;
     }
     __syncthreads();
     if (tid < 16) {
