@@ -13,13 +13,17 @@
 // S_uv(z) = (2/(1+z)) u^* R v term by term, but keeps the denominators' real part
 // exactly -Re(lambda_n), which float32 needs when a = 2/dt is large.
 //
-// Work split: one workgroup per (channel, tile of 256*RPT roots).  Per chunk of
-// states the workgroup stages a header (x^2, Im lambda) and the weight block of
-// each state in LDS (roots.hpp); every thread then sweeps the chunk for its RPT
+// Two kernels.  The float32 one (rank 1 below 128 states or 4096 roots, rank
+// 4): one workgroup per (channel, tile of 256*RPT roots).  Per chunk of states
+// the workgroup stages a header (x^2, Im lambda) and the weight block of each
+// state in LDS (roots.hpp); every thread then sweeps the chunk for its RPT
 // roots: per (root, state) one reciprocal and a multiply on the vector ALU
 // (with d = x + i y, x = -Re lambda, y = a t_k - Im lambda: inv = 1/|d|^2 and
 // y inv), and the products with the weights on the matrix cores, four real
-// columns per 4x4x1 instruction.
+// columns per 4x4x1 instruction.  The split-precision one (the other shapes):
+// a per-channel record kernel, then a sweep on the float16 matrix cores in
+// high and low parts, where waves of roots far from the poles sum a moment
+// expansion instead of the states (see its section below).
 // Exact zeros: a zero denominator makes the sums NaN; such roots are re-checked
 // with an exact test (-Re lambda == 0 and a t_k - Im lambda == 0 in float32) and
 // flagged resonant-diagonal.  A W with an exactly zero pivot (partial pivoting,
@@ -863,8 +867,9 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
             }
         }
         if (far) {
-            // A entries u v^j, u = v/|v| = conj(s - c)/|s - c|, for j = 8 kb +
-            // 4 (l / 32) + 0..3: the sums are Mt-products times tau_f/|s - c|
+            // Cauchy-side entries u v^j, u = v/|v| = conj(s - c)/|s - c|, for
+            // j = 8 kb + 4 (l / 32) + 0..3: the sums are the products with the
+            // moment blocks times tau'_f/|s - c|
             f2v vv[NB], pw[NB];
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) {
