@@ -22,7 +22,9 @@
 // slice k1 is the conjugate of slice P - 1 - k1 at the complemented positions.
 //
 // Launches (conv, per chunk of row pairs): wl_conv_a, one workgroup per (row
-// pair, k1), both halves, writes Z; wl_conv_b combines Z into the output rows.
+// pair, k1), the half c = 1 at slice k1 and the half c = 3 at slice P - 1 - k1
+// (conjugate radix-P weights: one pass over the inputs serves both), writes Z;
+// wl_conv_b combines Z into the output rows.
 // Spectrum: wl_spec, one workgroup per (channel, k1), from the real kernel.
 #include <type_traits>
 
@@ -190,12 +192,19 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
     for (int e = 0; e < 16; ++e) buf_st_c64(v[e], rs, vo, e * 64 * sizeof(float2));
 }
 
-// One workgroup per (row pair, k1) of the chunk [p0, p0 + np): both halves'
-// Y_k1 from the pair's inputs, transform, product with the spectrum slice,
-// inverse, conjugate twiddle; Z[pl][half][k1][q] (natural q).  Items are
-// renumbered so that the P workgroups of one pair share an XCD (their inputs
-// are read into its L2 once).
-template <int LOGP>
+// One workgroup per (row pair, k1) of the chunk [p0, p0 + np): the half c = 1
+// at slice k1 and the half c = 3 at slice P - 1 - k1, whose radix-P weights are
+// conjugates (3 + 4 (P - 1 - k1) = 4 P - (1 + 4 k1)), so one pass over the
+// pair's inputs gives both: with the rows a (real part) and b (imaginary part),
+// A = sum_p a_p W_p and B = sum_p b_p W_p, W_p = w_4P^(p (1 + 4 k1)), the c = 1
+// sum is A + i B and the c = 3 sum conj(A) + i conj(B).  Both halves take the
+// spectrum slice k1 (the c = 3 slice P - 1 - k1 is the conjugate of slice k1 at
+// the complemented positions).  Each half is transformed, multiplied by its
+// spectrum, inverse transformed and untwisted into Z[pl][half][slice][q]
+// (natural q).  Items are renumbered so that the P workgroups of one pair share
+// an XCD (their inputs are read into its L2 once).  FULL: L = M, every input
+// position exists (no per-element test).
+template <int LOGP, bool FULL>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl_conv_a_kernel(
     int Bsz, int H, int L, int npb, int64_t p0, int64_t nitems, int remap, const float* __restrict__ u,
     const float2* __restrict__ S, float2* __restrict__ Z, const float2* __restrict__ tw4Q,
@@ -220,36 +229,34 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
     const rsrc_t r2 = make_rsrc(u + row1 + (has2 ? (size_t)H * L : 0), (uint32_t)L * sizeof(float));
     const uint32_t vt = (uint32_t)t * sizeof(float);
 
-    // Y for both halves (m = 1 + 4 k1 and 3 + 4 k1) from the same P inputs per q
     float2 ya[16], yb[16];
     {
-        const int ma = 1 + 4 * k1, mb = 3 + 4 * k1;
-        float2 wa[P], wb[P];
+        const int ma = 1 + 4 * k1, mb = 4 * P - ma;
+        float2 wa[P];
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
-            wa[p] = root4p<LOGP>(tw4M, p * ma);
-            wb[p] = root4p<LOGP>(tw4M, p * mb);
-        }
+        for (int p = 0; p < P; ++p) wa[p] = root4p<LOGP>(tw4M, p * ma);
         float2 ta = tw4M[t * ma], tb = tw4M[t * mb];
         const float2 sa = tw4M[kT * ma], sb = tw4M[kT * mb];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int q = t + kT * e;
-            float2 aa = make_float2(0.0f, 0.0f), ab = make_float2(0.0f, 0.0f);
+            float2 A = make_float2(0.0f, 0.0f), B = make_float2(0.0f, 0.0f);
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                const int n = q + kQ * p;
-                float2 zv = make_float2(0.0f, 0.0f);
-                if (n < L) {
-                    const uint32_t so = (uint32_t)(kT * e + kQ * p) * sizeof(float);
-                    zv.x = buf_ld_f32(r1, vt, so);
-                    if (has2) zv.y = buf_ld_f32(r2, vt, so);
+                const uint32_t so = (uint32_t)(kT * e + kQ * p) * sizeof(float);
+                float av = 0.0f, bv = 0.0f;
+                if (FULL || q + kQ * p < L) {
+                    av = buf_ld_f32(r1, vt, so);
+                    bv = buf_ld_f32(r2, vt, so);  // row 1 again without a second row: dropped below
                 }
-                aa = c_add(aa, c_mul(zv, wa[p]));
-                ab = c_add(ab, c_mul(zv, wb[p]));
+                A.x = fmaf(av, wa[p].x, A.x);
+                A.y = fmaf(av, wa[p].y, A.y);
+                B.x = fmaf(bv, wa[p].x, B.x);
+                B.y = fmaf(bv, wa[p].y, B.y);
             }
-            ya[e] = c_mul(aa, ta);
-            yb[e] = c_mul(ab, tb);
+            if (!has2) B = make_float2(0.0f, 0.0f);
+            ya[e] = c_mul(make_float2(A.x - B.y, A.y + B.x), ta);
+            yb[e] = c_mul(make_float2(A.x + B.y, B.x - A.y), tb);
             if (e < 15) {
                 power_after(ta, ya[e]);
                 power_after(tb, yb[e]);
@@ -261,19 +268,18 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
     const uint32_t vq = (uint32_t)t * sizeof(float2);
     const int wv = t >> 6, lane = t & 63;
     // one half: transform, product with its spectrum slice, inverse, conjugate
-    // twiddle, store (HALF 0: c = 1; HALF 1: c = 3)
+    // twiddle, store (HALF 0: c = 1 at slice k1; HALF 1: c = 3 at slice P - 1 - k1)
     auto half = [&](float2(&v)[16], auto half_tag) {
         constexpr int HALF = decltype(half_tag)::value;
-        const int m = (HALF ? 3 : 1) + 4 * k1;
+        const int ks = HALF ? P - 1 - k1 : k1;
+        const int m = (HALF ? 3 : 1) + 4 * ks;
         wf_forward<kLogQ, 0>(v, lds, tw4Q, t);
+        const rsrc_t rs = make_rsrc(S + (size_t)h * M + (size_t)k1 * kQ, kQ * sizeof(float2));
         if constexpr (HALF == 0) {
-            const rsrc_t rs = make_rsrc(S + (size_t)h * M + (size_t)k1 * kQ, kQ * sizeof(float2));
             const uint32_t vk = (uint32_t)wf_pos(t, 0) * sizeof(float2);
 #pragma unroll
             for (int e = 0; e < 16; ++e) v[e] = c_mul(v[e], buf_ld_c64(rs, vk, e * 64 * sizeof(float2)));
         } else {
-            // the c = 3 slice k1: conj of slice P - 1 - k1 at the complemented position
-            const rsrc_t rs = make_rsrc(S + (size_t)h * M + (size_t)(P - 1 - k1) * kQ, kQ * sizeof(float2));
             const uint32_t vkm = (uint32_t)((GQ::W - 1 - wv) * 16 * 64 + 63 - lane) * sizeof(float2);
 #pragma unroll
             for (int e = 0; e < 16; ++e)
@@ -282,7 +288,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
         wf_inverse<kLogQ, 0>(v, lds, tw4Q, t);
         float2 tc = c_conj(tw4M[t * m]);
         const float2 sc = c_conj(tw4M[kT * m]);
-        const rsrc_t rz = make_rsrc(Z + ((size_t)pl * 2 + HALF) * M + (size_t)k1 * kQ, kQ * sizeof(float2));
+        const rsrc_t rz = make_rsrc(Z + ((size_t)pl * 2 + HALF) * M + (size_t)ks * kQ, kQ * sizeof(float2));
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             buf_st_c64(c_mul(v[e], tc), rz, vq, kT * e * sizeof(float2));
@@ -378,8 +384,12 @@ hipError_t wl_conv_t(int64_t Bsz, int64_t H, int64_t L, const float* u, float* y
         const int64_t items = np * P;
         // the renumbering is a bijection when the items fill whole rounds of 8 XCDs x P
         const int remap = items % (8 * P) == 0 ? 1 : 0;
-        hipLaunchKernelGGL((wl_conv_a_kernel<LOGP>), dim3((unsigned)items), dim3(kT), 0, s, (int)Bsz, (int)H, (int)L,
-                           (int)npb, p0, items, remap, u, S, Z, tw4Q, tw4M);
+        if (L == (int64_t)P * kQ)
+            hipLaunchKernelGGL((wl_conv_a_kernel<LOGP, true>), dim3((unsigned)items), dim3(kT), 0, s, (int)Bsz, (int)H,
+                               (int)L, (int)npb, p0, items, remap, u, S, Z, tw4Q, tw4M);
+        else
+            hipLaunchKernelGGL((wl_conv_a_kernel<LOGP, false>), dim3((unsigned)items), dim3(kT), 0, s, (int)Bsz,
+                               (int)H, (int)L, (int)npb, p0, items, remap, u, S, Z, tw4Q, tw4M);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL((wl_conv_b_kernel<LOGP>), dim3((unsigned)(np * (kQ / 256))), dim3(256), 0, s, (int)Bsz,
                            (int)H, (int)L, (int)npb, p0, y, (const float2*)Z, tw4M);

@@ -224,7 +224,7 @@ def test_forward_end_to_end(idx, nsample):
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("Bsz,H,L", [(1, 1, 1), (1, 1, 2), (3, 2, 3), (2, 3, 17), (5, 4, 100), (2, 9, 1000),
                                      (4, 8, 1024), (3, 5, 3000), (2, 3, 8192), (1, 2, 16384), (4, 2, 16384),
-                                     (3, 2, 20000), (2, 1, 65536)])
+                                     (3, 2, 20000), (1, 1, 32768), (2, 1, 65536), (3, 1, 65536)])
 def test_fftconv_matches_direct_sum(Bsz, H, L):
     ssm = _ssm()
     rng = np.random.default_rng(L * 7 + H)
