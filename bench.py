@@ -416,6 +416,57 @@ def bench_complex(args, w, p, u, dev):
     return 0
 
 
+def bench_kernel_gen(args, w, p, dev):
+    """ssm_kernel_gen (root values and the kernel K, no roots output) as whole
+    calls on the workload's channels.  Rated on the root values' algorithmic
+    flops alone (as the forward's root-value stage: the terms summed) over the
+    whole call, so the kernel transform's time counts against it."""
+    import torch
+
+    from structured_state_space_amd import ssm
+    d = ssm.to_device(p, dev)
+    Ct = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], w.L, want_bbar=False)["Ctilde"]
+    ws = torch.empty(ssm.workspace_bytes(ssm.OP_KERNEL_GEN, 1, w.H, w.N, w.r, w.L), dtype=torch.uint8, device=dev)
+
+    def call():
+        return ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], w.L, workspace=ws)
+
+    for _ in range(args.warmup):
+        out = call()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t_wall = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        out = call()
+    end.record()
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms_events = start.elapsed_time(end) / args.steps
+    ms = max(ms_events, 1e3 * t_wall / args.steps)
+    if int(out["status"].abs().max()) != 0 or not bool(torch.isfinite(out["K"]).all()):
+        raise RuntimeError("kernel generation produced a nonzero status or non-finite values")
+    M = ssm.transform_lengths(w.L)[0]
+    alg = algorithmic(w, M, False)["cauchy"]
+    if split_kernel(w.N, w.r, M):
+        alg["work"] = root_value_terms(p, M, False)[0] * (8 * (w.r + 1) ** 2 + 7)
+    achieved = alg["work"] * alg["scale"] / (ms * 1e-3)
+    one_launch = M == 1024 and w.H >= 256
+    line = {
+        "metric": "kernel generations/sec (root values and K for every channel)", "unit": "calls/s",
+        "value": 1e3 / ms, "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": w.name, "op": "kernel_gen", "H": w.H, "N": w.N, "r": w.r, "L": w.L, "M": M,
+                   "launches": 1 if one_launch else 2},
+        "roofline": {"bound": alg["bound"], "achieved": achieved, "peak": alg["peak"], "unit": alg["unit"],
+                     "frac": achieved / alg["peak"], "traffic": None,
+                     "work": "root values' algorithmic flops over the whole call"},
+        "ms_per_step_events": ms_events,
+    }
+    print(json.dumps(line))
+    return 0
+
+
 HIPPO_METRIC = "HiPPO-to-DPLR constructions/sec (generator, eigenvectors, B and per-channel C)"
 
 
@@ -512,11 +563,12 @@ def main():
                          "or time only them (only)")
     ap.add_argument("--hippo-kind", choices=("legs", "legt", "lagt"), default="legs",
                     help="generator for --op hippo")
-    ap.add_argument("--op", choices=("forward", "step", "complex", "hippo"), default="forward",
+    ap.add_argument("--op", choices=("forward", "step", "complex", "hippo", "kernel_gen"), default="forward",
                     help="forward: the filter path (the headline); step: the recurrent step mode, "
                          "T = L steps of every sequence per call, the state carried between calls; "
                          "complex: the filter path with the imaginary output as well; "
-                         "hippo: DPLR parameters of a HiPPO generator at the workload's N, one C row per channel")
+                         "hippo: DPLR parameters of a HiPPO generator at the workload's N, one C row per channel; "
+                         "kernel_gen: the kernel generator alone (root values and K)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration) and exit")
     args = ap.parse_args()
@@ -559,6 +611,8 @@ def main():
         return bench_complex(args, w, p, u, dev)
     if args.op == "hippo":
         return bench_hippo(args, w, dev)
+    if args.op == "kernel_gen":
+        return bench_kernel_gen(args, w, p, dev)
     M, n_fft = ssm.transform_lengths(w.L)
     form = ssm.forward_form(w.Bsz, w.H, w.L)
     fused = form == 2

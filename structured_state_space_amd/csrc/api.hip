@@ -29,7 +29,7 @@ bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M);
 hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
                          const float2* P, const float2* Q, const float2* Bv, const float2* Ct, const float* dt,
                          const float* D, const float* u, float* y, float2* K_out, int32_t* status,
-                         hipStream_t stream);
+                         hipStream_t stream, float2* roots_out = nullptr);
 hipError_t launch_conv_fused(int64_t Bsz, int64_t H, int64_t L, int64_t M, int64_t tiles, const float2* roots,
                              const int32_t* tstat, const float* D, float2* K_out, int32_t* status, const float* u,
                              float* y, const float2* twtab, hipStream_t stream);
@@ -280,6 +280,10 @@ int ssm_kernel_gen(int64_t H, int64_t N, int64_t r, int64_t L, const ssm_c64* La
     const WsLayout w = layout(SSM_OP_KERNEL_GEN, 1, H, N, r, L);
     if (ws_bytes < w.total || !ws) return SSM_ERR_WORKSPACE;
     hipStream_t s = (hipStream_t)stream;
+    if (single_launch_fits(0, H, M))  // one launch: root values and kernel transform per channel workgroup
+        return device_status(launch_single(0, H, N, r, L, (const float2*)Lambda, (const float2*)P,
+                                           (const float2*)Q, (const float2*)B, (const float2*)Ctilde, dt, nullptr,
+                                           nullptr, nullptr, (float2*)K, status, s, (float2*)roots_out));
     char* base = (char*)ws;
     float2* roots = roots_out ? (float2*)roots_out : (float2*)(base + w.roots);
     int32_t* tstat = (int32_t*)(base + w.tstat);

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
     int Bsz, int H, int N, int L, const float2* __restrict__ Lambda, const float2* __restrict__ P,
     const float2* __restrict__ Q, const float2* __restrict__ Bv, const float2* __restrict__ Ct,
     const float* __restrict__ dt, const float* __restrict__ D, const float* __restrict__ u, float* __restrict__ y,
-    float2* __restrict__ K_out, int32_t* __restrict__ status) {
+    float2* __restrict__ K_out, int32_t* __restrict__ status, float2* __restrict__ roots_out) {
     constexpr int M = kM1, E = kE1, T = kT1;
     constexpr int F = Fam<RK>::F, kChunk = Fam<RK>::CHUNK, U = sweep_unroll<RK, 1>();
     __shared__ float2 hdr[kChunk];
@@ -190,6 +190,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
         Hk = c_nan();
     }
     rootl[k] = Hk;
+    if (roots_out) roots_out[(size_t)h * M + k] = Hk;
     if (my_status) atomicMax(&blk_status, my_status);
     __syncthreads();
     const int chst = blk_status;
@@ -229,12 +230,13 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
             if (j == 0 && D) kr += D[h];
             kl[j] = kr * sc;
         }
-    } else if (zwave) {
+    } else if (zwave && Bsz > 0) {
 #pragma unroll
         for (int e = 0; e < E; ++e) x[0][e] = half ? c_mul(z[e], twl[t + T * e]) : z[e];
         fft_multi<1, kLogM1, kLogE1, false, false, 4, true>(x, mine, t, tw);
     }
     __syncthreads();
+    if (Bsz == 0) return;  // the kernel alone (uniform: no barrier follows for anyone)
 
     // B2: the cyclic (c = 0) and twisted (c = 1) spectra, each split over four
     // of the free waves (0 and 9-15) by one radix-4 step of decimation in
@@ -298,6 +300,7 @@ __global__ __launch_bounds__(kThreads1) void filter_m1024_kernel(
 
 }  // namespace
 
+// Bsz = 0: the kernel (and the root values) alone, no spectra and no rows
 bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M) {
     return M == kM1 && (Bsz + 1) / 2 <= kPairs1 && H >= 256;
 }
@@ -305,11 +308,11 @@ bool single_launch_fits(int64_t Bsz, int64_t H, int64_t M) {
 hipError_t launch_single(int64_t Bsz, int64_t H, int64_t N, int64_t r, int64_t L, const float2* Lambda,
                          const float2* P, const float2* Q, const float2* Bv, const float2* Ct, const float* dt,
                          const float* D, const float* u, float* y, float2* K_out, int32_t* status,
-                         hipStream_t stream) {
+                         hipStream_t stream, float2* roots_out) {
 #define SSM_SINGLE(RK)                                                                                        \
     if (r == RK) {                                                                                            \
         hipLaunchKernelGGL((filter_m1024_kernel<RK>), dim3((unsigned)H), dim3(kThreads1), 0, stream, (int)Bsz, \
-                           (int)H, (int)N, (int)L, Lambda, P, Q, Bv, Ct, dt, D, u, y, K_out, status);         \
+                           (int)H, (int)N, (int)L, Lambda, P, Q, Bv, Ct, dt, D, u, y, K_out, status, roots_out); \
         return hipGetLastError();                                                                             \
     }
     SSM_SINGLE(1) SSM_SINGLE(2) SSM_SINGLE(3) SSM_SINGLE(4)

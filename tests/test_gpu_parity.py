@@ -109,6 +109,8 @@ def test_root_values_multipass_lengths(L):
     (8, 300, 2, 2048, 2),     # rank 2 past one 256-state record chunk: 4 x 64 + 44 states in the sweep
     (4, 270, 3, 1024, 2),     # rank 3 past one record chunk
     (4, 66, 4, 1500, 2),      # rank 4: 64 + 2 states
+    (256, 64, 1, 1024, 4),    # M = 1024, 256 channels: one launch per channel workgroup
+    (256, 203, 2, 1000, 3),   # the same, rank 2, 128 + 75 states
 ])
 def test_root_values_chunks_and_roots_per_thread(H, N, r, L, nsample):
     """Root values from a supplied C~ (random here: the kernel generator takes it
@@ -341,21 +343,32 @@ def test_single_launch_form(r, L, Bsz, N):
     ut = torch.from_numpy(u).to(DEV)
     Ct = ssm.discretize(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], L, want_bbar=False)["Ctilde"]
     fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], d["D"], ut, want_kernel=True)
-    kg = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], L)
-    y_sep = ssm.fftconv(kg["K"], ut, D=d["D"])
+    # the kernel generator at M = 1024 and 256 channels takes the same one-launch
+    # form without rows; on 128 channels it takes the separate root-value and
+    # transform kernels
+    kg = ssm.kernel_gen(d["Lambda"], d["P"], d["Q"], d["B"], Ct, d["dt"], L, want_roots=True)
+    hs = slice(0, 128)
+    kg2 = ssm.kernel_gen(d["Lambda"][hs], d["P"][hs], d["Q"][hs], d["B"][hs], Ct[hs], d["dt"][hs], L,
+                         want_roots=True)
+    y_sep = ssm.fftconv(kg2["K"], ut[:, hs].contiguous(), D=d["D"][hs])
     torch.cuda.synchronize()
-    st, st_sep = _np(fw["status"]), _np(kg["status"])
+    st, st_kg, st_sep = _np(fw["status"]), _np(kg["status"]), _np(kg2["status"])
     expect = np.zeros(H, np.int32)
     expect[5], expect[7] = ssm.ST_INVALID_STEP, ssm.ST_RESONANT_DIAGONAL
-    assert list(st) == list(expect) and list(st_sep) == list(expect)
-    K, y, Ks, ys = _np(fw["K"]), _np(fw["y"]), _np(kg["K"]), _np(y_sep)
+    assert list(st) == list(expect) and list(st_kg) == list(expect) and list(st_sep) == list(expect[hs])
+    K, y, Kg, Ks, ys = _np(fw["K"]), _np(fw["y"]), _np(kg["K"]), _np(kg2["K"]), _np(y_sep)
+    R, Rs = _np(kg["roots"]), _np(kg2["roots"])
     for h in (5, 7):
-        assert np.isnan(K[h]).all() and np.isnan(y[:, h, :]).all()
+        assert np.isnan(K[h]).all() and np.isnan(y[:, h, :]).all() and np.isnan(Kg[h]).all()
+    assert np.isnan(R[5]).all() and np.isnan(Rs[5]).all()
     ok = np.array([h for h in range(H) if h not in (5, 7)])
-    assert np.isfinite(K[ok]).all() and np.isfinite(y[:, ok, :]).all()
+    assert np.isfinite(K[ok]).all() and np.isfinite(y[:, ok, :]).all() and np.isfinite(Kg[ok]).all()
     for h in ok:
-        assert_rows_close(K[h][None], Ks[h][None], what=f"K h{h} vs separate kernels")
-        assert_rows_close(y[:, h, :], ys[:, h, :], what=f"y h{h} vs separate kernels")
+        assert_rows_close(Kg[h][None], K[h][None], what=f"K h{h}: kernel generator vs forward")
+        if h < 128:
+            assert_rows_close(K[h][None], Ks[h][None], what=f"K h{h} vs separate kernels")
+            assert_rows_close(R[h][None], Rs[h][None], what=f"root values h{h} vs separate kernels")
+            assert_rows_close(y[:, h, :], ys[:, h, :], what=f"y h{h} vs separate kernels")
     for h in sample_channels(H, 3, seed=r + L):
         h = int(h)
         if h in (5, 7):
