@@ -85,6 +85,21 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
     const int tile = blockIdx.x - h * tiles;
     const int tid = threadIdx.x;
     const size_t hbase = (size_t)h * N;
+    // the first chunk's state inputs are loaded before anything else, so that
+    // their latency overlaps the step check and the tangents
+    float2 f_lam = make_float2(0.0f, 0.0f), f_uu[RK + 1], f_vv[RK + 1];
+    const bool f_has = tid < min(kChunk, N);
+    if (f_has) {
+        const size_t hn = hbase + tid;
+        f_lam = Lambda[hn];
+        f_uu[0] = Ct[hn];
+        f_vv[0] = Bv[hn];
+#pragma unroll
+        for (int j = 0; j < RK; ++j) {
+            f_uu[1 + j] = Q[hn * RK + j];
+            f_vv[1 + j] = P[hn * RK + j];
+        }
+    }
     const float dtv = dt[h];
 
 
@@ -150,18 +165,27 @@ __global__ __launch_bounds__(kCauchyThreads) __attribute__((amdgpu_waves_per_eu(
                 continue;
             }
             const size_t hn = hbase + n0 + nn;
-            const float2 lam = Lambda[hn];
-            float2 uu[RK + 1], vv[RK + 1];
-            uu[0] = Ct[hn];
-            vv[0] = Bv[hn];
+            float2 lam, uu[RK + 1], vv[RK + 1];
+            if (n0 == 0 && nn == tid) {  // the prefetched state (nn = tid < nch on the first chunk)
+                lam = f_lam;
+#pragma unroll
+                for (int j = 0; j <= RK; ++j) {
+                    uu[j] = f_uu[j];
+                    vv[j] = f_vv[j];
+                }
+            } else {
+                lam = Lambda[hn];
+                uu[0] = Ct[hn];
+                vv[0] = Bv[hn];
+#pragma unroll
+                for (int j = 0; j < RK; ++j) {
+                    uu[1 + j] = Q[hn * RK + j];
+                    vv[1 + j] = P[hn * RK + j];
+                }
+            }
             // z = -1 takes (dt/2) C~^* B: partial sums in float64, reduced after the sweep
             m1x += (double)uu[0].x * vv[0].x + (double)uu[0].y * vv[0].y;
             m1y += (double)uu[0].x * vv[0].y - (double)uu[0].y * vv[0].x;
-#pragma unroll
-            for (int j = 0; j < RK; ++j) {
-                uu[1 + j] = Q[hn * RK + j];
-                vv[1 + j] = P[hn * RK + j];
-            }
             stage_state<RK>(hdr + nn, wt + nn * Fam<RK>::WROW, lam, uu, vv);
         }
         __syncthreads();
