@@ -49,6 +49,13 @@ __device__ __forceinline__ float2 root4p(const float2* tw4M, int j) {
     return j >= 2 * P ? make_float2(-w.x, -w.y) : w;
 }
 
+// a i^k, exact (k folds to a constant in unrolled loops): conj(w_P^(p j)) =
+// i^(4 p j/P) for P = 2 and 4
+__device__ __forceinline__ float2 mul_ipow(float2 a, int k) {
+    const float2 r = (k & 1) ? make_float2(-a.y, a.x) : a;
+    return (k & 2) ? make_float2(-r.x, -r.y) : r;
+}
+
 // The kernel transform from the root values (M = P Q): the root values are
 // stored per channel as [P][Q] in the scrambled order (slice k1 holds the
 // frequencies P k2 + k1 in the Q-transform's order).  One workgroup per
@@ -109,7 +116,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
 // wl_kt (the workgroup with k1 = 0 also writes K_out); otherwise Kin: K [H][L]
 // with element stride kstride (1: real; 2: the real part of a complex kernel).
 // grid H * P, 1024 threads.
-template <int LOGP, bool FROM_T>
+template <int LOGP, bool FROM_T, bool FULL = false>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl_spec_kernel(
     int L, const float* __restrict__ Kin, int64_t kstride, const float2* __restrict__ Tin, const float* __restrict__ D,
     float2* __restrict__ K_out, float2* __restrict__ S, const float2* __restrict__ tw4Q,
@@ -147,7 +154,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
             for (int p = 0; p < P; ++p) {
                 float2 kv = make_float2(0.0f, 0.0f);
 #pragma unroll
-                for (int j = 0; j < P; ++j) kv = c_add(kv, c_mul(tk[j], c_conj(root4p<LOGP>(tw4M, 4 * p * j))));
+                for (int j = 0; j < P; ++j) kv = c_add(kv, mul_ipow(tk[j], (p * j) << (2 - LOGP)));
                 kv = c_scale(kv, invM);
                 const int n = q + kQ * p;
                 if (K_out && k1 == 0 && n < L) K_out[(size_t)h * L + n] = kv;
@@ -163,21 +170,30 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(4))) void wl
         }
     } else {
         const rsrc_t rk = make_rsrc(Kin + (size_t)h * L * kstride, (uint32_t)(L * kstride) * sizeof(float));
-        const uint32_t vk = (uint32_t)(t * kstride) * sizeof(float);
+        // all of the thread's taps first, with no branch between the loads (a
+        // tap past L reads tap 0 and is replaced by zero), so that they are in
+        // flight together; FULL (L = M): every tap exists.  Stride 2 (the real
+        // part of a complex kernel) reads every other float of one contiguous
+        // run per wave.
+        float kv[16][P];
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+#pragma unroll
+            for (int p = 0; p < P; ++p) {
+                const int n = t + kT * e + kQ * p;
+                const bool in = FULL || n < L;
+                kv[e][p] = buf_ld_f32(rk, (uint32_t)((in ? n : 0) * kstride) * sizeof(float), 0);
+            }
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int q = t + kT * e;
+            if (!FULL)
+#pragma unroll
+                for (int p = 0; p < P; ++p) kv[e][p] = q + kQ * p < L ? kv[e][p] : 0.0f;
+            if (q == 0) kv[e][0] += dv;
             float2 acc = make_float2(0.0f, 0.0f);
 #pragma unroll
-            for (int p = 0; p < P; ++p) {
-                const int n = q + kQ * p;
-                const uint32_t so = (uint32_t)((kT * e + kQ * p) * kstride) * sizeof(float);
-                // stride 2 (the real part of a complex kernel): whole complex loads, the
-                // wave's accesses one contiguous run
-                float kv = n < L ? (kstride == 2 ? buf_ld_c64(rk, vk, so).x : buf_ld_f32(rk, vk, so)) : 0.0f;
-                if (n == 0) kv += dv;
-                acc = c_add(acc, c_scale(wp[p], kv * sc));
-            }
+            for (int p = 0; p < P; ++p) acc = c_add(acc, c_scale(wp[p], kv[e][p] * sc));
             v[e] = c_mul(acc, tw);
             if (e < 15) {
                 power_after(tw, v[e]);
@@ -366,8 +382,12 @@ hipError_t wl_spec_t(int64_t H, int64_t L, int64_t tiles, float2* roots, const i
                            (int64_t)1, (const float2*)roots, D, K_out, S, (const float2*)tw4Q, (const float2*)tw4M,
                            remap);
     } else {
-        hipLaunchKernelGGL((wl_spec_kernel<LOGP, false>), dim3((unsigned)(H * P)), dim3(kT), 0, s, (int)L, Kin,
-                           kstride, nullptr, D, nullptr, S, (const float2*)tw4Q, (const float2*)tw4M, remap);
+        if (L == (int64_t)M)
+            hipLaunchKernelGGL((wl_spec_kernel<LOGP, false, true>), dim3((unsigned)(H * P)), dim3(kT), 0, s, (int)L,
+                               Kin, kstride, nullptr, D, nullptr, S, (const float2*)tw4Q, (const float2*)tw4M, remap);
+        else
+            hipLaunchKernelGGL((wl_spec_kernel<LOGP, false, false>), dim3((unsigned)(H * P)), dim3(kT), 0, s, (int)L,
+                               Kin, kstride, nullptr, D, nullptr, S, (const float2*)tw4Q, (const float2*)tw4M, remap);
     }
     return hipGetLastError();
 }
