@@ -447,19 +447,23 @@ def test_split_precision_root_values_hard_cases(r, L):
 @pytest.mark.parametrize("order,r,kind,N", [
     ("reversed", 2, "s4", 64), ("shuffled", 2, "s4", 64), ("shuffled", 3, "random", 64),
     ("shuffled", 2, "s4", 40), ("asis", 3, "s4", 57),
+    ("reversed", 1, "s4", 256), ("shuffled", 1, "s4", 130), ("shuffled", 1, "random", 200),
 ])
 def test_far_field_root_values(order, r, kind, N):
-    """Ranks 2 and 3 where many waves of roots take the far-field moment form
-    (the sum over the states replaced by 8 to 24 moment terms).  Poles given in
-    reversed or shuffled order, steps across [1e-3, 1e-1], N with a ragged last
-    block.  Root values
-    (natural order) and the forward path's kernel (the transforms' order)
-    against the oracle.  With the S4 poles at a tenth of the path tolerance:
-    the expansions' tails are below 3 2^-24 of the sums of |terms|, so an error
-    in a moment, a power or a scale shows here.  The random poles (Re down to
-    -0.1) have resonance peaks where rounding s = i a t to float32 alone moves
-    the value by ~4e-5 of the row's largest (with or without the far forms):
-    those take the path tolerance."""
+    """The split-precision kernel (ranks 2 and 3, and rank 1 from 128 states)
+    where many waves of roots take the far-field moment form (the sum over the
+    states replaced by 8 to 40 moment terms).  Poles given in reversed or
+    shuffled order, steps across
+    [1e-3, 1e-1], N with a ragged last block.  Root values (natural order) and
+    the forward path's kernel (the transforms' order) against the oracle.  With
+    the S4 poles at a tenth of the path tolerance: the expansions' tails are
+    below 5 2^-24 of the sums of |terms|, so an error in a moment, a power or a
+    scale shows here.  The random poles (Re down to -0.1) have resonance peaks
+    where rounding s = i a t to float32 alone moves the value by ~4e-5 of the
+    row's largest (with or without the far forms): those take the path
+    tolerance, and so do the S4 poles of more than 64 states, whose resonances
+    reach Im lambda ~ 800, where the same rounding moves a root value by up to
+    ~6e-5 of the row's largest."""
     ssm = _ssm()
     H, L, Bsz = 8, 16384, 2
     p = I.random_params(7000 + 10 * r + N, H, N, r, L, lambda_kind=kind)
@@ -479,7 +483,7 @@ def test_far_field_root_values(order, r, kind, N):
         assert st == O.OK
         ref.append(Hk)
     ref = np.array(ref)
-    tol = TOL / 10 if kind == "s4" else TOL
+    tol = TOL / 10 if kind == "s4" and N <= 64 else TOL
     assert_rows_close(roots, ref, tol=tol, what="root values")
     u = I.random_input(L + N, Bsz, H, L)
     fw = ssm.forward(d["Lambda"], d["P"], d["Q"], d["B"], d["C"], d["dt"], d["D"],
