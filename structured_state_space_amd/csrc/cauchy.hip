@@ -53,9 +53,22 @@ __device__ __forceinline__ void root_tables_at(int j, int M, int scr_logm, doubl
     if (k != j) sincospi((double)k / (double)M, &sn, &cs);
     tant[j] = (2 * k == M) ? 0.0 : sn / cs;
 }
+// exp(-i pi j/(2M)), j < 2M: the wave-structured transforms' table
+__device__ __forceinline__ void tw4_at(int j, int M, float2* __restrict__ tw4) {
+    if (j >= 2 * M) return;
+    double sn, cs;
+    sincospi((double)j / (double)(2 * M), &sn, &cs);
+    tw4[j] = make_float2((float)cs, (float)-sn);
+}
+// the root tables, then (tw4 given: workgroups from ceil(M/256) on) the
+// transforms' table
 __global__ __launch_bounds__(256) void root_tables_kernel(int M, int scr_logm, double* __restrict__ tant,
-                                                          float2* __restrict__ twtab) {
-    root_tables_at(blockIdx.x * 256 + threadIdx.x, M, scr_logm, tant, twtab);
+                                                          float2* __restrict__ twtab, float2* __restrict__ tw4) {
+    const int ntab = (M + 255) / 256, b = (int)blockIdx.x;
+    if (b < ntab)
+        root_tables_at(b * 256 + (int)threadIdx.x, M, scr_logm, tant, twtab);
+    else
+        tw4_at((b - ntab) * 256 + (int)threadIdx.x, M, tw4);
 }
 
 template <int RK, int RPT>
@@ -327,11 +340,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
             root_tables_at(b * 256 + (int)threadIdx.x, M, scr_logm, tant, twtab);
         } else {
             const int j = (b - ntab) * 256 + (int)threadIdx.x;
-            if (j < 2 * M) {
-                double sn, cs;
-                sincospi((double)j / (double)(2 * M), &sn, &cs);
-                tw4[j] = make_float2((float)cs, (float)-sn);
-            }
+            tw4_at(j, M, tw4);
         }
         return;
     }
@@ -1031,10 +1040,13 @@ hipError_t launch_h(int64_t H, int64_t N, int64_t M, int scr_logm, const float2*
 template <int RK, int RPT>
 hipError_t launch_rk(int64_t H, int64_t N, int64_t M, int scr_logm, const float2* Lambda, const float2* P,
                      const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
-                     int32_t* tstat, float2* twtab, double* tant, hipStream_t stream) {
+                     int32_t* tstat, float2* twtab, double* tant, float2* tw4, hipStream_t stream) {
+    // tw4 (nullable): the wave-structured transforms' table, written by the
+    // tables launch (four roots per thread only)
     if (RPT >= 4) {
-        hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)((M + 255) / 256)), dim3(256), 0, stream, (int)M,
-                           scr_logm, tant, twtab);
+        const int64_t blocks0 = (M + 255) / 256 + (tw4 ? (2 * M + 255) / 256 : 0);
+        hipLaunchKernelGGL(root_tables_kernel, dim3((unsigned)blocks0), dim3(256), 0, stream, (int)M, scr_logm, tant,
+                           twtab, tw4);
         if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
     const int tiles = (int)((M + kCauchyThreads * RPT - 1) / (kCauchyThreads * RPT));
@@ -1078,7 +1090,8 @@ int64_t cauchy_prep_bytes(int64_t H, int64_t N, int64_t r, int64_t M) {
 // scrambled: store the root values in the order the wave-structured
 // transforms take them (M >= 1024), not in natural order.  tw4 (nullable): the
 // wave-structured transforms' table of 2M entries, written here when the
-// split-precision kernel runs (*tw4_done tells whether it was).
+// split-precision kernel or the per-call root tables run (*tw4_done tells
+// whether it was).
 hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float2* Lambda, const float2* P,
                          const float2* Q, const float2* Bv, const float2* Ct, const float* dt, float2* roots,
                          int32_t* tile_status, float2* twtab, double* tant, void* prep, hipStream_t stream,
@@ -1089,9 +1102,11 @@ hipError_t launch_cauchy(int64_t H, int64_t N, int64_t r, int64_t M, const float
     const int scr_logm = scrambled ? ilog2_exact(M) : 0;
     if (scrambled && M < 1024) return hipErrorInvalidValue;
 #define SSM_CAUCHY(RK, RPT)                                                                                   \
-    if (!split && r == RK && rpt == RPT)                                                                      \
+    if (!split && r == RK && rpt == RPT) {                                                                    \
+        if (tw4_done) *tw4_done = RPT >= 4 && tw4 != nullptr;                                                 \
         return launch_rk<RK, RPT>(H, N, M, scr_logm, Lambda, P, Q, Bv, Ct, dt, roots, tile_status, twtab, tant, \
-                                  stream);
+                                  RPT >= 4 ? tw4 : nullptr, stream);                                          \
+    }
 #define SSM_CAUCHY_H(RK, RPT)                                                                                  \
     if (split && r == RK && rpt == RPT)                                                                        \
     {                                                                                                          \
