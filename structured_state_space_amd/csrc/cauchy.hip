@@ -515,9 +515,12 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
     // ---- far roots: the poles' centre c and radius R (float64), the moments
     //      Mt_{j,f}, their scales, and the moment blocks ----
     __shared__ double rmax[4];
-    __shared__ float2 qp[64][kFarJ];   // powers ((lambda_n - c)/R)^j of 64 states (formed in float64)
-    __shared__ double2 mt[kFarJ * F];
-    __shared__ float2 wsub[64 * F];    // the weights of 64 states
+    // states per sub-chunk of the moment sums (32 keeps the kernel's LDS under
+    // 40 KB at rank 2: four workgroups per CU)
+    constexpr int kSub = 32;
+    __shared__ float2 qp[kSub][kFarJ];  // powers ((lambda_n - c)/R)^j of kSub states (formed in float64)
+    __shared__ float2 mt[kFarJ * F];
+    __shared__ float2 wsub[kSub * F];   // the weights of kSub states
     __shared__ float tauf[F];
     const double cx = (lsum[0].x + lsum[1].x + lsum[2].x + lsum[3].x) / (double)N;
     const double cy = (lsum[0].y + lsum[1].y + lsum[2].y + lsum[3].y) / (double)N;
@@ -554,10 +557,10 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
             __syncthreads();  // the previous chunk's readers are done
             stage(n0);
         }
-        for (int sub = 0; sub < nch; sub += 64) {
+        for (int sub = 0; sub < nch; sub += kSub) {
             __syncthreads();  // staged states visible; the previous sub-chunk's powers and weights are read
-            const int nsub = min(64, nch - sub);
-            {   // 4 threads per state, each 10 consecutive powers from q^(10 k)
+            const int nsub = min(kSub, nch - sub);
+            if (tid < 4 * kSub) {   // 4 threads per state, each 10 consecutive powers from q^(10 k)
                 static_assert(kFarJ == 40, "4 x 10 powers");
                 const int m = tid >> 2, k = tid & 3;
                 double2 q = make_double2(0.0, 0.0), pw = make_double2(0.0, 0.0);
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
                 }
             }
             // the weights of the sub-chunk's states (zero past it)
-            for (int i = tid; i < 64 * F; i += 256) {
+            for (int i = tid; i < kSub * F; i += 256) {
                 const int m = i / F, f = i - m * F;
                 const int iu = f / (RK + 1), iv = f - iu * (RK + 1);
                 float2 w = make_float2(0.0f, 0.0f);
@@ -597,7 +600,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
                 // two partial sums (even and odd states) to halve the FMA chain
                 float2 a = macc[i2], b = make_float2(0.0f, 0.0f);
 #pragma unroll 4
-                for (int m = 0; m < 64; m += 2) {
+                for (int m = 0; m < kSub; m += 2) {
                     const float2 w0 = wsub[m * F + f], w1 = wsub[(m + 1) * F + f];
                     const float2 q0 = qp[m][j], q1 = qp[m + 1][j];
                     a.x = fmaf(w0.x, q0.x, fmaf(-w0.y, q0.y, a.x));
@@ -611,7 +614,7 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
     }
 #pragma unroll
     for (int i2 = 0; i2 < NMT; ++i2)
-        if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = make_double2(macc[i2].x, macc[i2].y);
+        if (tid + 256 * i2 < NM) mt[tid + 256 * i2] = macc[i2];
     __syncthreads();
     // tau'_f: 8 threads per family (consecutive lanes) take every 8th moment,
     // then a shuffle maximum over the 8
@@ -621,8 +624,8 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
         float tm = 0.0f;
 #pragma unroll
         for (int j = g; j < kFarJ; j += 8) {
-            const double2 m = mt[j * F + f];
-            tm = fmaxf(tm, fmaxf(fabsf((float)m.x), fabsf((float)m.y)));
+            const float2 m = mt[j * F + f];
+            tm = fmaxf(tm, fmaxf(fabsf(m.x), fabsf(m.y)));
         }
 #pragma unroll
         for (int o = 1; o < 8; o <<= 1) tm = fmaxf(tm, __shfl_xor(tm, o, 64));
@@ -649,8 +652,8 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
             const int j = 8 * kb + 4 * lh + q;
             float2 m = make_float2(0.0f, 0.0f);
             if (f < F) {
-                const double2 md = mt[j * F + f];
-                m = make_float2((float)md.x * it_f, (float)md.y * it_f);
+                const float2 md = mt[j * F + f];
+                m = make_float2(md.x * it_f, md.y * it_f);
             }
             h2 hi, lo;
             if (col & 1)
