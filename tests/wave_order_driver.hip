@@ -5,6 +5,7 @@
 // run-time forms of the map agree, and the root z = -1 (k = M/2) sits at
 // position 512 (where the root-value kernels place its finite formula).
 #include <stdio.h>
+#include <stdlib.h>
 
 #include <vector>
 
@@ -25,7 +26,13 @@ static int check_static() {
     return bad;
 }
 
-int main() {
+int main(int argc, char** argv) {
+    if (argc == 3 && argv[1][0] == 'd') {  // "dump LOGM": the frequency at each position, one per line
+        const int logm = atoi(argv[2]);
+        if (logm < 10 || logm > 16) return 2;
+        for (int pos = 0; pos < (1 << logm); ++pos) printf("%d\n", wf_freq_rt(logm, pos));
+        return 0;
+    }
     int bad = check_static<10>() + check_static<11>() + check_static<12>() + check_static<13>() + check_static<14>();
     if (bad) {
         printf("static and run-time maps differ at %d positions\n", bad);
