@@ -312,11 +312,19 @@ struct HRec {
 };
 
 // (a, b) as float16 high and low parts: hi the rounding, lo the rounding of the
-// float32 remainder
+// float32 remainder.  Each remainder is one v_fma_mix_f32, -hi * 1 + a with the
+// float16 half converted inside the instruction: the same value as converting
+// and subtracting (the product is exact, one rounding), one instruction instead
+// of two.  (Where a is itself a product the compiler fuses that product into a
+// mixed FMA on its own; the far form's powers are not products at this point.)
 __device__ __forceinline__ void split_pair(float a, float b, h2& hi, h2& lo) {
     const f2v v = {a, b};
     hi = __builtin_convertvector(v, h2);
-    const f2v r = {a - (float)hi[0], b - (float)hi[1]};
+    const unsigned hb = __builtin_bit_cast(unsigned, hi);
+    float ra, rb;
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel_hi:[1,0,0]" : "=v"(ra) : "v"(hb), "v"(a));
+    asm("v_fma_mix_f32 %0, -%1, 1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "=v"(rb) : "v"(hb), "v"(b));
+    const f2v r = {ra, rb};
     lo = __builtin_convertvector(r, h2);
 }
 
