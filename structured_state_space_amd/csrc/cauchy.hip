@@ -523,9 +523,10 @@ __global__ __launch_bounds__(256) void cauchy_h_prep_kernel(int H, int N, const 
     // ---- far roots: the poles' centre c and radius R (float64), the moments
     //      Mt_{j,f}, their scales, and the moment blocks ----
     __shared__ double rmax[4];
-    // states per sub-chunk of the moment sums (32 keeps the kernel's LDS under
-    // 40 KB at rank 2: four workgroups per CU)
-    constexpr int kSub = 32;
+    // states per sub-chunk of the moment sums: 32 at ranks 2 and 3 keeps the
+    // kernel's LDS at 30 and 38 KB (five and four workgroups per CU); rank 1
+    // fits 64 (34 KB), half the sub-chunk barriers for its longer state vectors
+    constexpr int kSub = RK == 1 ? 64 : 32;
     __shared__ float2 qp[kSub][kFarJ];  // powers ((lambda_n - c)/R)^j of kSub states (formed in float64)
     __shared__ float2 mt[kFarJ * F];
     __shared__ float2 wsub[kSub * F];   // the weights of kSub states
