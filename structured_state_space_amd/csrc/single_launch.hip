@@ -31,6 +31,9 @@
 //   B3: waves 1-8 multiply by the spectrum of their half and inverse-
 //       transform; the twisted halves are untwisted and added to the cyclic
 //       ones through LDS; rows are stored.
+// With no rows (Bsz = 0) the launch is the kernel generator's: phase A (the
+// root values also written out when asked for) and the kernel transform of
+// B1, then it returns.
 #include <float.h>
 
 #include "common.hpp"
